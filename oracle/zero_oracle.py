@@ -1,0 +1,269 @@
+"""Oracle: a plain, slow, CPU implementation of one ZeRO-DP rank's step.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's ``cpu_baseline`` leg may import or call this module.  It shares
+no code with the HIP library: no kernels, headers, helpers or constants.
+
+What it computes follows the ZeRO pages:
+
+* "ZeRO: partitioning training state across GPUs" (upskillscore concept page),
+  section "How it works": the model states of Psi parameters are split into
+  Nd parts; the owner of a gradient partition reduces it (reduce-scatter),
+  updates only its own optimizer-state partition, and an all-gather
+  distributes the updated fp16 parameters.  Memory 16Psi / 4Psi+12Psi/Nd /
+  2Psi+14Psi/Nd / 16Psi/Nd; communication 2Psi (stages 0-2) or 3Psi.
+* "ZeRO: Memory Optimization for Training Large Models" (trishampatil.com
+  engineering dissection), sections "The Real Problem" (2Psi + 2Psi + K Psi,
+  K = 12 for fp32 copy, momentum, variance) and "The Full Progression, in One
+  View" (the per-stage table and the 7.5B / Nd = 64 numbers).
+* The anthology note on ZeRO (dmarx.github.io note-103), "Assumptions": Adam
+  in mixed precision, fp16 params, fp32 param copy, momentum and variance.
+
+Where the pages are silent (the Adam arithmetic, the loss scale, padding,
+accumulation precision, the overflow policy) the plainest reading is taken:
+
+* sum:      s_j = G_0[j] + G_1[j] + ... + G_{Nd-1}[j], left to right in
+            float64.  Every fp16 value is an integer multiple of 2^-24 below
+            2^16 in magnitude, so the float64 sum is exact for Nd < 8192 and
+            any order gives the same bits (up to the sign of a zero sum, which
+            the left-to-right order fixes).
+* unscale:  g = s * (1/L);  overflow = any(!isfinite(s)) over the window;
+            sumsq = sum of g*g, summed exactly and rounded once (math.fsum).
+* Adam:     bias-corrected Adam with eps added after the square root of the
+            corrected second moment, AdamW-style decoupled weight decay
+            p * (1 - lr*wd).  All arithmetic in float64, one IEEE operation at
+            a time (no fused multiply-add), state stored back as float32:
+                m' = b1*m + (1-b1)*g
+                v' = b2*v + (1-b2)*(g*g)
+                d  = sqrt(v') * (1/sqrt(1-b2^t)) + eps
+                q  = m' / d
+                p' = p*(1-lr*wd) - (lr/(1-b1^t)) * q
+            b1^t and b2^t are running products (t multiplications from 1.0).
+* skip:     an overflowing step stores nothing and does not advance t.
+* emit:     allgather[off + j] = fp16 round-to-nearest-even of the fp32 master.
+* plan:     tensors packed in list order; S = A*ceil(Psi/(Nd*A)); rank r owns
+            [r*S, (r+1)*S); the padding sits at the tail of rank Nd-1.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Sequence
+
+import numpy as np
+
+F16 = np.float16
+F32 = np.float32
+F64 = np.float64
+
+
+# --------------------------------------------------------------------------
+# Partition plan.  Upskillscore "How it works": optimizer states are split
+# into Nd parts, each process updating its own; trishampatil "ZeRO's Core
+# Idea" figure: GPU i holds shard i.  Padding/alignment is a reading (the
+# pages do not fix it): equal shards of S = A*ceil(Psi/(Nd*A)) elements.
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Frag:
+    tensor: int       # index in the tensor list
+    rank: int         # owning rank
+    tensor_off: int   # first element inside the tensor
+    flat_off: int     # first element inside the flat buffer
+    local_off: int    # first element inside the owner's shard
+    length: int
+
+
+@dataclass(frozen=True)
+class Plan:
+    psi: int
+    nd: int
+    align: int
+    part: int         # S, elements per rank
+    padded: int       # Nd * S
+    pad: int          # padded - psi
+    frags: List[Frag] = field(default_factory=list)
+
+    def rank_offset(self, r: int) -> int:
+        return r * self.part
+
+
+def plan(numels: Sequence[int], nd: int, align: int = 256) -> Plan:
+    if nd < 1 or align < 1:
+        raise ValueError("nd and align must be >= 1")
+    numels = [int(x) for x in numels]
+    if any(x < 0 for x in numels):
+        raise ValueError("negative tensor size")
+    psi = sum(numels)
+    # ceil(psi / (nd*align)) in exact integer arithmetic
+    units = -(-psi // (nd * align))
+    part = align * units
+    padded = nd * part
+    frags: List[Frag] = []
+    flat = 0
+    for ti, numel in enumerate(numels):
+        done = 0
+        while done < numel:
+            pos = flat + done
+            rank = pos // part
+            local = pos - rank * part
+            length = min(numel - done, part - local)
+            frags.append(Frag(ti, rank, done, pos, local, length))
+            done += length
+        flat += numel
+    return Plan(psi, nd, align, part, padded, padded - psi, frags)
+
+
+# --------------------------------------------------------------------------
+# Memory and communication model.  trishampatil "The Real Problem" (16 Psi =
+# 2 Psi + 2 Psi + K Psi, K = 12), sections "ZeRO-1/2/3" and "The Full
+# Progression, in One View" (per-stage memory and 2Psi/2Psi/2Psi/3Psi);
+# upskillscore "How it works" (same formulas; 3Psi = two parameter
+# all-gathers plus the gradient reduce-scatter).
+# --------------------------------------------------------------------------
+def memory_model(psi: float, nd: int, stage: int, k: int = 12) -> dict:
+    if nd < 1 or stage not in (0, 1, 2, 3) or k < 0:
+        raise ValueError("bad arguments")
+    psi = float(psi)
+    params = 2.0 * psi if stage < 3 else 2.0 * psi / nd
+    grads = 2.0 * psi if stage < 2 else 2.0 * psi / nd
+    optim = k * psi if stage < 1 else k * psi / nd
+    total = params + grads + optim
+    comm = 2.0 * psi if stage < 3 else 3.0 * psi
+    dp_total = (2.0 + 2.0 + k) * psi
+    return {
+        "params_bytes": params,
+        "grads_bytes": grads,
+        "optim_bytes": optim,
+        "total_bytes": total,
+        "comm_elems": comm,
+        # a ring collective moves (Nd-1)/Nd of the nominal volume per rank
+        "comm_elems_ring": comm * (nd - 1) / nd,
+        "reduction_vs_dp": dp_total / total if total > 0 else float("inf"),
+    }
+
+
+# --------------------------------------------------------------------------
+# Local half of the reduce-scatter.  Upskillscore "How it works" (Pos+g: each
+# gradient is reduced only on the process that owns the partition);
+# trishampatil "Forward/Backward Under ZeRO-3" (reduce-scatter gradients into
+# shards).  Reading: the reduction is an exact sum.
+# --------------------------------------------------------------------------
+def reduce_owned(slices: np.ndarray) -> np.ndarray:
+    """slices: float16 array [Nd, n] (slice k = rank k's contribution to the
+    owned window).  Returns the float64 sum over k, left to right."""
+    slices = np.asarray(slices)
+    if slices.dtype != F16 or slices.ndim != 2 or slices.shape[0] < 1:
+        raise ValueError("expected float16 [Nd >= 1, n]")
+    s = slices[0].astype(F64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        for k in range(1, slices.shape[0]):
+            s = s + slices[k].astype(F64)
+    return s
+
+
+def unscale(s: np.ndarray, loss_scale: float):
+    """Returns (g, overflow, sumsq).  Overflow is any non-finite reduced value
+    (mixed-precision practice cited by the anthology note, "Connections":
+    Micikevicius et al.).  sumsq is meaningful only without overflow."""
+    if not (loss_scale > 0 and math.isfinite(loss_scale)):
+        raise ValueError("loss scale must be positive and finite")
+    inv = 1.0 / float(loss_scale)
+    overflow = bool(np.any(~np.isfinite(s)))
+    g = s * inv
+    if overflow:
+        return g, True, float("nan")
+    return g, False, math.fsum((g * g).tolist())
+
+
+# --------------------------------------------------------------------------
+# Mixed-precision Adam.  Anthology note "Assumptions" and trishampatil "The
+# Real Problem": fp32 parameter copy, momentum and variance (K = 12).
+# --------------------------------------------------------------------------
+def step_scalars(lr, beta1, beta2, eps, weight_decay, b1_pow_prev, b2_pow_prev):
+    """Scalars of the step being taken, from the running powers of the
+    committed steps (b^0 = 1.0).  Each line is one IEEE float64 operation."""
+    b1t = b1_pow_prev * beta1
+    b2t = b2_pow_prev * beta2
+    bc1 = 1.0 - b1t
+    bc2 = 1.0 - b2t
+    return {
+        "b1": float(beta1),
+        "b2": float(beta2),
+        "omb1": 1.0 - beta1,
+        "omb2": 1.0 - beta2,
+        "ss": lr / bc1,
+        "isb": 1.0 / math.sqrt(bc2),
+        "dcy": 1.0 - lr * weight_decay,
+        "eps": float(eps),
+        "b1t": b1t,
+        "b2t": b2t,
+    }
+
+
+def adam_update(p, m, v, g, sc):
+    """One Adam/AdamW update of (p, m, v) with unscaled gradient g (float64).
+
+    Arithmetic in float64, one rounded operation per step in the order below;
+    results are stored in the dtype of ``p`` (float32 for the 16-byte model,
+    float64 when the test suite compares against a float64 library Adam)."""
+    store = p.dtype
+    p64 = p.astype(F64)
+    m64 = m.astype(F64)
+    v64 = v.astype(F64)
+    g = np.asarray(g, dtype=F64)
+    m1 = (sc["b1"] * m64) + (sc["omb1"] * g)
+    v1 = (sc["b2"] * v64) + (sc["omb2"] * (g * g))
+    d = (np.sqrt(v1) * sc["isb"]) + sc["eps"]
+    q = m1 / d
+    p1 = (p64 * sc["dcy"]) - (sc["ss"] * q)
+    return p1.astype(store), m1.astype(store), v1.astype(store)
+
+
+def emit(master: np.ndarray) -> np.ndarray:
+    """fp16 copy of the fp32 master for the all-gather buffer (upskillscore
+    "How it works": the all-gather distributes the updated parameters).
+    IEEE round-to-nearest-even; overflow to +-inf."""
+    return np.asarray(master, dtype=F32).astype(F16)
+
+
+# --------------------------------------------------------------------------
+# One rank's owned shard across steps, with the skip/commit rule.
+# --------------------------------------------------------------------------
+class OwnedShard:
+    """Owned-partition state of one rank: fp32 master/m/v of S elements, the
+    committed step count t and the running beta powers.  ``step`` performs
+    reduce -> unscale/flag/sumsq -> Adam -> commit (or skip) -> emit."""
+
+    def __init__(self, master: np.ndarray, lr=1e-3, beta1=0.9, beta2=0.999,
+                 eps=1e-8, weight_decay=0.0, state_dtype=F32):
+        self.p = np.array(master, dtype=state_dtype, copy=True)
+        self.m = np.zeros_like(self.p)
+        self.v = np.zeros_like(self.p)
+        self.hp = dict(lr=float(lr), beta1=float(beta1), beta2=float(beta2),
+                       eps=float(eps), weight_decay=float(weight_decay))
+        self.t = 0
+        self.b1_pow = 1.0
+        self.b2_pow = 1.0
+        self.flags: List[int] = []
+        self.sumsq: List[float] = []
+
+    def window(self) -> np.ndarray:
+        return emit(self.p.astype(F32))
+
+    def step(self, slices: np.ndarray, loss_scale: float):
+        s = reduce_owned(slices)
+        if s.shape[0] != self.p.shape[0]:
+            raise ValueError("window size mismatch")
+        g, overflow, sq = unscale(s, loss_scale)
+        self.flags.append(int(overflow))
+        self.sumsq.append(sq)
+        if overflow:
+            return True, sq
+        sc = step_scalars(self.hp["lr"], self.hp["beta1"], self.hp["beta2"],
+                          self.hp["eps"], self.hp["weight_decay"],
+                          self.b1_pow, self.b2_pow)
+        self.p, self.m, self.v = adam_update(self.p, self.m, self.v, g, sc)
+        self.t += 1
+        self.b1_pow = sc["b1t"]
+        self.b2_pow = sc["b2t"]
+        return False, sq
