@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the ZeRO-DP owned-partition step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+A step is one pass of the whole hot path over one batch of gradients: the
+fused reduce + unscale/flag/sum-of-squares + Adam + commit + fp16 emit
+kernel (zero_adam_step) followed by the conditional all-gather restore
+(zero_restore_skipped).  Inputs are resident in HBM before timing starts.
+Prints one JSON line with the whole-step throughput (owned elements per
+second), the fused kernel's achieved HBM bandwidth against the 8 TB/s peak
+(algorithmic bytes (2*Nd + 26) per owned element), and the oracle's rate on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "owned-shard elements updated/sec + achieved HBM GB/s vs peak, 1 MI355X"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", help="c1..c5 (c2 is the reported workload)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="gradient sets cycled through (0 = enough to exceed 1 GB of slices)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def fill_grads(torch, slices, w, seed, step, pool_rows=8):
+    """Seeded synthetic fp16 slices with the workload's distribution.  Large
+    workloads draw a pool of `pool_rows` independent rows and give slice k
+    row k % pool_rows cyclically shifted by 4099*k + step*131 elements."""
+    from workloads import gen
+    nd, width = slices.shape
+    if nd * width <= (1 << 31):
+        gen.device_fill_grads(slices, seed, step, w.grad_sigma, w.loss_scale, w.dist, width)
+        return
+    rows = min(pool_rows, nd)
+    pool = torch.empty((rows, width), dtype=torch.float16, device=slices.device)
+    gen.device_fill_grads(pool, seed, step, w.grad_sigma, w.loss_scale, w.dist, width)
+    for k in range(nd):
+        s = (4099 * k + 131 * step) % width
+        src = pool[k % rows]
+        slices[k, :width - s].copy_(src[s:])
+        if s:
+            slices[k, width - s:].copy_(src[:s])
+    del pool
+
+
+def cpu_baseline(w, n_sample, budget_s):
+    """The oracle, as it stands, on a bounded sample of the workload's window."""
+    import numpy as np
+    import oracle
+    from workloads import gen
+    master = gen.host_params(w.seed, w.psi, 0, n_sample, w.param_sigma)
+    sh = oracle.OwnedShard(master, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                           weight_decay=w.weight_decay)
+    grads = [gen.host_grad_slices(w.seed, s, 0, w.nd, n_sample, 0, w.psi, w.grad_sigma, w.loss_scale,
+                                  w.dist) for s in (1, 2)]
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        sh.step(grads[steps % 2], w.loss_scale)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    rate = n_sample * steps / el
+    return {"value": rate, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} oracle steps over a {n_sample}-element window of workload {w.key} "
+                      f"(Nd={w.nd}, numpy float64, one thread), {el:.1f} s",
+            "gbs": rate * (2 * w.nd + 26) / 1e9}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the step of one rank runs on one MI355X and no "
+              f"collective is part of this path (asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from workloads import configs, gen
+    from zero_partitioned_mixed_buffer_amd import OwnedShard, binding as B
+
+    w = configs.ALL[args.workload]
+    owner = w.owners[-1]
+    plan, _ = B.plan_partitions(list(w.numels), w.nd, 256)
+    S = plan["part"]
+    off = owner * S
+    valid = max(0, min(S, w.psi - off))  # real (non-padding) elements of the window
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"workload {w.key}: {w.title}; S={S} owner={owner} offset={off} Nd={w.nd}")
+
+    slice_bytes = 2 * w.nd * S
+    rot = args.rotate or max(1, min(8, -(-(1 << 30) // max(slice_bytes, 1))))
+    gsets = []
+    for r in range(rot):
+        t = torch.empty((w.nd, S), dtype=torch.float16, device=dev)
+        fill_grads(torch, t, w, w.seed, r + 1)
+        if valid < S:
+            t[:, valid:].zero_()
+        gsets.append(t)
+    log(f"{rot} gradient set(s) of {slice_bytes / 1e9:.3f} GB filled")
+
+    master = torch.empty(S, dtype=torch.float32, device=dev)
+    gen.device_fill_params(master, w.seed + off, w.param_sigma, valid)
+    shard = OwnedShard(master, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                       weight_decay=w.weight_decay)
+    # the all-gather buffer: the full flat fp16 buffer when it is modest,
+    # otherwise this rank's window only
+    full = plan["padded"] * 2 <= (8 << 30)
+    if full:
+        ag = torch.zeros(plan["padded"], dtype=torch.float16, device=dev)
+        ag_off = off
+    else:
+        ag = torch.zeros(S, dtype=torch.float16, device=dev)
+        ag_off = 0
+    shard.emit(ag, ag_off)
+    del master
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    state, hp, ws = shard.state, shard.hp, shard.workspace
+    srcs = [B.grad_src(t, S, 0, S, w.nd, w.loss_scale) for t in gsets]
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        B.adam_step(srcs[i % rot], state, hp, ag, ag_off, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        B.restore_skipped(state, S, ag, ag_off, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    ctl = shard.control()
+    if ctl["t"] != args.warmup + args.steps or ctl["skipped"] != 0:
+        log(f"unexpected control state after timing: {ctl}")
+        sys.exit(1)
+
+    ms_step = wall * 1e3 / args.steps
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    kern_sorted = sorted(kern_ms)
+    bytes_elem = 2 * w.nd + 26
+    achieved = bytes_elem * S / (kern_avg * 1e-3) / 1e9
+    log(f"fused kernel: avg {kern_avg * 1e3:.1f} us, median {kern_sorted[len(kern_sorted) // 2] * 1e3:.1f} us, "
+        f"min {kern_sorted[0] * 1e3:.1f} us; step {ms_step * 1e3:.1f} us; {achieved:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n_sample = min(S, 1 << 21) if w.nd <= 64 else min(S, 1 << 16)
+        cpu = cpu_baseline(w, n_sample, args.cpu_seconds)
+        log(f"oracle: {cpu['value']:.3e} elements/s on 1 core")
+
+    out = {
+        "metric": METRIC,
+        "value": S / (ms_step * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.key}: {w.title}",
+            "nd": w.nd,
+            "owner": owner,
+            "owned_elems": S,
+            "bytes_per_elem": bytes_elem,
+            "grad_sets_rotated": rot,
+            "allgather": "full flat buffer" if full else "owned window",
+            "step_hbm_gbs": bytes_elem * S / (ms_step * 1e-3) / 1e9,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": None,
+            "kernel": "fused_step_kernel",
+            "kernel_avg_us": kern_avg * 1e3,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,260 @@
+/*
+ * zero_dp.h -- C ABI of the ZeRO-DP owned-partition step on one AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (ZeRO-DP, "Zero Redundancy Optimizer", data-parallel stages
+ * Pos / Pos+g / Pos+g+p) partitions the model states of Psi parameters over
+ * Nd data-parallel ranks.  Each rank owns a contiguous window of the flat
+ * parameter buffer; per training step it
+ *   1. receives and sums the Nd ranks' fp16 gradient contributions for its
+ *      window (the local half of the reduce-scatter),
+ *   2. unscales by the loss scale, flags inf/NaN and forms sum(g^2),
+ *   3. runs mixed-precision Adam on its fp32 master / momentum / variance
+ *      (16 bytes per parameter: fp16 param + fp16 grad + 12 bytes of Adam
+ *      state), and
+ *   4. writes its updated fp16 parameters into the flat all-gather buffer at
+ *      its window's offset (the local half of the all-gather).
+ * Sources: upskillscore.com "ZeRO: partitioning training state across GPUs",
+ * section "How it works"; trishampatil.com "ZeRO: Memory Optimization for
+ * Training Large Models", sections "The Real Problem", "ZeRO-1/2/3", "The
+ * Full Progression, in One View" and "Forward/Backward Under ZeRO-3"; the
+ * anthology note on ZeRO (dmarx.github.io note-103), "Assumptions" and
+ * "Method".
+ *
+ * Conventions
+ *   - Every call returns an int status: ZERO_OK (0) or a negative ZERO_E*.
+ *   - "device" pointers are HIP device memory (e.g. from hipMalloc or a
+ *     PyTorch CUDA/HIP tensor); "host" pointers are ordinary CPU memory.
+ *   - Asynchronous calls validate their arguments on the host, enqueue work
+ *     on `stream` (a hipStream_t; NULL = the legacy default stream) and
+ *     return without synchronising.  Results are valid once the stream has
+ *     reached them.  On a non-OK return nothing was enqueued, except for
+ *     ZERO_EHIP, which reports a failed launch (see zero_last_hip_error).
+ *   - The library allocates nothing, keeps no global mutable state and only
+ *     borrows the caller's buffers for the duration of the enqueued work.
+ *   - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
+ *   - Element counts and offsets are int64_t; sizes up to 2^62 elements.
+ *   - A data pointer may be NULL when its element count is 0 (empty window).
+ */
+#ifndef ZERO_DP_H
+#define ZERO_DP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_DP_ABI_VERSION 1
+
+/* ---- status codes --------------------------------------------------- */
+#define ZERO_OK          0
+#define ZERO_EINVAL     -1  /* null pointer, nd < 1, n < 0, bad stage/align, bad hyperparameter */
+#define ZERO_EALIGN     -2  /* a vector operand is not 16-byte aligned, or an offset/stride is not a multiple of 8 elements */
+#define ZERO_EOVERFLOW  -3  /* an int64 size or offset computation would overflow */
+#define ZERO_ECAPACITY  -4  /* the caller's fragment array is too small; *n_frags holds the needed count */
+#define ZERO_EALIAS     -5  /* an output buffer overlaps an input it must not overlap */
+#define ZERO_EHIP       -6  /* a HIP launch or runtime call failed; see zero_last_hip_error() */
+
+/* Message for a status code (static string, never NULL). */
+const char* zero_strerror(int status);
+/* hipError_t of the last ZERO_EHIP returned on the calling thread (0 if none). */
+int zero_last_hip_error(void);
+/* ZERO_DP_ABI_VERSION of the loaded library. */
+int zero_abi_version(void);
+
+/* ---- partition plan (host, synchronous) ------------------------------
+ * The flat parameter buffer holds the tensors packed in list order; it is
+ * split into Nd equal windows ("shard i" on GPU i: trishampatil "ZeRO's Core
+ * Idea"; "the optimizer states are split into Nd parts": upskillscore "How
+ * it works").  The pages leave padding open; this library pads the total to
+ * S = align * ceil(Psi / (Nd * align)) elements per rank, so rank r owns flat
+ * elements [r*S, (r+1)*S) and all padding sits at the tail of rank Nd-1.
+ */
+typedef struct zero_plan {
+    int64_t psi;      /* sum of tensor sizes (real parameters) */
+    int32_t nd;       /* data-parallel degree */
+    int32_t align;    /* alignment of S in elements */
+    int64_t part;     /* S: elements owned by each rank */
+    int64_t padded;   /* Nd * S */
+    int64_t pad;      /* padded - psi, 0 <= pad < Nd * align */
+} zero_plan;
+
+/* One piece of a tensor that lies inside one rank's window. */
+typedef struct zero_frag {
+    int32_t tensor;       /* index into the tensor list */
+    int32_t rank;         /* owning rank */
+    int64_t tensor_off;   /* first element of the piece inside the tensor */
+    int64_t flat_off;     /* first element inside the flat buffer */
+    int64_t local_off;    /* first element inside the owner's window (flat_off - rank*S) */
+    int64_t len;          /* elements in the piece, > 0 */
+} zero_frag;
+
+/*
+ * numels:    host array of n_tensors sizes (>= 0); may be NULL if n_tensors == 0.
+ * nd:        >= 1.   align_elems: >= 8 and a multiple of 8 (keeps every
+ *            window 16-byte aligned for fp16 and fp32 data).
+ * plan:      host, written on success.
+ * frags:     host array of frag_cap entries, written in tensor order and,
+ *            within a tensor, in rank order.  May be NULL if frag_cap == 0.
+ * n_frags:   host, receives the number of fragments.  If it exceeds
+ *            frag_cap the call returns ZERO_ECAPACITY after filling *plan and
+ *            *n_frags (call again with a larger array).
+ * Errors: ZERO_EINVAL, ZERO_EOVERFLOW, ZERO_ECAPACITY.
+ */
+int zero_plan_partitions(const int64_t* numels, int32_t n_tensors, int32_t nd,
+                         int32_t align_elems, zero_plan* plan, zero_frag* frags,
+                         int64_t frag_cap, int64_t* n_frags);
+
+/* ---- memory / communication model (host, synchronous, pure) ----------
+ * Per-device model-state bytes of mixed-precision Adam, K bytes of optimizer
+ * state per parameter (K = 12: fp32 copy, momentum, variance):
+ *   stage 0 (DP)        2Psi + 2Psi + K Psi
+ *   stage 1 (Pos)       2Psi + 2Psi + K Psi/Nd
+ *   stage 2 (Pos+g)     2Psi + (2+K) Psi/Nd
+ *   stage 3 (Pos+g+p)   (2+2+K) Psi/Nd
+ * and the per-step communication volume in elements: 2Psi for stages 0-2
+ * (reduce-scatter Psi + all-gather Psi), 3Psi for stage 3 (two parameter
+ * all-gathers + one reduce-scatter).  trishampatil "The Real Problem",
+ * "ZeRO-1", "ZeRO-2", "ZeRO-3", "The Full Progression, in One View";
+ * upskillscore "How it works".
+ */
+typedef struct zero_mem_report {
+    double params_bytes;     /* fp16 parameters held per device */
+    double grads_bytes;      /* fp16 gradients held per device */
+    double optim_bytes;      /* optimizer state held per device */
+    double total_bytes;
+    double comm_elems;       /* nominal per-rank volume: 2Psi or 3Psi */
+    double comm_elems_ring;  /* comm_elems * (Nd-1)/Nd, what a ring moves per rank */
+    double reduction_vs_dp;  /* (4+K)Psi / total_bytes */
+} zero_mem_report;
+
+/* psi >= 0 and finite; nd >= 1; stage in 0..3; k >= 0.  Errors: ZERO_EINVAL. */
+int zero_memory_model(double psi, int32_t nd, int32_t stage, int32_t k, zero_mem_report* out);
+
+/* ---- gradient source --------------------------------------------------
+ * The Nd ranks' fp16 contributions to the owned window, as the
+ * reduce-scatter delivers them: slice k (rank k) starts at
+ * base + k*slice_stride, and the owned window is elements
+ * [elem_off, elem_off + n) of every slice.
+ */
+typedef struct zero_grad_src {
+    const uint16_t* base;   /* device, fp16 bit patterns, 16-byte aligned */
+    int64_t slice_stride;   /* elements between slices; multiple of 8 (any value if nd == 1) */
+    int64_t elem_off;       /* window offset inside each slice; multiple of 8 */
+    int64_t n;              /* window length S >= 0 (any value; a tail of n % 8 is handled) */
+    int32_t nd;             /* number of slices, 1 <= nd < 8192 (the float64 sum is exact below 2^13 terms) */
+    int32_t reserved;       /* must be 0 */
+    double loss_scale;      /* L > 0 and finite; g = s * (1/L) */
+} zero_grad_src;
+
+/* ---- workspace ----------------------------------------------------------
+ * Device scratch for per-block partial results and a completion counter.
+ * Allocate zero_workspace_bytes() bytes of device memory (16-byte aligned),
+ * zero it ONCE before first use, and never share one workspace between calls
+ * that may run concurrently (different streams).  Every call leaves it ready
+ * for the next call.
+ */
+int64_t zero_workspace_bytes(void);
+
+/* ---- reduce (decomposed path) ---------------------------------------
+ * s_j = G_0[j] + ... + G_{Nd-1}[j] (exact, float64), g_j = s_j * (1/L),
+ * *overflow = 1 if any s_j is inf/NaN else 0, *sumsq = sum_j g_j^2 (float64,
+ * deterministic order).  Pos+g: "each gradient is reduced only on the
+ * process that owns the partition" (upskillscore "How it works").
+ *   grad_out: device float[n], 16-byte aligned, receives fp32(g); may be NULL.
+ *   overflow: device int32, required.  sumsq: device double, required.
+ *   workspace: see above.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EALIAS, ZERO_EHIP.
+ */
+int zero_reduce_owned(const zero_grad_src* src, float* grad_out, int32_t* overflow,
+                      double* sumsq, void* workspace, void* stream);
+
+/* ---- Adam state of one owned shard -----------------------------------
+ * fp32 master weights, momentum and variance (12 bytes per parameter:
+ * anthology note "Assumptions"; trishampatil "The Real Problem"), held twice
+ * (ping-pong) so that a step found to overflow after its single pass can be
+ * dropped: each step reads set ctl->cur and writes set 1 - ctl->cur, and the
+ * step's last workgroup commits it (cur ^= 1, t += 1) only when no element
+ * overflowed.  The control block lives in device memory; initialise it with
+ * zero_ctl_init() on the host and copy it to the device.
+ */
+typedef struct zero_step_ctl {
+    int32_t cur;        /* index (0/1) of the buffers holding the committed state */
+    int32_t t;          /* committed optimizer steps */
+    int32_t overflow;   /* 1 if the last step was skipped (inf/NaN gradient) */
+    int32_t reserved;
+    double beta1_pow;   /* beta1^t, as t successive products from 1.0 */
+    double beta2_pow;   /* beta2^t */
+    double sumsq;       /* sum g^2 of the last step (meaningful when overflow == 0) */
+    int64_t skipped;    /* number of skipped steps */
+} zero_step_ctl;
+
+/* Fills *ctl (host) with t = 0, cur = 0, powers 1.0. */
+void zero_ctl_init(zero_step_ctl* ctl);
+
+typedef struct zero_adam_state {
+    float* master[2];      /* device float[n] each, 16-byte aligned */
+    float* exp_avg[2];     /* momentum m */
+    float* exp_avg_sq[2];  /* variance v */
+    zero_step_ctl* ctl;    /* device */
+} zero_adam_state;
+
+/* Hyperparameters; beta1/beta2 must stay constant over the life of a ctl.
+ * weight_decay is decoupled (AdamW): p <- p*(1 - lr*wd) - ... ; 0 = Adam. */
+typedef struct zero_adam_hp {
+    double lr;
+    double beta1;         /* in [0, 1) */
+    double beta2;         /* in [0, 1) */
+    double eps;           /* > 0 */
+    double weight_decay;  /* >= 0 */
+} zero_adam_hp;
+
+/* ---- fused step (hot path) -------------------------------------------
+ * One pass over the owned window: exact Nd-way sum -> unscale -> overflow
+ * flag and sum g^2 -> Adam/AdamW in float64 (m' = b1 m + (1-b1) g;
+ * v' = b2 v + (1-b2) g^2; d = sqrt(v') / sqrt(1-b2^t) + eps;
+ * p' = p (1 - lr wd) - lr/(1-b1^t) * m'/d; state stored as fp32, RNE) ->
+ * allgather[allgather_off + j] = fp16_RNE(fp32 p'_j).  Then the commit in
+ * ctl (see zero_adam_state).  "Each process updates only its own
+ * [partition] and an all-gather distributes the updated parameters"
+ * (upskillscore "How it works"; trishampatil "Forward/Backward Under
+ * ZeRO-3": reduce-scatter, update the shard, all-gather).
+ *   src: gradient source, src->n = window length.
+ *   st:  ping-pong state; neither set may overlap the other, the slices or
+ *        the all-gather window.
+ *   allgather: device uint16 buffer; the window [allgather_off,
+ *        allgather_off + n) is written (16-byte aligned start).  NULL skips
+ *        the emit.
+ * On an overflowing step the state is untouched (not committed) but the
+ * all-gather window has been overwritten: call zero_restore_skipped before
+ * the window is read.  Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW,
+ * ZERO_EALIAS, ZERO_EHIP.
+ */
+int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st,
+                   const zero_adam_hp* hp, uint16_t* allgather, int64_t allgather_off,
+                   void* workspace, void* stream);
+
+/* Re-emits allgather[off + j] = fp16_RNE(master[ctl->cur][j]) for j < n when
+ * ctl->overflow == 1 (the step was skipped), and does nothing otherwise; the
+ * decision is taken on the device, so no host synchronisation is needed.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EHIP. */
+int zero_restore_skipped(const zero_adam_state* st, int64_t n, uint16_t* allgather,
+                         int64_t allgather_off, void* stream);
+
+/* ---- emit (all-gather half) ------------------------------------------
+ * allgather[allgather_off + j] = fp16_RNE(master[j]) for j < n (IEEE
+ * round-to-nearest-even, overflow to inf).  Initial fill of the all-gather
+ * buffer from the fp32 master (upskillscore "How it works").
+ *   master: device float[n], 16-byte aligned.  allgather: device, window
+ *   start 16-byte aligned.  Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW,
+ *   ZERO_EHIP.
+ */
+int zero_emit_fp16(const float* master, int64_t n, uint16_t* allgather,
+                   int64_t allgather_off, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_DP_H */

@@ -1,0 +1,192 @@
+"""Host-side checks of the C ABI (no GPU): the library loads and exports every
+declared entry point; the C++ planner and memory model agree with the
+oracle; argument validation rejects bad calls before any device work."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+B = pytest.importorskip("zero_partitioned_mixed_buffer_amd.binding")
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(zero_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared_functions()
+    assert {"zero_plan_partitions", "zero_reduce_owned", "zero_adam_step", "zero_emit_fp16",
+            "zero_memory_model"} <= declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert declared == set(B.EXPORTED)
+    assert L.zero_abi_version() == 1
+
+
+def test_strerror(L):
+    for st in (0, -1, -2, -3, -4, -5, -6, -99):
+        assert isinstance(L.zero_strerror(st), bytes)
+
+
+def _cmp_plan(numels, nd, align):
+    cp, cf = B.plan_partitions(numels, nd, align)
+    op = oracle.plan(numels, nd, align)
+    assert (cp["psi"], cp["part"], cp["padded"], cp["pad"]) == (op.psi, op.part, op.padded, op.pad)
+    assert cf == [(f.tensor, f.rank, f.tensor_off, f.flat_off, f.local_off, f.length) for f in op.frags]
+    return cp
+
+
+def test_plan_matches_oracle_random():
+    g = np.random.default_rng(1)
+    for _ in range(400):
+        numels = [int(x) for x in g.integers(0, 5000, int(g.integers(0, 8)))]
+        _cmp_plan(numels, int(g.integers(1, 70)), int(g.choice([8, 16, 256, 1024])))
+
+
+@pytest.mark.parametrize("key", sorted(configs.ALL))
+def test_plan_matches_oracle_workloads(key):
+    w = configs.ALL[key]
+    cp = _cmp_plan(list(w.numels), w.nd, 256)
+    assert cp["padded"] - cp["pad"] == w.psi
+
+
+def test_plan_errors(L):
+    plan = B.Plan()
+    n = C.c_int64()
+    one = (C.c_int64 * 1)(10)
+    assert L.zero_plan_partitions(one, 1, 0, 256, C.byref(plan), None, 0, C.byref(n)) == B.ZERO_EINVAL
+    assert L.zero_plan_partitions(one, 1, 4, 12, C.byref(plan), None, 0, C.byref(n)) == B.ZERO_EINVAL
+    assert L.zero_plan_partitions(one, 1, 4, 0, C.byref(plan), None, 0, C.byref(n)) == B.ZERO_EINVAL
+    assert L.zero_plan_partitions(None, 1, 4, 256, C.byref(plan), None, 0, C.byref(n)) == B.ZERO_EINVAL
+    neg = (C.c_int64 * 1)(-1)
+    assert L.zero_plan_partitions(neg, 1, 4, 256, C.byref(plan), None, 0, C.byref(n)) == B.ZERO_EINVAL
+    big = (C.c_int64 * 2)(2**62, 2**62)
+    assert L.zero_plan_partitions(big, 2, 4, 256, C.byref(plan), None, 0, C.byref(n)) == B.ZERO_EOVERFLOW
+    # psi = 2^63 - 1 fits, but padding it to 3 equal shards of 8-aligned size does not
+    edge = (C.c_int64 * 2)(2**62, 2**62 - 1)
+    assert L.zero_plan_partitions(edge, 2, 3, 8, C.byref(plan), None, 0, C.byref(n)) == B.ZERO_EOVERFLOW
+    # two-call pattern: capacity error reports the needed count
+    three = (C.c_int64 * 1)(1000)
+    assert L.zero_plan_partitions(three, 1, 4, 8, C.byref(plan), None, 0, C.byref(n)) == B.ZERO_ECAPACITY
+    assert n.value == 4 and plan.part == 256
+    buf = (B.Frag * 4)()
+    assert L.zero_plan_partitions(three, 1, 4, 8, C.byref(plan), buf, 4, C.byref(n)) == B.ZERO_OK
+
+
+def test_memory_model_matches_oracle():
+    for psi in (0.0, 1.0, 1.5e9, 7.5e9, 6e10, 124439808.0):
+        for nd in (1, 4, 8, 16, 64, 400):
+            for stage in range(4):
+                for k in (12, 0, 16):
+                    c = B.memory_model(psi, nd, stage, k)
+                    o = oracle.memory_model(psi, nd, stage, k)
+                    for key, val in o.items():
+                        if np.isinf(val):
+                            assert np.isinf(c[key])
+                        else:
+                            assert c[key] == pytest.approx(val, rel=1e-15, abs=0), (psi, nd, stage, k, key)
+
+
+def test_memory_model_printed_values():
+    """The C++ model reproduces the printed 7.5B / Nd = 64 numbers."""
+    got = [round(B.memory_model(7.5e9, 64, s)["total_bytes"] / 1e9, 1) for s in range(4)]
+    assert got == [120.0, 31.4, 16.6, 1.9]
+    assert B.memory_model(7.5e9, 64, 3)["reduction_vs_dp"] == 64.0
+    assert B.memory_model(7.5e9, 64, 3)["comm_elems"] / B.memory_model(7.5e9, 64, 2)["comm_elems"] == 1.5
+
+
+def test_memory_model_errors(L):
+    r = B.MemReport()
+    for args in ((1e9, 0, 1, 12), (1e9, 4, 4, 12), (1e9, 4, -1, 12), (-1.0, 4, 1, 12), (float("nan"), 4, 1, 12),
+                 (1e9, 4, 1, -1)):
+        assert L.zero_memory_model(*args, C.byref(r)) == B.ZERO_EINVAL
+    assert L.zero_memory_model(1e9, 4, 1, 12, None) == B.ZERO_EINVAL
+
+
+def test_ctl_init():
+    c = B.ctl_from_bytes(B.ctl_init_bytes())
+    assert c == {"cur": 0, "t": 0, "overflow": 0, "beta1_pow": 1.0, "beta2_pow": 1.0, "sumsq": 0.0,
+                 "skipped": 0}
+    assert B.CTL_BYTES == 48
+
+
+# Argument validation of the asynchronous calls: every case below fails
+# before the library touches the HIP runtime, so it runs without a GPU.
+A = 1 << 20  # fake, 16-byte aligned "device" addresses; never dereferenced
+
+
+def _state(base=1 << 24, n=64, ctl=1 << 30):
+    return B.adam_state([base, base + 4 * n * 2], [base + 4 * n * 4, base + 4 * n * 6],
+                        [base + 4 * n * 8, base + 4 * n * 10], ctl)
+
+
+def test_step_validation(L):
+    hp = B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    ok_src = B.grad_src(A, 64, 0, 64, 4, 1024.0)
+    st = _state()
+
+    def step(src=ok_src, state=st, hpp=hp, ag=None, off=0, ws=1 << 28):
+        return L.zero_adam_step(C.byref(src), C.byref(state), C.byref(hpp), ag, off, ws, None)
+
+    assert step(src=B.grad_src(None, 64, 0, 64, 4, 1024.0)) == B.ZERO_EINVAL
+    assert step(src=B.grad_src(A, 64, 0, 64, 0, 1024.0)) == B.ZERO_EINVAL
+    assert step(src=B.grad_src(A, 64, 0, -1, 4, 1024.0)) == B.ZERO_EINVAL
+    assert step(src=B.grad_src(A, 64, 0, 64, 4, 0.0)) == B.ZERO_EINVAL
+    assert step(src=B.grad_src(A, 64, 0, 64, 4, float("inf"))) == B.ZERO_EINVAL
+    assert step(src=B.grad_src(A, 64, 0, 64, 8192, 1024.0)) == B.ZERO_EINVAL
+    assert step(src=B.grad_src(A + 2, 64, 0, 64, 4, 1024.0)) == B.ZERO_EALIGN
+    assert step(src=B.grad_src(A, 60, 0, 64, 4, 1024.0)) == B.ZERO_EALIGN
+    assert step(src=B.grad_src(A, 64, 4, 64, 4, 1024.0)) == B.ZERO_EALIGN
+    assert step(src=B.grad_src(A, 2**62, 0, 64, 4, 1024.0)) == B.ZERO_EOVERFLOW
+    for bad in (B.adam_hp(-1, 0.9, 0.999, 1e-8, 0), B.adam_hp(1e-3, 1.0, 0.999, 1e-8, 0),
+                B.adam_hp(1e-3, 0.9, 1.0, 1e-8, 0), B.adam_hp(1e-3, 0.9, 0.999, 0.0, 0),
+                B.adam_hp(1e-3, 0.9, 0.999, 1e-8, -0.1), B.adam_hp(float("nan"), 0.9, 0.999, 1e-8, 0)):
+        assert step(hpp=bad) == B.ZERO_EINVAL
+    assert step(state=_state(ctl=None)) == B.ZERO_EINVAL
+    assert step(state=_state(base=(1 << 24) + 4)) == B.ZERO_EALIGN
+    assert step(ws=None) == B.ZERO_EINVAL
+    assert step(ws=(1 << 28) + 8) == B.ZERO_EALIGN
+    # aliasing: ping and pong master overlap
+    alias = B.adam_state([1 << 24, (1 << 24) + 128], [1 << 25, (1 << 25) + 4096],
+                         [1 << 26, (1 << 26) + 4096], 1 << 30)
+    assert step(state=alias) == B.ZERO_EALIAS
+    # aliasing: all-gather window inside the gradient slices
+    assert step(ag=A + 64, off=0) == B.ZERO_EALIAS
+    # aliasing: state inside the gradient slices
+    assert step(state=_state(base=A)) == B.ZERO_EALIAS
+    # misaligned all-gather window
+    assert step(ag=1 << 29, off=3) == B.ZERO_EALIGN
+
+
+def test_other_validation(L):
+    src = B.grad_src(A, 64, 0, 64, 4, 1024.0)
+    assert L.zero_reduce_owned(C.byref(src), None, None, 1 << 26, 1 << 28, None) == B.ZERO_EINVAL
+    assert L.zero_reduce_owned(C.byref(src), A + 8, 1 << 25, 1 << 26, 1 << 28, None) == B.ZERO_EALIGN
+    assert L.zero_reduce_owned(C.byref(src), A + 16, 1 << 25, 1 << 26, 1 << 28, None) == B.ZERO_EALIAS
+    assert L.zero_emit_fp16(None, 8, 1 << 29, 0, None) == B.ZERO_EINVAL
+    assert L.zero_emit_fp16(1 << 24, -1, 1 << 29, 0, None) == B.ZERO_EINVAL
+    assert L.zero_emit_fp16(1 << 24, 8, 1 << 29, 1, None) == B.ZERO_EALIGN
+    assert L.zero_emit_fp16(1 << 24, 64, (1 << 24) + 64, 0, None) == B.ZERO_EALIAS
+    assert L.zero_emit_fp16(1 << 24, 0, 1 << 29, 0, None) == B.ZERO_OK  # empty: nothing to do
+    st = _state()
+    assert L.zero_restore_skipped(C.byref(st), -1, 1 << 29, 0, None) == B.ZERO_EINVAL
+    assert L.zero_restore_skipped(C.byref(st), 8, None, 0, None) == B.ZERO_EINVAL
+    assert L.zero_restore_skipped(C.byref(st), 8, 1 << 29, 1, None) == B.ZERO_EALIGN

@@ -1,0 +1,192 @@
+"""GPU parity of the HIP path (through the C ABI) against the oracle.
+
+Bar: overflow flags and the committed step count bit-exact; fp32 master,
+momentum and variance elementwise within relative 1e-5 of the oracle
+(equality where the oracle is 0); the fp16 all-gather window within 1 ulp;
+sum of g^2 within relative 1e-12; the buffer outside the window untouched.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import gen
+
+from gpu_util import F16, F32, GpuShardRun, assert_fp16_close, assert_state_close, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+
+
+def _compare_step(run, sh, ctl, p, m, v, bits, ovf, sq, t, tag):
+    assert ctl["overflow"] == int(ovf), tag
+    assert ctl["t"] == sh.t == t, tag
+    stats = [assert_state_close(p, sh.p, f"{tag} master"),
+             assert_state_close(m, sh.m, f"{tag} exp_avg"),
+             assert_state_close(v, sh.v, f"{tag} exp_avg_sq"),
+             assert_fp16_close(run.window(bits), sh.window().view(np.uint16), f"{tag} fp16 window")]
+    assert run.guards_intact(bits), f"{tag}: all-gather buffer written outside the window"
+    if not ovf:
+        assert ctl["sumsq"] == pytest.approx(sq, rel=1e-12, abs=1e-300), tag
+    return stats
+
+
+def _run_case(n, nd, steps, seed, hp=HP, L=1024.0, sigma=1e-3, dist="normal", mutate=None):
+    g = np.random.default_rng(seed)
+    master0 = (g.standard_normal(n) * 0.02).astype(F32)
+    sh = oracle.OwnedShard(master0, **hp)
+    run = GpuShardRun(master0, nd, hp)
+    stats = []
+    for step in range(1, steps + 1):
+        sl = gen.host_grad_slices(seed, step, 0, nd, n, 0, n, sigma, L, dist)
+        if mutate is not None:
+            sl = mutate(step, sl)
+        ovf, sq = sh.step(sl, L)
+        ctl, p, m, v, bits = run.step(sl, L)
+        stats.append(_compare_step(run, sh, ctl, p, m, v, bits, ovf, sq, sh.t, f"n={n} nd={nd} step={step}"))
+    return sh, run, stats
+
+
+@pytest.mark.parametrize("n", [0, 8, 256, 2048 * 3 + 256, 5003, 65536 + 7])
+@pytest.mark.parametrize("nd", [1, 2, 3, 17])
+def test_fused_step_small(n, nd):
+    _, _, stats = _run_case(n, nd, steps=3, seed=100 + n + nd)
+    # the fixed float64 operation sequence is expected to agree bit for bit
+    assert min(s[0] for s in stats) >= 0.999
+
+
+@pytest.mark.parametrize("nd", [4, 8, 64])
+def test_fused_step_adamw_many_steps(nd):
+    hp = dict(HP, weight_decay=0.01)
+    _, _, stats = _run_case(20000, nd, steps=20, seed=7 + nd, hp=hp, L=4096.0, sigma=1e-4)
+    assert min(s[0] for s in stats) >= 0.999
+
+
+def test_fused_step_student_t():
+    _run_case(30000, 20, steps=4, seed=31, L=2048.0, sigma=1e-4, dist="student_t3")
+
+
+def _edge_mutate(step, sl):
+    g = np.random.default_rng(step)
+    pool = np.array([0.0, -0.0, 65504.0, -65504.0, 2.0**-24, -(2.0**-24), 2.0**-14, -(2.0**-14),
+                     6.1e-5, 1.0], dtype=F16)
+    sl = sl.copy()
+    pick = g.random(sl.shape) < 0.2
+    sl[pick] = pool[g.integers(0, len(pool), int(pick.sum()))]
+    sl[:, :4] = np.array([0.0, -0.0, 2.0**-24, -65504.0], dtype=F16)
+    sl[:, -3:] = np.array([-0.0, 65504.0, 2.0**-24], dtype=F16)
+    return sl
+
+
+def test_fused_step_edge_values():
+    """Signed zeros, fp16 subnormals and +-65504 at the first, last and
+    random elements; all-zero (padding-like) elements stay zero."""
+    _run_case(4099, 5, steps=4, seed=5, mutate=_edge_mutate, L=1.0)
+
+
+@pytest.mark.parametrize("where", ["first", "middle", "last"])
+@pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan, "inf-inf"])
+def test_overflow_skip(where, bad):
+    """An inf/NaN anywhere skips the step: state bit-identical, t unchanged,
+    all-gather window restored; the following steps proceed normally."""
+    n, nd = 10000 + 3, 6
+    pos = {"first": 0, "middle": n // 2, "last": n - 1}[where]
+
+    def mutate(step, sl):
+        if step == 2:
+            sl = sl.copy()
+            if bad == "inf-inf":
+                sl[1, pos], sl[4, pos] = np.inf, -np.inf
+            else:
+                sl[3, pos] = bad
+        return sl
+
+    sh, run, _ = _run_case(n, nd, steps=4, seed=9, mutate=mutate)
+    assert sh.flags == [0, 1, 0, 0] and sh.t == 3
+    ctl = run.shard.control()
+    assert ctl["skipped"] == 1 and ctl["t"] == 3
+
+
+def test_overflow_window_restored_bitwise():
+    n, nd = 3000, 4
+    g = np.random.default_rng(3)
+    master0 = (g.standard_normal(n) * 0.02).astype(F32)
+    run = GpuShardRun(master0, nd, HP)
+    sl = gen.host_grad_slices(3, 1, 0, nd, n, 0, n, 1e-3, 1024.0)
+    _, p1, m1, v1, bits1 = run.step(sl, 1024.0)
+    sl2 = sl.copy()
+    sl2[2, 1234] = np.inf
+    ctl, p2, m2, v2, bits2 = run.step(sl2, 1024.0)
+    assert ctl["overflow"] == 1 and ctl["t"] == 1
+    for a, b in ((p1, p2), (m1, m2), (v1, v2)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(bits1, bits2)
+
+
+def test_reduce_owned_parity():
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    g = np.random.default_rng(17)
+    for n, nd in ((0, 3), (5, 1), (8203, 7), (70001, 33)):
+        sl = gen.host_grad_slices(17, 1, 0, nd, n, 0, n, 1e-3, 1024.0)
+        sl = _edge_mutate(1, sl) if n > 8 else sl
+        s = oracle.reduce_owned(sl)
+        gg, ovf, sq = oracle.unscale(s, 1024.0)
+        stride = (n + 7) // 8 * 8 + 8
+        dsl = torch.zeros((nd, stride), dtype=torch.float16, device="cuda")
+        dsl[:, :n] = torch.from_numpy(sl).cuda()
+        out = torch.full((max(n, 1),), 123.0, dtype=torch.float32, device="cuda")
+        flag = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+        ssq = torch.zeros(1, dtype=torch.float64, device="cuda")
+        ws = torch.zeros(B.workspace_bytes(), dtype=torch.uint8, device="cuda")
+        src = B.grad_src(dsl, stride, 0, n, nd, 1024.0)
+        B.reduce_owned(src, out, flag, ssq, ws)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == int(ovf)
+        got = out.cpu().numpy()[:n]
+        assert np.array_equal(got.view(np.uint32), gg.astype(F32).view(np.uint32))
+        assert float(ssq.item()) == pytest.approx(sq, rel=1e-12, abs=1e-300)
+        # second call on the same workspace (completion counter reset)
+        sl2 = sl.copy()
+        if n:
+            sl2[nd - 1, n - 1] = np.nan
+            dsl[:, :n] = torch.from_numpy(sl2).cuda()
+            B.reduce_owned(src, None, flag, ssq, ws)
+            torch.cuda.synchronize()
+            assert int(flag.item()) == 1
+
+
+def test_emit_parity():
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    g = np.random.default_rng(19)
+    specials = np.array([int(r, 16) for r in
+                         "3f801000 3f803000 477fe000 477ff000 33000000 33400000 387fe000 80000000 "
+                         "7f800000 ff800000 00000001 80000001 7f7fffff 3dcccccd".split()],
+                        dtype=np.uint32).view(F32)
+    for n in (1, 7, 8, 4096 + 5, 300001):
+        x = (g.standard_normal(n) * 10.0 ** g.uniform(-9, 5, n)).astype(F32)
+        x[:min(n, specials.size)] = specials[:min(n, specials.size)]
+        d = torch.from_numpy(x).cuda()
+        ag = torch.full((n + 16,), 0x7E5A, dtype=torch.int16, device="cuda")
+        B.emit_fp16(d, n, ag, 8)
+        torch.cuda.synchronize()
+        bits = ag.cpu().numpy().view(np.uint16)
+        with np.errstate(over="ignore"):
+            want = oracle.emit(x).view(np.uint16)
+        assert np.array_equal(bits[8:8 + n], want)
+        assert np.all(bits[:8] == 0x7E5A) and np.all(bits[8 + n:] == 0x7E5A)
+
+
+def test_determinism_two_runs():
+    n, nd = 100003, 9
+    results = []
+    for _ in range(2):
+        g = np.random.default_rng(77)
+        master0 = (g.standard_normal(n) * 0.02).astype(F32)
+        run = GpuShardRun(master0, nd, HP)
+        for step in range(1, 4):
+            sl = gen.host_grad_slices(77, step, 0, nd, n, 0, n, 1e-3, 1024.0)
+            ctl, p, m, v, bits = run.step(sl, 1024.0)
+        results.append((ctl["sumsq"], p.tobytes(), m.tobytes(), v.tobytes(), bits.tobytes()))
+    assert results[0] == results[1]

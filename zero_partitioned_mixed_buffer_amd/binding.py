@@ -1,0 +1,211 @@
+"""ctypes binding of libzero_dp.so (argument marshalling only).
+
+Every function here converts its arguments (torch tensors or raw device
+addresses, Python numbers) into the C structs of include/zero_dp.h and calls
+the library; all computation happens inside the library.  If the shared
+library is missing, loading raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import List, Optional, Sequence, Tuple
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzero_dp.so")
+_lib = None
+
+ZERO_OK = 0
+ZERO_EINVAL = -1
+ZERO_EALIGN = -2
+ZERO_EOVERFLOW = -3
+ZERO_ECAPACITY = -4
+ZERO_EALIAS = -5
+ZERO_EHIP = -6
+
+EXPORTED = (
+    "zero_strerror", "zero_last_hip_error", "zero_abi_version", "zero_plan_partitions",
+    "zero_memory_model", "zero_workspace_bytes", "zero_reduce_owned", "zero_ctl_init",
+    "zero_adam_step", "zero_restore_skipped", "zero_emit_fp16",
+)
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib().zero_strerror(status).decode()
+        if status == ZERO_EHIP:
+            msg += f" (hipError {lib().zero_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [{status}]")
+        self.status = status
+
+
+class Plan(C.Structure):
+    _fields_ = [("psi", C.c_int64), ("nd", C.c_int32), ("align", C.c_int32), ("part", C.c_int64),
+                ("padded", C.c_int64), ("pad", C.c_int64)]
+
+
+class Frag(C.Structure):
+    _fields_ = [("tensor", C.c_int32), ("rank", C.c_int32), ("tensor_off", C.c_int64),
+                ("flat_off", C.c_int64), ("local_off", C.c_int64), ("len", C.c_int64)]
+
+
+class MemReport(C.Structure):
+    _fields_ = [(k, C.c_double) for k in ("params_bytes", "grads_bytes", "optim_bytes", "total_bytes",
+                                          "comm_elems", "comm_elems_ring", "reduction_vs_dp")]
+
+
+class GradSrc(C.Structure):
+    _fields_ = [("base", C.c_void_p), ("slice_stride", C.c_int64), ("elem_off", C.c_int64),
+                ("n", C.c_int64), ("nd", C.c_int32), ("reserved", C.c_int32), ("loss_scale", C.c_double)]
+
+
+class StepCtl(C.Structure):
+    _fields_ = [("cur", C.c_int32), ("t", C.c_int32), ("overflow", C.c_int32), ("reserved", C.c_int32),
+                ("beta1_pow", C.c_double), ("beta2_pow", C.c_double), ("sumsq", C.c_double),
+                ("skipped", C.c_int64)]
+
+
+class AdamState(C.Structure):
+    _fields_ = [("master", C.c_void_p * 2), ("exp_avg", C.c_void_p * 2), ("exp_avg_sq", C.c_void_p * 2),
+                ("ctl", C.c_void_p)]
+
+
+class AdamHp(C.Structure):
+    _fields_ = [(k, C.c_double) for k in ("lr", "beta1", "beta2", "eps", "weight_decay")]
+
+
+def lib():
+    """Loads libzero_dp.so from the package directory (raises if absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run "
+                           "`python -m zero_partitioned_mixed_buffer_amd.build_lib`")
+    L = C.CDLL(_LIB_PATH)
+    P = C.c_void_p
+    L.zero_strerror.restype = C.c_char_p
+    L.zero_strerror.argtypes = [C.c_int]
+    L.zero_last_hip_error.restype = C.c_int
+    L.zero_abi_version.restype = C.c_int
+    L.zero_plan_partitions.argtypes = [C.POINTER(C.c_int64), C.c_int32, C.c_int32, C.c_int32,
+                                       C.POINTER(Plan), C.POINTER(Frag), C.c_int64, C.POINTER(C.c_int64)]
+    L.zero_memory_model.argtypes = [C.c_double, C.c_int32, C.c_int32, C.c_int32, C.POINTER(MemReport)]
+    L.zero_workspace_bytes.restype = C.c_int64
+    L.zero_reduce_owned.argtypes = [C.POINTER(GradSrc), P, P, P, P, P]
+    L.zero_ctl_init.argtypes = [C.POINTER(StepCtl)]
+    L.zero_ctl_init.restype = None
+    L.zero_adam_step.argtypes = [C.POINTER(GradSrc), C.POINTER(AdamState), C.POINTER(AdamHp), P,
+                                 C.c_int64, P, P]
+    L.zero_restore_skipped.argtypes = [C.POINTER(AdamState), C.c_int64, P, C.c_int64, P]
+    L.zero_emit_fp16.argtypes = [P, C.c_int64, P, C.c_int64, P]
+    for name in ("zero_plan_partitions", "zero_memory_model", "zero_reduce_owned", "zero_adam_step",
+                 "zero_restore_skipped", "zero_emit_fp16"):
+        getattr(L, name).restype = C.c_int
+    if L.zero_abi_version() != 1:
+        raise RuntimeError("libzero_dp.so ABI version mismatch")
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != ZERO_OK:
+        raise ZeroError(status, where)
+
+
+def _ptr(x) -> Optional[int]:
+    """Device or host address of a torch tensor, or an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+# ------------------------------------------------------------------ host calls
+def plan_partitions(numels: Sequence[int], nd: int, align: int = 256) -> Tuple[dict, List[tuple]]:
+    L = lib()
+    arr = (C.c_int64 * max(len(numels), 1))(*[int(x) for x in numels])
+    plan = Plan()
+    n = C.c_int64(0)
+    st = L.zero_plan_partitions(arr, len(numels), nd, align, C.byref(plan), None, 0, C.byref(n))
+    frags: List[tuple] = []
+    if st == ZERO_ECAPACITY or (st == ZERO_OK and n.value > 0):
+        buf = (Frag * n.value)()
+        st = L.zero_plan_partitions(arr, len(numels), nd, align, C.byref(plan), buf, n.value, C.byref(n))
+        frags = [(f.tensor, f.rank, f.tensor_off, f.flat_off, f.local_off, f.len) for f in buf]
+    _check(st, "zero_plan_partitions")
+    return ({"psi": plan.psi, "nd": plan.nd, "align": plan.align, "part": plan.part,
+             "padded": plan.padded, "pad": plan.pad}, frags)
+
+
+def memory_model(psi: float, nd: int, stage: int, k: int = 12) -> dict:
+    r = MemReport()
+    _check(lib().zero_memory_model(float(psi), nd, stage, k, C.byref(r)), "zero_memory_model")
+    return {name: getattr(r, name) for name, _ in MemReport._fields_}
+
+
+def workspace_bytes() -> int:
+    return int(lib().zero_workspace_bytes())
+
+
+def ctl_init_bytes() -> bytes:
+    c = StepCtl()
+    lib().zero_ctl_init(C.byref(c))
+    return bytes(c)
+
+
+def ctl_from_bytes(b: bytes) -> dict:
+    c = StepCtl.from_buffer_copy(b)
+    return {name: getattr(c, name) for name, _ in StepCtl._fields_ if name != "reserved"}
+
+
+CTL_BYTES = C.sizeof(StepCtl)
+
+
+# ------------------------------------------------------------------ device calls
+def grad_src(base, slice_stride: int, elem_off: int, n: int, nd: int, loss_scale: float) -> GradSrc:
+    return GradSrc(_ptr(base), int(slice_stride), int(elem_off), int(n), int(nd), 0, float(loss_scale))
+
+
+def adam_state(master: Sequence, exp_avg: Sequence, exp_avg_sq: Sequence, ctl) -> AdamState:
+    s = AdamState()
+    for i in range(2):
+        s.master[i] = _ptr(master[i])
+        s.exp_avg[i] = _ptr(exp_avg[i])
+        s.exp_avg_sq[i] = _ptr(exp_avg_sq[i])
+    s.ctl = _ptr(ctl)
+    return s
+
+
+def adam_hp(lr: float, beta1: float, beta2: float, eps: float, weight_decay: float) -> AdamHp:
+    return AdamHp(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay))
+
+
+def reduce_owned(src: GradSrc, grad_out, overflow, sumsq, workspace, stream=None):
+    _check(lib().zero_reduce_owned(C.byref(src), _ptr(grad_out), _ptr(overflow), _ptr(sumsq),
+                                   _ptr(workspace), _stream(stream)), "zero_reduce_owned")
+
+
+def adam_step(src: GradSrc, state: AdamState, hp: AdamHp, allgather, allgather_off: int, workspace,
+              stream=None):
+    _check(lib().zero_adam_step(C.byref(src), C.byref(state), C.byref(hp), _ptr(allgather),
+                                int(allgather_off), _ptr(workspace), _stream(stream)), "zero_adam_step")
+
+
+def restore_skipped(state: AdamState, n: int, allgather, allgather_off: int, stream=None):
+    _check(lib().zero_restore_skipped(C.byref(state), int(n), _ptr(allgather), int(allgather_off),
+                                      _stream(stream)), "zero_restore_skipped")
+
+
+def emit_fp16(master, n: int, allgather, allgather_off: int, stream=None):
+    _check(lib().zero_emit_fp16(_ptr(master), int(n), _ptr(allgather), int(allgather_off),
+                                _stream(stream)), "zero_emit_fp16")

@@ -1,0 +1,617 @@
+// Device side of the ZeRO-DP owned-partition step for CDNA4 (gfx950).
+//
+// One rank's step over its owned window, fused into a single streaming pass
+// (upskillscore "How it works": the owner reduces its gradient partition by
+// reduce-scatter, updates only its own optimizer-state partition, and an
+// all-gather distributes the updated parameters; trishampatil
+// "Forward/Backward Under ZeRO-3": reduce-scatter -> update shard ->
+// all-gather):
+//
+//   s_j  = G_0[j] + G_1[j] + ... + G_{Nd-1}[j]       exact in float64
+//   g_j  = s_j * (1/L);  flag |= !isfinite(s_j);  sumsq += g_j^2
+//   m'   = b1*m + (1-b1)*g          v' = b2*v + (1-b2)*(g*g)
+//   d    = sqrt(v') * (1/sqrt(1-b2^t)) + eps          q = m'/d
+//   p'   = p*(1-lr*wd) - (lr/(1-b1^t))*q
+//   fp32 stores of p', m', v';  allgather[off+j] = fp16(fp32(p'))
+//
+// Every floating-point operation above is one IEEE float64 operation with
+// round-to-nearest-even; contraction into fused multiply-adds is disabled
+// for this file, and division and square root are the correctly rounded
+// sequences, so the results are reproducible bit for bit.  The fp16 values
+// are integer multiples of 2^-24 below 2^16, so float64 holds the Nd-way sum
+// exactly for Nd < 2^13 and the summation order does not matter.
+//
+// The work is HBM-bound (about 1 flop per byte), so there is no matrix-core
+// work here; what matters is 16-byte coalesced vector access, enough bytes
+// in flight per CU, and a single pass over every array.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "../../include/zero_dp.h"
+#include "zero_dp_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+using zdp::kBlock;
+using zdp::kVec;
+using zdp::kWaves;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ double lo16(uint32_t w) {
+    const half2_t h = __builtin_bit_cast(half2_t, w);
+    return static_cast<double>(static_cast<float>(h.x));
+}
+__device__ __forceinline__ double hi16(uint32_t w) {
+    const half2_t h = __builtin_bit_cast(half2_t, w);
+    return static_cast<double>(static_cast<float>(h.y));
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+    half2_t h;
+    h.x = static_cast<_Float16>(a);  // IEEE round-to-nearest-even
+    h.y = static_cast<_Float16>(b);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ void init8(double (&acc)[kVec], const uint4& w) {
+    acc[0] = lo16(w.x); acc[1] = hi16(w.x);
+    acc[2] = lo16(w.y); acc[3] = hi16(w.y);
+    acc[4] = lo16(w.z); acc[5] = hi16(w.z);
+    acc[6] = lo16(w.w); acc[7] = hi16(w.w);
+}
+
+__device__ __forceinline__ void add8(double (&acc)[kVec], const uint4& w) {
+    acc[0] += lo16(w.x); acc[1] += hi16(w.x);
+    acc[2] += lo16(w.y); acc[3] += hi16(w.y);
+    acc[4] += lo16(w.z); acc[5] += hi16(w.z);
+    acc[6] += lo16(w.w); acc[7] += hi16(w.w);
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+// Nd-way sum of 8 consecutive window elements starting at `p` (slice 0);
+// slice k is at p + k*stride.  Slices are added in index order.
+template <int U>
+__device__ __forceinline__ void sum_slices8(double (&acc)[kVec], const uint16_t* p, int64_t stride,
+                                            int nd) {
+    init8(acc, ld16(p));
+    int k = 1;
+    for (; k + U <= nd; k += U) {
+        uint4 w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) w[u] = ld16(p + static_cast<int64_t>(k + u) * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) add8(acc, w[u]);
+    }
+    for (; k < nd; ++k) add8(acc, ld16(p + static_cast<int64_t>(k) * stride));
+}
+
+__device__ __forceinline__ double sum_slices1(const uint16_t* p, int64_t stride, int nd) {
+    double s = static_cast<double>(static_cast<float>(*reinterpret_cast<const _Float16*>(p)));
+    for (int k = 1; k < nd; ++k)
+        s += static_cast<double>(
+            static_cast<float>(*reinterpret_cast<const _Float16*>(p + static_cast<int64_t>(k) * stride)));
+    return s;
+}
+
+__device__ __forceinline__ bool finite(double x) { return __builtin_isfinite(x); }
+
+// Deterministic workgroup reduction of one double and one flag; the result
+// is valid in thread 0.
+__device__ __forceinline__ void block_reduce(double& sq, int& flag) {
+    __shared__ double s_sq[kWaves];
+    __shared__ int s_flag[kWaves];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        sq += __shfl_xor(sq, o);
+        flag |= __shfl_xor(flag, o);
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        s_sq[wave] = sq;
+        s_flag[wave] = flag;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = s_sq[0];
+        int f = s_flag[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+            t += s_sq[w];
+            f |= s_flag[w];
+        }
+        sq = t;
+        flag = f;
+    }
+    __syncthreads();
+}
+
+struct Partials {
+    uint32_t* ticket;
+    double* sq;
+    int32_t* flag;
+};
+
+// Publishes this workgroup's partial and returns true in every thread of
+// the workgroup that finishes last; that workgroup then holds the totals
+// (fixed summation order: lane i sums partials i, i+256, ..., then the
+// deterministic workgroup tree) in thread 0.
+__device__ __forceinline__ bool last_block_totals(const Partials& ws, double& sq, int& flag) {
+    __shared__ int s_last;
+    block_reduce(sq, flag);
+    if (threadIdx.x == 0) {
+        ws.sq[blockIdx.x] = sq;
+        ws.flag[blockIdx.x] = flag;
+        __threadfence();
+        const uint32_t prev =
+            __hip_atomic_fetch_add(ws.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == gridDim.x - 1);
+    }
+    __syncthreads();
+    if (!s_last) return false;
+    __threadfence();
+    double t = 0.0;
+    int f = 0;
+    for (uint32_t i = threadIdx.x; i < gridDim.x; i += kBlock) {
+        t += __hip_atomic_load(ws.sq + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        f |= __hip_atomic_load(ws.flag + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    block_reduce(t, f);
+    if (threadIdx.x == 0) {
+        sq = t;
+        flag = f;
+        __hip_atomic_store(ws.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------- kernels
+struct SrcArgs {
+    const uint16_t* win;   // base + elem_off: slice 0 of the window
+    int64_t stride;
+    int64_t n;
+    int32_t nd;
+    double inv_scale;
+};
+
+constexpr int kUnroll = 8;
+
+__global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src, float* grad_out,
+                                                              int32_t* overflow, double* sumsq,
+                                                              Partials ws) {
+    const int64_t ngroups = (src.n + kVec - 1) / kVec;
+    const int64_t nfull = src.n / kVec;
+    double sq = 0.0;
+    int bad = 0;
+    for (int64_t gi = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; gi < ngroups;
+         gi += static_cast<int64_t>(gridDim.x) * kBlock) {
+        const int64_t j = gi * kVec;
+        if (gi < nfull) {
+            double acc[kVec];
+            sum_slices8<kUnroll>(acc, src.win + j, src.stride, src.nd);
+            float gf[kVec];
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                bad |= !finite(acc[e]);
+                const double g = acc[e] * src.inv_scale;
+                sq += g * g;
+                gf[e] = static_cast<float>(g);
+            }
+            if (grad_out != nullptr) {
+                float4* o = reinterpret_cast<float4*>(grad_out + j);
+                o[0] = make_float4(gf[0], gf[1], gf[2], gf[3]);
+                o[1] = make_float4(gf[4], gf[5], gf[6], gf[7]);
+            }
+        } else {
+            for (int64_t e = j; e < src.n; ++e) {
+                const double s = sum_slices1(src.win + e, src.stride, src.nd);
+                bad |= !finite(s);
+                const double g = s * src.inv_scale;
+                sq += g * g;
+                if (grad_out != nullptr) grad_out[e] = static_cast<float>(g);
+            }
+        }
+    }
+    if (last_block_totals(ws, sq, bad) && threadIdx.x == 0) {
+        *overflow = bad;
+        *sumsq = sq;
+    }
+}
+
+struct AdamArgs {
+    float* p[2];
+    float* m[2];
+    float* v[2];
+    zero_step_ctl* ctl;
+    double lr, b1, b2, eps, wd;
+    uint16_t* ag;  // all-gather window start, or null
+};
+
+// Per-element Adam/AdamW update (float64 arithmetic, fp32 storage).
+struct AdamScalars {
+    double b1, b2, omb1, omb2, ss, isb, dcy, eps;
+};
+
+__device__ __forceinline__ void adam1(const AdamScalars& c, double g, float p, float m, float v,
+                                      float& po, float& mo, float& vo) {
+    const double m1 = (c.b1 * static_cast<double>(m)) + (c.omb1 * g);
+    const double v1 = (c.b2 * static_cast<double>(v)) + (c.omb2 * (g * g));
+    const double d = (__builtin_sqrt(v1) * c.isb) + c.eps;
+    const double q = m1 / d;
+    const double p1 = (static_cast<double>(p) * c.dcy) - (c.ss * q);
+    mo = static_cast<float>(m1);
+    vo = static_cast<float>(v1);
+    po = static_cast<float>(p1);
+}
+
+__global__ void __launch_bounds__(kBlock) fused_step_kernel(SrcArgs src, AdamArgs a, Partials ws) {
+    // Scalars of the step being taken, t = committed + 1 (identical in every
+    // lane and workgroup: the same IEEE operations on the same inputs).
+    const zero_step_ctl* ctl = a.ctl;
+    const int cur = ctl->cur;
+    const double b1t = ctl->beta1_pow * a.b1;
+    const double b2t = ctl->beta2_pow * a.b2;
+    AdamScalars c;
+    c.b1 = a.b1;
+    c.b2 = a.b2;
+    c.omb1 = 1.0 - a.b1;
+    c.omb2 = 1.0 - a.b2;
+    c.ss = a.lr / (1.0 - b1t);
+    c.isb = 1.0 / __builtin_sqrt(1.0 - b2t);
+    c.dcy = 1.0 - a.lr * a.wd;
+    c.eps = a.eps;
+
+    const float* __restrict__ pin = a.p[cur];
+    const float* __restrict__ min_ = a.m[cur];
+    const float* __restrict__ vin = a.v[cur];
+    float* __restrict__ pout = a.p[cur ^ 1];
+    float* __restrict__ mout = a.m[cur ^ 1];
+    float* __restrict__ vout = a.v[cur ^ 1];
+    uint16_t* __restrict__ ag = a.ag;
+
+    const int64_t ngroups = (src.n + kVec - 1) / kVec;
+    const int64_t nfull = src.n / kVec;
+    double sq = 0.0;
+    int bad = 0;
+    for (int64_t gi = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; gi < ngroups;
+         gi += static_cast<int64_t>(gridDim.x) * kBlock) {
+        const int64_t j = gi * kVec;
+        if (gi < nfull) {
+            const float4* p4 = reinterpret_cast<const float4*>(pin + j);
+            const float4* m4 = reinterpret_cast<const float4*>(min_ + j);
+            const float4* v4 = reinterpret_cast<const float4*>(vin + j);
+            const float4 pa = p4[0], pb = p4[1];
+            const float4 ma = m4[0], mb = m4[1];
+            const float4 va = v4[0], vb = v4[1];
+            double acc[kVec];
+            sum_slices8<kUnroll>(acc, src.win + j, src.stride, src.nd);
+            const float pi[kVec] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+            const float mi[kVec] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+            const float vi[kVec] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+            float po[kVec], mo[kVec], vo[kVec];
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                bad |= !finite(acc[e]);
+                const double g = acc[e] * src.inv_scale;
+                sq += g * g;
+                adam1(c, g, pi[e], mi[e], vi[e], po[e], mo[e], vo[e]);
+            }
+            float4* po4 = reinterpret_cast<float4*>(pout + j);
+            float4* mo4 = reinterpret_cast<float4*>(mout + j);
+            float4* vo4 = reinterpret_cast<float4*>(vout + j);
+            po4[0] = make_float4(po[0], po[1], po[2], po[3]);
+            po4[1] = make_float4(po[4], po[5], po[6], po[7]);
+            mo4[0] = make_float4(mo[0], mo[1], mo[2], mo[3]);
+            mo4[1] = make_float4(mo[4], mo[5], mo[6], mo[7]);
+            vo4[0] = make_float4(vo[0], vo[1], vo[2], vo[3]);
+            vo4[1] = make_float4(vo[4], vo[5], vo[6], vo[7]);
+            if (ag != nullptr) {
+                uint4 h;
+                h.x = pack_f16(po[0], po[1]);
+                h.y = pack_f16(po[2], po[3]);
+                h.z = pack_f16(po[4], po[5]);
+                h.w = pack_f16(po[6], po[7]);
+                *reinterpret_cast<uint4*>(ag + j) = h;
+            }
+        } else {
+            for (int64_t e = j; e < src.n; ++e) {
+                const double s = sum_slices1(src.win + e, src.stride, src.nd);
+                bad |= !finite(s);
+                const double g = s * src.inv_scale;
+                sq += g * g;
+                float po, mo, vo;
+                adam1(c, g, pin[e], min_[e], vin[e], po, mo, vo);
+                pout[e] = po;
+                mout[e] = mo;
+                vout[e] = vo;
+                if (ag != nullptr) {
+                    const _Float16 h = static_cast<_Float16>(po);
+                    ag[e] = __builtin_bit_cast(uint16_t, h);
+                }
+            }
+        }
+    }
+    if (last_block_totals(ws, sq, bad) && threadIdx.x == 0) {
+        // Commit (or skip) the step for the whole window.
+        zero_step_ctl* w = a.ctl;
+        w->overflow = bad;
+        w->sumsq = sq;
+        if (!bad) {
+            w->cur = cur ^ 1;
+            w->t = ctl->t + 1;
+            w->beta1_pow = b1t;
+            w->beta2_pow = b2t;
+        } else {
+            w->skipped = ctl->skipped + 1;
+        }
+    }
+}
+
+__device__ __forceinline__ void emit_range(const float* __restrict__ src, uint16_t* __restrict__ ag,
+                                           int64_t n) {
+    const int64_t ngroups = (n + kVec - 1) / kVec;
+    const int64_t nfull = n / kVec;
+    for (int64_t gi = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; gi < ngroups;
+         gi += static_cast<int64_t>(gridDim.x) * kBlock) {
+        const int64_t j = gi * kVec;
+        if (gi < nfull) {
+            const float4* s4 = reinterpret_cast<const float4*>(src + j);
+            const float4 a = s4[0], b = s4[1];
+            uint4 h;
+            h.x = pack_f16(a.x, a.y);
+            h.y = pack_f16(a.z, a.w);
+            h.z = pack_f16(b.x, b.y);
+            h.w = pack_f16(b.z, b.w);
+            *reinterpret_cast<uint4*>(ag + j) = h;
+        } else {
+            for (int64_t e = j; e < n; ++e) {
+                const _Float16 h = static_cast<_Float16>(src[e]);
+                ag[e] = __builtin_bit_cast(uint16_t, h);
+            }
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kBlock) emit_kernel(const float* src, uint16_t* ag, int64_t n) {
+    emit_range(src, ag, n);
+}
+
+__global__ void __launch_bounds__(kBlock) restore_kernel(const float* p0, const float* p1,
+                                                         const zero_step_ctl* ctl, uint16_t* ag,
+                                                         int64_t n) {
+    if (ctl->overflow == 0) return;
+    emit_range(ctl->cur ? p1 : p0, ag, n);
+}
+
+// ---------------------------------------------------------------- host glue
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_grid_cache[4][kMaxDevices];  // 0 = not computed yet
+
+enum KernelId { kReduce = 0, kFused = 1, kEmit = 2, kRestore = 3 };
+
+// Workgroups that keep every CU of the current device busy at the kernel's
+// occupancy (grid-stride loops then cover any n).
+int resident_blocks(KernelId id) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1024;
+    int cached = g_grid_cache[id][dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+    int cus = 0, per_cu = 0;
+    const void* fn = nullptr;
+    switch (id) {
+        case kReduce: fn = reinterpret_cast<const void*>(reduce_owned_kernel); break;
+        case kFused: fn = reinterpret_cast<const void*>(fused_step_kernel); break;
+        case kEmit: fn = reinterpret_cast<const void*>(emit_kernel); break;
+        case kRestore: fn = reinterpret_cast<const void*>(restore_kernel); break;
+    }
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlock, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0) {
+        (void)hipGetLastError();
+        return 1024;
+    }
+    int blocks = cus * per_cu;
+    if (blocks > zdp::kMaxBlocks) blocks = zdp::kMaxBlocks;
+    g_grid_cache[id][dev].store(blocks, std::memory_order_relaxed);
+    return blocks;
+}
+
+int grid_for(KernelId id, int64_t n) {
+    const int64_t groups = (n + kVec - 1) / kVec;
+    const int64_t need = (groups + kBlock - 1) / kBlock;
+    const int64_t cap = resident_blocks(id);
+    int64_t g = need < cap ? need : cap;
+    return static_cast<int>(g < 1 ? 1 : g);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
+
+int finish_launch() {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        zdp::set_last_hip_error(static_cast<int>(e));
+        return ZERO_EHIP;
+    }
+    return ZERO_OK;
+}
+
+// Validates a gradient source and returns the byte span its slices cover.
+int check_src(const zero_grad_src* src, Range* span) {
+    if (src == nullptr || src->nd < 1 || src->nd >= 8192 || src->n < 0 || src->elem_off < 0 ||
+        src->reserved != 0)
+        return ZERO_EINVAL;
+    if (src->base == nullptr && src->n != 0) return ZERO_EINVAL;
+    if (!(src->loss_scale > 0.0) || !__builtin_isfinite(src->loss_scale)) return ZERO_EINVAL;
+    if (src->nd > 1 && src->slice_stride < 0) return ZERO_EINVAL;
+    if (!aligned16(src->base) || src->elem_off % kVec != 0) return ZERO_EALIGN;
+    if (src->nd > 1 && src->slice_stride % kVec != 0) return ZERO_EALIGN;
+    int64_t last = 0, end = 0, bytes = 0;
+    const int64_t stride = src->nd > 1 ? src->slice_stride : 0;
+    if (zdp::mul_overflows(static_cast<int64_t>(src->nd - 1), stride, &last) ||
+        zdp::add_overflows(last, src->elem_off, &last) || zdp::add_overflows(last, src->n, &end) ||
+        zdp::mul_overflows(end, 2, &bytes))
+        return ZERO_EOVERFLOW;
+    span->lo = reinterpret_cast<uintptr_t>(src->base + src->elem_off);
+    span->hi = reinterpret_cast<uintptr_t>(src->base) + static_cast<uintptr_t>(bytes);
+    return ZERO_OK;
+}
+
+SrcArgs make_src(const zero_grad_src* src) {
+    SrcArgs s;
+    s.win = src->base + src->elem_off;
+    s.stride = src->nd > 1 ? src->slice_stride : 0;
+    s.n = src->n;
+    s.nd = src->nd;
+    s.inv_scale = 1.0 / src->loss_scale;
+    return s;
+}
+
+Partials make_ws(void* workspace) {
+    char* w = static_cast<char*>(workspace);
+    Partials p;
+    p.ticket = reinterpret_cast<uint32_t*>(w + zdp::kWsTicket);
+    p.sq = reinterpret_cast<double*>(w + zdp::kWsPartSq);
+    p.flag = reinterpret_cast<int32_t*>(w + zdp::kWsPartFlag);
+    return p;
+}
+
+Range bytes_of(const void* p, int64_t n, int64_t elem) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + static_cast<uintptr_t>(n) * static_cast<uintptr_t>(elem)};
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t zero_workspace_bytes(void) { return zdp::kWsBytes; }
+
+int zero_reduce_owned(const zero_grad_src* src, float* grad_out, int32_t* overflow, double* sumsq,
+                      void* workspace, void* stream) {
+    Range span{};
+    int rc = check_src(src, &span);
+    if (rc != ZERO_OK) return rc;
+    if (overflow == nullptr || sumsq == nullptr || workspace == nullptr) return ZERO_EINVAL;
+    if (!aligned16(workspace)) return ZERO_EALIGN;
+    if (grad_out != nullptr) {
+        if (!aligned16(grad_out)) return ZERO_EALIGN;
+        int64_t b = 0;
+        if (zdp::mul_overflows(src->n, 4, &b)) return ZERO_EOVERFLOW;
+        if (overlap(bytes_of(grad_out, src->n, 4), span)) return ZERO_EALIAS;
+    }
+    const int grid = grid_for(kReduce, src->n);
+    (void)hipGetLastError();
+    reduce_owned_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
+        make_src(src), grad_out, overflow, sumsq, make_ws(workspace));
+    return finish_launch();
+}
+
+int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st, const zero_adam_hp* hp,
+                   uint16_t* allgather, int64_t allgather_off, void* workspace, void* stream) {
+    Range span{};
+    int rc = check_src(src, &span);
+    if (rc != ZERO_OK) return rc;
+    if (st == nullptr || hp == nullptr || st->ctl == nullptr || workspace == nullptr)
+        return ZERO_EINVAL;
+    if (!(hp->lr >= 0.0) || !__builtin_isfinite(hp->lr) || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
+        !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps > 0.0) || !__builtin_isfinite(hp->eps) ||
+        !(hp->weight_decay >= 0.0) || !__builtin_isfinite(hp->weight_decay))
+        return ZERO_EINVAL;
+    const int64_t n = src->n;
+    int64_t b4 = 0;
+    if (zdp::mul_overflows(n, 4, &b4)) return ZERO_EOVERFLOW;
+    float* arrs[6] = {st->master[0], st->master[1], st->exp_avg[0],
+                      st->exp_avg[1], st->exp_avg_sq[0], st->exp_avg_sq[1]};
+    Range r[8];
+    for (int i = 0; i < 6; ++i) {
+        if (arrs[i] == nullptr && n != 0) return ZERO_EINVAL;
+        if (!aligned16(arrs[i])) return ZERO_EALIGN;
+        r[i] = bytes_of(arrs[i], n, 4);
+    }
+    if (!aligned16(workspace)) return ZERO_EALIGN;
+    int nr = 6;
+    uint16_t* ag = nullptr;
+    if (allgather != nullptr) {
+        if (allgather_off < 0) return ZERO_EINVAL;
+        int64_t e = 0;
+        if (zdp::add_overflows(allgather_off, n, &e) || zdp::mul_overflows(e, 2, &e)) return ZERO_EOVERFLOW;
+        ag = allgather + allgather_off;
+        if (!aligned16(ag)) return ZERO_EALIGN;
+        r[nr++] = bytes_of(ag, n, 2);
+    }
+    r[nr++] = span;
+    for (int i = 0; i < nr; ++i)
+        for (int k = i + 1; k < nr; ++k)
+            if (overlap(r[i], r[k])) return ZERO_EALIAS;
+
+    AdamArgs a;
+    for (int i = 0; i < 2; ++i) {
+        a.p[i] = st->master[i];
+        a.m[i] = st->exp_avg[i];
+        a.v[i] = st->exp_avg_sq[i];
+    }
+    a.ctl = st->ctl;
+    a.lr = hp->lr;
+    a.b1 = hp->beta1;
+    a.b2 = hp->beta2;
+    a.eps = hp->eps;
+    a.wd = hp->weight_decay;
+    a.ag = ag;
+    const int grid = grid_for(kFused, n);
+    (void)hipGetLastError();
+    fused_step_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(make_src(src), a,
+                                                                              make_ws(workspace));
+    return finish_launch();
+}
+
+int zero_restore_skipped(const zero_adam_state* st, int64_t n, uint16_t* allgather,
+                         int64_t allgather_off, void* stream) {
+    if (st == nullptr || st->ctl == nullptr || n < 0 || allgather_off < 0) return ZERO_EINVAL;
+    if (n != 0 && (allgather == nullptr || st->master[0] == nullptr || st->master[1] == nullptr))
+        return ZERO_EINVAL;
+    int64_t e = 0;
+    if (zdp::mul_overflows(n, 4, &e) || zdp::add_overflows(allgather_off, n, &e) ||
+        zdp::mul_overflows(e, 2, &e))
+        return ZERO_EOVERFLOW;
+    if (n == 0) return ZERO_OK;  // nothing to restore
+    uint16_t* ag = allgather + allgather_off;
+    if (!aligned16(ag) || !aligned16(st->master[0]) || !aligned16(st->master[1])) return ZERO_EALIGN;
+    const int grid = grid_for(kRestore, n);
+    (void)hipGetLastError();
+    restore_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
+        st->master[0], st->master[1], st->ctl, ag, n);
+    return finish_launch();
+}
+
+int zero_emit_fp16(const float* master, int64_t n, uint16_t* allgather, int64_t allgather_off,
+                   void* stream) {
+    if (n < 0 || allgather_off < 0) return ZERO_EINVAL;
+    if (n == 0) return ZERO_OK;  // nothing to write
+    if (master == nullptr || allgather == nullptr) return ZERO_EINVAL;
+    int64_t e = 0;
+    if (zdp::mul_overflows(n, 4, &e) || zdp::add_overflows(allgather_off, n, &e) ||
+        zdp::mul_overflows(e, 2, &e))
+        return ZERO_EOVERFLOW;
+    uint16_t* ag = allgather + allgather_off;
+    if (!aligned16(ag) || !aligned16(master)) return ZERO_EALIGN;
+    if (overlap(bytes_of(master, n, 4), bytes_of(ag, n, 2))) return ZERO_EALIAS;
+    const int grid = grid_for(kEmit, n);
+    (void)hipGetLastError();
+    emit_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(master, ag, n);
+    return finish_launch();
+}
+
+}  // extern "C"

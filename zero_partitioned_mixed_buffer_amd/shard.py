@@ -1,0 +1,52 @@
+"""Device buffers of one rank's owned shard, allocated with torch.
+
+Holds the ping-pong fp32 Adam state, the device control block and the
+workspace, and forwards each step to the library (zero_adam_step followed
+by zero_restore_skipped).  torch is used only to allocate device memory and
+to name the stream.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+from . import binding as B
+
+
+class OwnedShard:
+    def __init__(self, master, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0):
+        import torch
+        if master.dtype != torch.float32 or master.dim() != 1 or not master.is_cuda:
+            raise ValueError("master must be a 1-D float32 device tensor")
+        dev = master.device
+        n = master.numel()
+        self.n = n
+        self.master = [master.clone(), torch.empty(n, dtype=torch.float32, device=dev)]
+        self.exp_avg = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(2)]
+        self.exp_avg_sq = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(2)]
+        ctl0 = torch.frombuffer(bytearray(B.ctl_init_bytes()), dtype=torch.uint8)
+        self.ctl = ctl0.to(dev)
+        self.workspace = torch.zeros(B.workspace_bytes(), dtype=torch.uint8, device=dev)
+        self.state = B.adam_state(self.master, self.exp_avg, self.exp_avg_sq, self.ctl)
+        self.hp = B.adam_hp(lr, beta1, beta2, eps, weight_decay)
+
+    def step(self, slices, loss_scale: float, elem_off: int = 0, allgather=None, allgather_off: int = 0,
+             stream=None):
+        """One fused step; ``slices`` is a float16 device tensor [Nd, stride]
+        whose columns [elem_off, elem_off + n) are the owned window."""
+        nd, stride = slices.shape
+        src = B.grad_src(slices, stride, elem_off, self.n, nd, loss_scale)
+        B.adam_step(src, self.state, self.hp, allgather, allgather_off, self.workspace, stream)
+        if allgather is not None:
+            B.restore_skipped(self.state, self.n, allgather, allgather_off, stream)
+
+    def emit(self, allgather, allgather_off: int = 0, stream=None):
+        """fp16 copy of the committed master into the all-gather buffer."""
+        B.emit_fp16(self.committed()[0], self.n, allgather, allgather_off, stream)
+
+    def control(self) -> dict:
+        """Reads the device control block (synchronises with the device)."""
+        return B.ctl_from_bytes(bytes(self.ctl.cpu().numpy().tobytes()))
+
+    def committed(self, ctl: Optional[dict] = None):
+        cur = (ctl or self.control())["cur"]
+        return self.master[cur], self.exp_avg[cur], self.exp_avg_sq[cur]
