@@ -7,10 +7,9 @@
 namespace zdp {
 
 // Work decomposition of the streaming kernels: a workgroup of 256 lanes
-// (four wave64s), each lane owning a group of 8 consecutive elements, so
-// fp16 data moves in 16-byte and fp32 data in 2 x 16-byte vectors.
+// (four wave64s); each lane owns groups of consecutive elements (the group
+// width is a compile-time choice of the device code).
 constexpr int kBlock = 256;
-constexpr int kVec = 8;
 constexpr int kWaves = kBlock / 64;
 
 // Upper bound on workgroups of the reducing kernels (one partial each).

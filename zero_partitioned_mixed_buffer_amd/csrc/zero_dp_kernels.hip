@@ -37,19 +37,24 @@
 namespace {
 
 using zdp::kBlock;
-using zdp::kVec;
 using zdp::kWaves;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
+// Elements per lane per group (8: 16-byte fp16 and 2 x 16-byte fp32 vectors;
+// 4: 8-byte fp16 and 16-byte fp32 vectors).
+#ifndef ZDP_VEC
+#define ZDP_VEC 4
+#endif
+constexpr int kV = ZDP_VEC;
+static_assert(kV == 4 || kV == 8, "ZDP_VEC must be 4 or 8");
+typedef uint32_t hvec __attribute__((ext_vector_type(kV / 2)));  // kV fp16 values
+typedef float fvec __attribute__((ext_vector_type(kV)));         // kV fp32 values
+
 // ---------------------------------------------------------------- helpers
-__device__ __forceinline__ double lo16(uint32_t w) {
-    const half2_t h = __builtin_bit_cast(half2_t, w);
-    return static_cast<double>(static_cast<float>(h.x));
-}
-__device__ __forceinline__ double hi16(uint32_t w) {
-    const half2_t h = __builtin_bit_cast(half2_t, w);
-    return static_cast<double>(static_cast<float>(h.y));
+__device__ __forceinline__ double h2d(const hvec& w, int e) {
+    const half2_t h = __builtin_bit_cast(half2_t, static_cast<uint32_t>(w[e >> 1]));
+    return static_cast<double>(static_cast<float>((e & 1) ? h.y : h.x));
 }
 
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
@@ -59,39 +64,119 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-__device__ __forceinline__ void init8(double (&acc)[kVec], const uint4& w) {
-    acc[0] = lo16(w.x); acc[1] = hi16(w.x);
-    acc[2] = lo16(w.y); acc[3] = hi16(w.y);
-    acc[4] = lo16(w.z); acc[5] = hi16(w.z);
-    acc[6] = lo16(w.w); acc[7] = hi16(w.w);
+__device__ __forceinline__ void init_v(double (&acc)[kV], const hvec& w) {
+#pragma unroll
+    for (int e = 0; e < kV; ++e) acc[e] = h2d(w, e);
 }
 
-__device__ __forceinline__ void add8(double (&acc)[kVec], const uint4& w) {
-    acc[0] += lo16(w.x); acc[1] += hi16(w.x);
-    acc[2] += lo16(w.y); acc[3] += hi16(w.y);
-    acc[4] += lo16(w.z); acc[5] += hi16(w.z);
-    acc[6] += lo16(w.w); acc[7] += hi16(w.w);
+__device__ __forceinline__ void add_v(double (&acc)[kV], const hvec& w) {
+#pragma unroll
+    for (int e = 0; e < kV; ++e) acc[e] += h2d(w, e);
 }
 
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
-    return *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ hvec pack_v(const float (&x)[kV]) {
+    hvec h;
+#pragma unroll
+    for (int i = 0; i < kV / 2; ++i) h[i] = pack_f16(x[2 * i], x[2 * i + 1]);
+    return h;
 }
 
-// Nd-way sum of 8 consecutive window elements starting at `p` (slice 0);
+// Tuning knobs (compile-time; the defaults are the measured best on gfx950).
+#ifndef ZDP_UNROLL
+#define ZDP_UNROLL 16  // slice loads issued together per chunk
+#endif
+#ifndef ZDP_NT_LOAD
+#define ZDP_NT_LOAD 1  // streaming (non-temporal) loads of slices and state
+#endif
+#ifndef ZDP_NT_STORE
+#define ZDP_NT_STORE 1  // streaming (non-temporal) stores of state and fp16
+#endif
+#ifndef ZDP_WAVES_PER_EU
+#define ZDP_WAVES_PER_EU 0  // >0: cap registers so this many waves fit per SIMD
+#endif
+#if ZDP_WAVES_PER_EU > 0
+#define ZDP_FUSED_ATTR __attribute__((amdgpu_waves_per_eu(ZDP_WAVES_PER_EU)))
+#else
+#define ZDP_FUSED_ATTR
+#endif
+#ifndef ZDP_BPC
+#define ZDP_BPC 1  // >0: at most this many workgroups per CU (reducing kernels)
+#endif
+#ifndef ZDP_XCD_REMAP
+#define ZDP_XCD_REMAP 1  // 1: consecutive logical workgroups on one XCD
+#endif
+#ifndef ZDP_CONTIG
+#define ZDP_CONTIG 0  // 1: each workgroup walks its own contiguous range
+#endif
+#ifndef ZDP_GRID_MULT
+#define ZDP_GRID_MULT 1  // workgroups per resident slot (0: one group per lane)
+#endif
+
+template <typename T>
+__device__ __forceinline__ T ldg(const T* p) {
+#if ZDP_NT_LOAD
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+template <typename T>
+__device__ __forceinline__ void stg(T* p, const T& v) {
+#if ZDP_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+__device__ __forceinline__ hvec ldh(const uint16_t* p) { return ldg(reinterpret_cast<const hvec*>(p)); }
+
+// R slices k0 .. k0+R-1 of 8 consecutive window elements: all R loads are
+// issued before the first add, so R x 16 bytes per lane are in flight.  The
+// first chunk initialises the sums from slice 0 (s = G_0 + G_1 + ...).
+template <int R, bool kFirst>
+__device__ __forceinline__ void sum_chunk(double (&acc)[kV], const uint16_t* p, int64_t stride, int k0) {
+    hvec w[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) w[u] = ldh(p + static_cast<int64_t>(k0 + u) * stride);
+    if constexpr (kFirst) {
+        init_v(acc, w[0]);
+#pragma unroll
+        for (int u = 1; u < R; ++u) add_v(acc, w[u]);
+    } else {
+#pragma unroll
+        for (int u = 0; u < R; ++u) add_v(acc, w[u]);
+    }
+}
+
+// Chunk of r < U slices (r uniform across the workgroup), dispatched to a
+// compile-time size.
+template <int R, bool kFirst>
+__device__ __forceinline__ void sum_rem(double (&acc)[kV], const uint16_t* p, int64_t stride, int k0,
+                                        int r) {
+    if constexpr (R >= 1) {
+        if (r == R) {
+            sum_chunk<R, kFirst>(acc, p, stride, k0);
+            return;
+        }
+        sum_rem<R - 1, kFirst>(acc, p, stride, k0, r);
+    }
+}
+
+// Nd-way sum of kV consecutive window elements starting at `p` (slice 0);
 // slice k is at p + k*stride.  Slices are added in index order.
 template <int U>
-__device__ __forceinline__ void sum_slices8(double (&acc)[kVec], const uint16_t* p, int64_t stride,
+__device__ __forceinline__ void sum_slices(double (&acc)[kV], const uint16_t* p, int64_t stride,
                                             int nd) {
-    init8(acc, ld16(p));
-    int k = 1;
-    for (; k + U <= nd; k += U) {
-        uint4 w[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) w[u] = ld16(p + static_cast<int64_t>(k + u) * stride);
-#pragma unroll
-        for (int u = 0; u < U; ++u) add8(acc, w[u]);
+    if (nd >= U) {
+        sum_chunk<U, true>(acc, p, stride, 0);
+        int k = U;
+        for (; k + U <= nd; k += U) sum_chunk<U, false>(acc, p, stride, k);
+        if (k < nd) sum_rem<U - 1, false>(acc, p, stride, k, nd - k);
+    } else {
+        sum_rem<U - 1, true>(acc, p, stride, 0, nd);
     }
-    for (; k < nd; ++k) add8(acc, ld16(p + static_cast<int64_t>(k) * stride));
 }
 
 __device__ __forceinline__ double sum_slices1(const uint16_t* p, int64_t stride, int nd) {
@@ -133,6 +218,36 @@ __device__ __forceinline__ void block_reduce(double& sq, int& flag) {
     }
     __syncthreads();
 }
+
+// Workgroups are dispatched round-robin over the 8 XCDs; with remapping,
+// logical workgroup w runs on XCD w / (G/8) so each XCD streams one
+// contiguous part of the window.
+__device__ __forceinline__ int64_t logical_block() {
+#if ZDP_XCD_REMAP
+    const uint32_t g = gridDim.x, b = blockIdx.x;
+    if (g % 8 == 0) return static_cast<int64_t>(b % 8) * (g / 8) + b / 8;
+#endif
+    return blockIdx.x;
+}
+
+// Iteration space of one lane over element groups [0, ngroups).
+struct GroupIter {
+    int64_t gi, end, step;
+    __device__ __forceinline__ GroupIter(int64_t ngroups) {
+#if ZDP_CONTIG
+        const int64_t per = (ngroups + gridDim.x - 1) / gridDim.x;
+        const int64_t b = logical_block();
+        const int64_t lo = b * per;
+        end = lo + per < ngroups ? lo + per : ngroups;
+        gi = lo + threadIdx.x;
+        step = kBlock;
+#else
+        gi = logical_block() * kBlock + threadIdx.x;
+        end = ngroups;
+        step = static_cast<int64_t>(gridDim.x) * kBlock;
+#endif
+    }
+};
 
 struct Partials {
     uint32_t* ticket;
@@ -182,33 +297,34 @@ struct SrcArgs {
     double inv_scale;
 };
 
-constexpr int kUnroll = 8;
+constexpr int kUnroll = ZDP_UNROLL;
 
 __global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src, float* grad_out,
                                                               int32_t* overflow, double* sumsq,
                                                               Partials ws) {
-    const int64_t ngroups = (src.n + kVec - 1) / kVec;
-    const int64_t nfull = src.n / kVec;
+    const int64_t ngroups = (src.n + kV - 1) / kV;
+    const int64_t nfull = src.n / kV;
     double sq = 0.0;
     int bad = 0;
-    for (int64_t gi = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; gi < ngroups;
-         gi += static_cast<int64_t>(gridDim.x) * kBlock) {
-        const int64_t j = gi * kVec;
+    for (GroupIter it(ngroups); it.gi < it.end; it.gi += it.step) {
+        const int64_t gi = it.gi;
+        const int64_t j = gi * kV;
         if (gi < nfull) {
-            double acc[kVec];
-            sum_slices8<kUnroll>(acc, src.win + j, src.stride, src.nd);
-            float gf[kVec];
+            double acc[kV];
+            sum_slices<kUnroll>(acc, src.win + j, src.stride, src.nd);
+            float gf[kV];
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) {
+            for (int e = 0; e < kV; ++e) {
                 bad |= !finite(acc[e]);
                 const double g = acc[e] * src.inv_scale;
                 sq += g * g;
                 gf[e] = static_cast<float>(g);
             }
             if (grad_out != nullptr) {
-                float4* o = reinterpret_cast<float4*>(grad_out + j);
-                o[0] = make_float4(gf[0], gf[1], gf[2], gf[3]);
-                o[1] = make_float4(gf[4], gf[5], gf[6], gf[7]);
+                fvec o;
+#pragma unroll
+                for (int e = 0; e < kV; ++e) o[e] = gf[e];
+                stg(reinterpret_cast<fvec*>(grad_out + j), o);
             }
         } else {
             for (int64_t e = j; e < src.n; ++e) {
@@ -252,7 +368,7 @@ __device__ __forceinline__ void adam1(const AdamScalars& c, double g, float p, f
     po = static_cast<float>(p1);
 }
 
-__global__ void __launch_bounds__(kBlock) fused_step_kernel(SrcArgs src, AdamArgs a, Partials ws) {
+__global__ void __launch_bounds__(kBlock) ZDP_FUSED_ATTR fused_step_kernel(SrcArgs src, AdamArgs a, Partials ws) {
     // Scalars of the step being taken, t = committed + 1 (identical in every
     // lane and workgroup: the same IEEE operations on the same inputs).
     const zero_step_ctl* ctl = a.ctl;
@@ -277,50 +393,38 @@ __global__ void __launch_bounds__(kBlock) fused_step_kernel(SrcArgs src, AdamArg
     float* __restrict__ vout = a.v[cur ^ 1];
     uint16_t* __restrict__ ag = a.ag;
 
-    const int64_t ngroups = (src.n + kVec - 1) / kVec;
-    const int64_t nfull = src.n / kVec;
+    const int64_t ngroups = (src.n + kV - 1) / kV;
+    const int64_t nfull = src.n / kV;
     double sq = 0.0;
     int bad = 0;
-    for (int64_t gi = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; gi < ngroups;
-         gi += static_cast<int64_t>(gridDim.x) * kBlock) {
-        const int64_t j = gi * kVec;
+    for (GroupIter it(ngroups); it.gi < it.end; it.gi += it.step) {
+        const int64_t gi = it.gi;
+        const int64_t j = gi * kV;
         if (gi < nfull) {
-            const float4* p4 = reinterpret_cast<const float4*>(pin + j);
-            const float4* m4 = reinterpret_cast<const float4*>(min_ + j);
-            const float4* v4 = reinterpret_cast<const float4*>(vin + j);
-            const float4 pa = p4[0], pb = p4[1];
-            const float4 ma = m4[0], mb = m4[1];
-            const float4 va = v4[0], vb = v4[1];
-            double acc[kVec];
-            sum_slices8<kUnroll>(acc, src.win + j, src.stride, src.nd);
-            const float pi[kVec] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-            const float mi[kVec] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
-            const float vi[kVec] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-            float po[kVec], mo[kVec], vo[kVec];
+            const fvec pv = ldg(reinterpret_cast<const fvec*>(pin + j));
+            const fvec mv = ldg(reinterpret_cast<const fvec*>(min_ + j));
+            const fvec vv = ldg(reinterpret_cast<const fvec*>(vin + j));
+            double acc[kV];
+            sum_slices<kUnroll>(acc, src.win + j, src.stride, src.nd);
+            float po[kV], mo[kV], vo[kV];
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) {
+            for (int e = 0; e < kV; ++e) {
                 bad |= !finite(acc[e]);
                 const double g = acc[e] * src.inv_scale;
                 sq += g * g;
-                adam1(c, g, pi[e], mi[e], vi[e], po[e], mo[e], vo[e]);
+                adam1(c, g, pv[e], mv[e], vv[e], po[e], mo[e], vo[e]);
             }
-            float4* po4 = reinterpret_cast<float4*>(pout + j);
-            float4* mo4 = reinterpret_cast<float4*>(mout + j);
-            float4* vo4 = reinterpret_cast<float4*>(vout + j);
-            po4[0] = make_float4(po[0], po[1], po[2], po[3]);
-            po4[1] = make_float4(po[4], po[5], po[6], po[7]);
-            mo4[0] = make_float4(mo[0], mo[1], mo[2], mo[3]);
-            mo4[1] = make_float4(mo[4], mo[5], mo[6], mo[7]);
-            vo4[0] = make_float4(vo[0], vo[1], vo[2], vo[3]);
-            vo4[1] = make_float4(vo[4], vo[5], vo[6], vo[7]);
-            if (ag != nullptr) {
-                uint4 h;
-                h.x = pack_f16(po[0], po[1]);
-                h.y = pack_f16(po[2], po[3]);
-                h.z = pack_f16(po[4], po[5]);
-                h.w = pack_f16(po[6], po[7]);
-                *reinterpret_cast<uint4*>(ag + j) = h;
+            fvec pw, mw, vw;
+#pragma unroll
+            for (int e = 0; e < kV; ++e) {
+                pw[e] = po[e];
+                mw[e] = mo[e];
+                vw[e] = vo[e];
             }
+            stg(reinterpret_cast<fvec*>(pout + j), pw);
+            stg(reinterpret_cast<fvec*>(mout + j), mw);
+            stg(reinterpret_cast<fvec*>(vout + j), vw);
+            if (ag != nullptr) stg(reinterpret_cast<hvec*>(ag + j), pack_v(po));
         } else {
             for (int64_t e = j; e < src.n; ++e) {
                 const double s = sum_slices1(src.win + e, src.stride, src.nd);
@@ -357,20 +461,17 @@ __global__ void __launch_bounds__(kBlock) fused_step_kernel(SrcArgs src, AdamArg
 
 __device__ __forceinline__ void emit_range(const float* __restrict__ src, uint16_t* __restrict__ ag,
                                            int64_t n) {
-    const int64_t ngroups = (n + kVec - 1) / kVec;
-    const int64_t nfull = n / kVec;
-    for (int64_t gi = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; gi < ngroups;
-         gi += static_cast<int64_t>(gridDim.x) * kBlock) {
-        const int64_t j = gi * kVec;
+    const int64_t ngroups = (n + kV - 1) / kV;
+    const int64_t nfull = n / kV;
+    for (GroupIter it(ngroups); it.gi < it.end; it.gi += it.step) {
+        const int64_t gi = it.gi;
+        const int64_t j = gi * kV;
         if (gi < nfull) {
-            const float4* s4 = reinterpret_cast<const float4*>(src + j);
-            const float4 a = s4[0], b = s4[1];
-            uint4 h;
-            h.x = pack_f16(a.x, a.y);
-            h.y = pack_f16(a.z, a.w);
-            h.z = pack_f16(b.x, b.y);
-            h.w = pack_f16(b.z, b.w);
-            *reinterpret_cast<uint4*>(ag + j) = h;
+            const fvec a = ldg(reinterpret_cast<const fvec*>(src + j));
+            float x[kV];
+#pragma unroll
+            for (int e = 0; e < kV; ++e) x[e] = a[e];
+            stg(reinterpret_cast<hvec*>(ag + j), pack_v(x));
         } else {
             for (int64_t e = j; e < n; ++e) {
                 const _Float16 h = static_cast<_Float16>(src[e]);
@@ -418,6 +519,7 @@ int resident_blocks(KernelId id) {
         (void)hipGetLastError();
         return 1024;
     }
+    if (ZDP_BPC > 0 && per_cu > ZDP_BPC && (id == kReduce || id == kFused)) per_cu = ZDP_BPC;
     int blocks = cus * per_cu;
     if (blocks > zdp::kMaxBlocks) blocks = zdp::kMaxBlocks;
     g_grid_cache[id][dev].store(blocks, std::memory_order_relaxed);
@@ -425,9 +527,10 @@ int resident_blocks(KernelId id) {
 }
 
 int grid_for(KernelId id, int64_t n) {
-    const int64_t groups = (n + kVec - 1) / kVec;
+    const int64_t groups = (n + kV - 1) / kV;
     const int64_t need = (groups + kBlock - 1) / kBlock;
-    const int64_t cap = resident_blocks(id);
+    int64_t cap = static_cast<int64_t>(resident_blocks(id)) * ZDP_GRID_MULT;
+    if (ZDP_GRID_MULT == 0 || cap > zdp::kMaxBlocks) cap = zdp::kMaxBlocks;
     int64_t g = need < cap ? need : cap;
     return static_cast<int>(g < 1 ? 1 : g);
 }
@@ -456,8 +559,8 @@ int check_src(const zero_grad_src* src, Range* span) {
     if (src->base == nullptr && src->n != 0) return ZERO_EINVAL;
     if (!(src->loss_scale > 0.0) || !__builtin_isfinite(src->loss_scale)) return ZERO_EINVAL;
     if (src->nd > 1 && src->slice_stride < 0) return ZERO_EINVAL;
-    if (!aligned16(src->base) || src->elem_off % kVec != 0) return ZERO_EALIGN;
-    if (src->nd > 1 && src->slice_stride % kVec != 0) return ZERO_EALIGN;
+    if (!aligned16(src->base) || src->elem_off % 8 != 0) return ZERO_EALIGN;
+    if (src->nd > 1 && src->slice_stride % 8 != 0) return ZERO_EALIGN;
     int64_t last = 0, end = 0, bytes = 0;
     const int64_t stride = src->nd > 1 ? src->slice_stride : 0;
     if (zdp::mul_overflows(static_cast<int64_t>(src->nd - 1), stride, &last) ||
