@@ -44,25 +44,41 @@ def parse():
     return ap.parse_args()
 
 
-def fill_grads(torch, slices, w, seed, step, pool_rows=8):
-    """Seeded synthetic fp16 slices with the workload's distribution.  Large
-    workloads draw a pool of `pool_rows` independent rows and give slice k
-    row k % pool_rows cyclically shifted by 4099*k + step*131 elements."""
-    from workloads import gen
-    nd, width = slices.shape
-    if nd * width <= (1 << 31):
-        gen.device_fill_grads(slices, seed, step, w.grad_sigma, w.loss_scale, w.dist, width)
-        return
-    rows = min(pool_rows, nd)
-    pool = torch.empty((rows, width), dtype=torch.float16, device=slices.device)
-    gen.device_fill_grads(pool, seed, step, w.grad_sigma, w.loss_scale, w.dist, width)
-    for k in range(nd):
-        s = (4099 * k + 131 * step) % width
-        src = pool[k % rows]
-        slices[k, :width - s].copy_(src[s:])
-        if s:
-            slices[k, width - s:].copy_(src[:s])
-    del pool
+def kernel_fingerprint():
+    """Hash of the device source and its build flags; a counter summary in
+    profiles/ applies to the kernel only while this matches."""
+    import hashlib
+    from zero_partitioned_mixed_buffer_amd import build_lib
+    h = hashlib.sha256()
+    for f in ("zero_dp_kernels.hip", "zero_dp_internal.h"):
+        with open(os.path.join(build_lib.CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join(build_lib.HIP_FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the fused kernel from the committed rocprofv3
+    counter summary for this workload, or None if absent or stale."""
+    import glob
+    import re
+    fp = kernel_fingerprint()
+    for path in glob.glob(os.path.join(ROOT, "profiles", f"fused_step_{workload}_*pmc*.md")):
+        text = open(path).read()
+        m_fp = re.search(r"kernel_fingerprint:\s*([0-9a-f]+)", text)
+        m_tr = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+        if m_fp and m_tr and m_fp.group(1) == fp:
+            return int(m_tr.group(1))
+    return None
+
+
+def calibration_copy(torch, dev):
+    """A plain device copy of known size (256 MiB -> 256 MiB) for scaling the
+    FETCH_SIZE / WRITE_SIZE counters of a profiled run; not timed."""
+    a = torch.ones(1 << 26, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(w, n_sample, budget_s):
@@ -116,9 +132,7 @@ def main():
     gsets = []
     for r in range(rot):
         t = torch.empty((w.nd, S), dtype=torch.float16, device=dev)
-        fill_grads(torch, t, w, w.seed, r + 1)
-        if valid < S:
-            t[:, valid:].zero_()
+        gen.device_fill_grads(t, w.seed, r + 1, w.grad_sigma, w.loss_scale, w.dist, valid)
         gsets.append(t)
     log(f"{rot} gradient set(s) of {slice_bytes / 1e9:.3f} GB filled")
 
@@ -169,6 +183,9 @@ def main():
         log(f"unexpected control state after timing: {ctl}")
         sys.exit(1)
 
+    calibration_copy(torch, dev)
+    traffic = measured_traffic(w.key)
+
     ms_step = wall * 1e3 / args.steps
     kern_avg = sum(kern_ms) / len(kern_ms)
     kern_sorted = sorted(kern_ms)
@@ -212,9 +229,14 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
-            "traffic": None,
+            # measured HBM bytes per launch (rocprofv3 counters, committed summary)
+            # over the same average duration, in GB/s like `achieved`
+            "traffic": None if traffic is None else traffic / (kern_avg * 1e-3) / 1e9,
+            "traffic_bytes_per_launch": traffic,
+            "algorithmic_bytes_per_launch": bytes_elem * S,
             "kernel": "fused_step_kernel",
             "kernel_avg_us": kern_avg * 1e3,
+            "kernel_fingerprint": kernel_fingerprint(),
         },
         "cpu_baseline": cpu,
     }

@@ -15,9 +15,10 @@
  *   4. writes its updated fp16 parameters into the flat all-gather buffer at
  *      its window's offset (the local half of the all-gather).
  * Sources: upskillscore.com "ZeRO: partitioning training state across GPUs",
- * section "How it works"; trishampatil.com "ZeRO: Memory Optimization for
- * Training Large Models", sections "The Real Problem", "ZeRO-1/2/3", "The
- * Full Progression, in One View" and "Forward/Backward Under ZeRO-3"; the
+ * section "How it works"; the trishampatil.com engineering dissection of ZeRO
+ * (page zero-memory-optimization-training-large-models), sections "The Real
+ * Problem", "ZeRO-1/2/3", "The Full Progression, in One View" and
+ * "Forward/Backward Under ZeRO-3"; the
  * anthology note on ZeRO (dmarx.github.io note-103), "Assumptions" and
  * "Method".
  *

@@ -12,8 +12,8 @@ What it computes follows the ZeRO pages:
   updates only its own optimizer-state partition, and an all-gather
   distributes the updated fp16 parameters.  Memory 16Psi / 4Psi+12Psi/Nd /
   2Psi+14Psi/Nd / 16Psi/Nd; communication 2Psi (stages 0-2) or 3Psi.
-* "ZeRO: Memory Optimization for Training Large Models" (trishampatil.com
-  engineering dissection), sections "The Real Problem" (2Psi + 2Psi + K Psi,
+* The trishampatil.com engineering dissection of ZeRO (page
+  zero-memory-optimization-training-large-models), sections "The Real Problem" (2Psi + 2Psi + K Psi,
   K = 12 for fp32 copy, momentum, variance) and "The Full Progression, in One
   View" (the per-stage table and the 7.5B / Nd = 64 numbers).
 * The anthology note on ZeRO (dmarx.github.io note-103), "Assumptions": Adam
