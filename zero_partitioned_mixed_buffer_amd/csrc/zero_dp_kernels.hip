@@ -368,6 +368,97 @@ __device__ __forceinline__ void adam1(const AdamScalars& c, double g, float p, f
     po = static_cast<float>(p1);
 }
 
+
+// Buffers of one fused step after the ping-pong selection.
+struct FusedPtrs {
+    const float* pin;
+    const float* min_;
+    const float* vin;
+    float* pout;
+    float* mout;
+    float* vout;
+    uint16_t* ag;
+};
+
+template <int R>
+__device__ __forceinline__ void pf_load(hvec (&w)[R], fvec& p, fvec& m, fvec& v, const SrcArgs& src,
+                                        const FusedPtrs& f, int64_t j) {
+    p = ldg(reinterpret_cast<const fvec*>(f.pin + j));
+    m = ldg(reinterpret_cast<const fvec*>(f.min_ + j));
+    v = ldg(reinterpret_cast<const fvec*>(f.vin + j));
+#pragma unroll
+    for (int u = 0; u < R; ++u) w[u] = ldh(src.win + j + static_cast<int64_t>(u) * src.stride);
+}
+
+template <int R>
+__device__ __forceinline__ void pf_finish(const hvec (&w)[R], const fvec& pv, const fvec& mv, const fvec& vv,
+                                          const SrcArgs& src, const FusedPtrs& f, const AdamScalars& c,
+                                          int64_t j, double& sq, int& bad) {
+    double acc[kV];
+    init_v(acc, w[0]);
+#pragma unroll
+    for (int u = 1; u < R; ++u) add_v(acc, w[u]);
+    float po[kV], mo[kV], vo[kV];
+#pragma unroll
+    for (int e = 0; e < kV; ++e) {
+        bad |= !finite(acc[e]);
+        const double g = acc[e] * src.inv_scale;
+        sq += g * g;
+        adam1(c, g, pv[e], mv[e], vv[e], po[e], mo[e], vo[e]);
+    }
+    fvec pw, mw, vw;
+#pragma unroll
+    for (int e = 0; e < kV; ++e) {
+        pw[e] = po[e];
+        mw[e] = mo[e];
+        vw[e] = vo[e];
+    }
+    stg(reinterpret_cast<fvec*>(f.pout + j), pw);
+    stg(reinterpret_cast<fvec*>(f.mout + j), mw);
+    stg(reinterpret_cast<fvec*>(f.vout + j), vw);
+    if (f.ag != nullptr) stg(reinterpret_cast<hvec*>(f.ag + j), pack_v(po));
+}
+
+// Full groups gi, gi+step, ... < end when all Nd = R slices fit in one
+// chunk: the next group's R + 3 loads are issued before the current group
+// is summed and updated, so its memory latency overlaps this group's fp64
+// work.  The last iteration re-reads its own group instead of running past
+// the end (the values are not used).
+template <int R>
+__device__ void pf_run(int64_t gi, int64_t end, int64_t step, const SrcArgs& src, const FusedPtrs& f,
+                       const AdamScalars& c, double& sq, int& bad) {
+    if (gi >= end) return;
+    hvec w[R];
+    fvec p, m, v;
+    pf_load<R>(w, p, m, v, src, f, gi * kV);
+    for (;;) {
+        const int64_t gn = gi + step;
+        const int64_t gl = gn < end ? gn : gi;
+        hvec wc[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) wc[u] = w[u];
+        const fvec pc = p, mc = m, vc = v;
+        pf_load<R>(w, p, m, v, src, f, gl * kV);
+        __builtin_amdgcn_sched_barrier(0);  // keep the next group's loads ahead of this group's work
+        pf_finish<R>(wc, pc, mc, vc, src, f, c, gi * kV, sq, bad);
+        if (gn >= end) break;
+        gi = gn;
+    }
+}
+
+template <int R>
+__device__ __forceinline__ bool pf_dispatch(int nd, int64_t gi, int64_t end, int64_t step, const SrcArgs& src,
+                                            const FusedPtrs& f, const AdamScalars& c, double& sq, int& bad) {
+    if constexpr (R >= 1) {
+        if (nd == R) {
+            pf_run<R>(gi, end, step, src, f, c, sq, bad);
+            return true;
+        }
+        return pf_dispatch<R - 1>(nd, gi, end, step, src, f, c, sq, bad);
+    }
+    return false;
+}
+
 __global__ void __launch_bounds__(kBlock) ZDP_FUSED_ATTR fused_step_kernel(SrcArgs src, AdamArgs a, Partials ws) {
     // Scalars of the step being taken, t = committed + 1 (identical in every
     // lane and workgroup: the same IEEE operations on the same inputs).
@@ -397,7 +488,32 @@ __global__ void __launch_bounds__(kBlock) ZDP_FUSED_ATTR fused_step_kernel(SrcAr
     const int64_t nfull = src.n / kV;
     double sq = 0.0;
     int bad = 0;
-    for (GroupIter it(ngroups); it.gi < it.end; it.gi += it.step) {
+    bool done = false;
+    if (src.nd <= kUnroll) {
+        GroupIter it(ngroups);
+        const FusedPtrs f{pin, min_, vin, pout, mout, vout, ag};
+        const int64_t endf = it.end < nfull ? it.end : nfull;
+        done = pf_dispatch<kUnroll>(src.nd, it.gi, endf, it.step, src, f, c, sq, bad);
+        if (done && ngroups > nfull) {
+            // the ragged tail group, by the lane whose sequence contains it
+            const int64_t g = nfull;
+            if (g >= it.gi && g < it.end && (g - it.gi) % it.step == 0) {
+                for (int64_t e = g * kV; e < src.n; ++e) {
+                    const double s = sum_slices1(src.win + e, src.stride, src.nd);
+                    bad |= !finite(s);
+                    const double gg = s * src.inv_scale;
+                    sq += gg * gg;
+                    float po, mo, vo;
+                    adam1(c, gg, pin[e], min_[e], vin[e], po, mo, vo);
+                    pout[e] = po;
+                    mout[e] = mo;
+                    vout[e] = vo;
+                    if (ag != nullptr) ag[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(po));
+                }
+            }
+        }
+    }
+    for (GroupIter it(ngroups); !done && it.gi < it.end; it.gi += it.step) {
         const int64_t gi = it.gi;
         const int64_t j = gi * kV;
         if (gi < nfull) {
