@@ -138,39 +138,50 @@ def main():
         gsets.append(t)
     log(f"{rot} gradient set(s) of {slice_bytes / 1e9:.3f} GB filled")
 
-    master = torch.empty(S, dtype=torch.float32, device=dev)
-    gen.device_fill_params(master, w.seed + off, w.param_sigma, valid)
-    shard = OwnedShard(master, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
-                       weight_decay=w.weight_decay)
+    # Several ranks' owned shards (each with its own ping-pong state and
+    # all-gather window) are stepped in turn, so that at least 1.5 GB of
+    # other traffic passes between two visits to one shard's state: the
+    # 256 MB MALL cannot serve a step the state written by the previous one
+    # (between two optimizer steps of real training, forward and backward
+    # traffic evicts it too).  Every step still processes one full shard.
+    step_bytes = (2 * w.nd + 26) * S
+    n_shards = 1 if step_bytes > 2e9 else min(w.nd, max(2, -(-int(1.5e9) // step_bytes)))
     # the all-gather buffer: the full flat fp16 buffer when it is modest,
-    # otherwise this rank's window only
+    # otherwise one window per stepped shard
     full = plan["padded"] * 2 <= (8 << 30)
-    if full:
-        ag = torch.zeros(plan["padded"], dtype=torch.float16, device=dev)
-        ag_off = off
-    else:
-        ag = torch.zeros(S, dtype=torch.float16, device=dev)
-        ag_off = 0
-    shard.emit(ag, ag_off)
-    del master
+    ag = torch.zeros(plan["padded"] if full else S * n_shards, dtype=torch.float16, device=dev)
+    shards, ag_offs = [], []
+    for r in range(n_shards):
+        rank = (owner + r) % w.nd
+        roff = rank * S
+        rvalid = max(0, min(S, w.psi - roff))
+        master = torch.empty(S, dtype=torch.float32, device=dev)
+        gen.device_fill_params(master, w.seed + roff, w.param_sigma, rvalid)
+        shards.append(OwnedShard(master, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                                 weight_decay=w.weight_decay))
+        ag_offs.append(roff if full else r * S)
+        shards[r].emit(ag, ag_offs[r])
+        del master
     torch.cuda.synchronize()
+    log(f"{n_shards} owned shard(s) stepped in turn; all-gather: {'full flat buffer' if full else 'windows'}")
 
     stream = torch.cuda.current_stream()
-    state, hp, ws = shard.state, shard.hp, shard.workspace
     srcs = [B.grad_src(t, S, 0, S, w.nd, w.loss_scale) for t in gsets]
 
-    def step(i):
-        B.adam_step(srcs[i % rot], state, hp, ag, ag_off, ws, stream)
-        B.restore_skipped(state, S, ag, ag_off, stream)
+    def launch(i, restore=True):
+        sh = shards[i % n_shards]
+        B.adam_step(srcs[i % rot], sh.state, sh.hp, ag, ag_offs[i % n_shards], sh.workspace, stream)
+        if restore:
+            B.restore_skipped(sh.state, S, ag, ag_offs[i % n_shards], stream)
 
     for i in range(args.warmup):
-        step(i)
+        launch(i)
     torch.cuda.synchronize()
 
     # Timed region: K whole steps back to back, nothing else on the stream.
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i)
+        launch(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -180,14 +191,15 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
-        B.adam_step(srcs[(args.warmup + args.steps + i) % rot], state, hp, ag, ag_off, ws, stream)
+        launch(args.warmup + args.steps + i, restore=False)
     e1.record(stream)
     torch.cuda.synchronize()
     kern_avg = e0.elapsed_time(e1) / args.steps
-    B.restore_skipped(state, S, ag, ag_off, stream)
-    ctl = shard.control()
-    if ctl["t"] != args.warmup + 2 * args.steps or ctl["skipped"] != 0:
-        log(f"unexpected control state after timing: {ctl}")
+    for r in range(n_shards):
+        B.restore_skipped(shards[r].state, S, ag, ag_offs[r], stream)
+    ctls = [sh.control() for sh in shards]
+    if sum(c["t"] for c in ctls) != args.warmup + 2 * args.steps or any(c["skipped"] for c in ctls):
+        log(f"unexpected control state after timing: {ctls}")
         sys.exit(1)
 
     calibration_copy(torch, dev)
@@ -225,7 +237,8 @@ def main():
             "owned_elems": S,
             "bytes_per_elem": bytes_elem,
             "grad_sets_rotated": rot,
-            "allgather": "full flat buffer" if full else "owned window",
+            "shards_rotated": n_shards,
+            "allgather": "full flat buffer" if full else "one window per shard",
             "step_hbm_gbs": bytes_elem * S / (ms_step * 1e-3) / 1e9,
         },
         "roofline": {

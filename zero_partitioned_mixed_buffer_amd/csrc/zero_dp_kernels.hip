@@ -89,15 +89,8 @@ __device__ __forceinline__ hvec pack_v(const float (&x)[kV]) {
 #define ZDP_NT_LOAD 1  // streaming (non-temporal) loads of slices and state
 #endif
 #ifndef ZDP_NT_STORE
-#define ZDP_NT_STORE 1  // streaming (non-temporal) stores in the emit and reduce kernels
+#define ZDP_NT_STORE 1  // streaming (non-temporal) stores of state and fp16
 #endif
-// The fused step picks its store policy per call from Nd (measured on
-// gfx950): write-back stores win while the stores are a large share of the
-// traffic (3 <= Nd <= 96); non-temporal stores win for Nd <= 2 (the state
-// streams dominate) and for large Nd (the slice reads dominate and the
-// write-back lines only compete with them in L2).
-constexpr int kPlainStoreMinNd = 3;
-constexpr int kPlainStoreMaxNd = 96;
 #ifndef ZDP_WAVES_PER_EU
 #define ZDP_WAVES_PER_EU 0  // >0: cap registers so this many waves fit per SIMD
 #endif
@@ -128,18 +121,13 @@ __device__ __forceinline__ T ldg(const T* p) {
 #endif
 }
 
-template <bool kNt, typename T>
-__device__ __forceinline__ void stg_p(T* p, const T& v) {
-    if constexpr (kNt) {
-        __builtin_nontemporal_store(v, p);
-    } else {
-        *p = v;
-    }
-}
-
 template <typename T>
 __device__ __forceinline__ void stg(T* p, const T& v) {
-    stg_p<ZDP_NT_STORE != 0>(p, v);
+#if ZDP_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
 }
 
 __device__ __forceinline__ hvec ldh(const uint16_t* p) { return ldg(reinterpret_cast<const hvec*>(p)); }
@@ -402,7 +390,7 @@ __device__ __forceinline__ void pf_load(hvec (&w)[R], fvec& p, fvec& m, fvec& v,
     for (int u = 0; u < R; ++u) w[u] = ldh(src.win + j + static_cast<int64_t>(u) * src.stride);
 }
 
-template <int R, bool kNt>
+template <int R>
 __device__ __forceinline__ void pf_finish(const hvec (&w)[R], const fvec& pv, const fvec& mv, const fvec& vv,
                                           const SrcArgs& src, const FusedPtrs& f, const AdamScalars& c,
                                           int64_t j, double& sq, int& bad) {
@@ -425,10 +413,10 @@ __device__ __forceinline__ void pf_finish(const hvec (&w)[R], const fvec& pv, co
         mw[e] = mo[e];
         vw[e] = vo[e];
     }
-    stg_p<kNt>(reinterpret_cast<fvec*>(f.pout + j), pw);
-    stg_p<kNt>(reinterpret_cast<fvec*>(f.mout + j), mw);
-    stg_p<kNt>(reinterpret_cast<fvec*>(f.vout + j), vw);
-    if (f.ag != nullptr) stg_p<kNt>(reinterpret_cast<hvec*>(f.ag + j), pack_v(po));
+    stg(reinterpret_cast<fvec*>(f.pout + j), pw);
+    stg(reinterpret_cast<fvec*>(f.mout + j), mw);
+    stg(reinterpret_cast<fvec*>(f.vout + j), vw);
+    if (f.ag != nullptr) stg(reinterpret_cast<hvec*>(f.ag + j), pack_v(po));
 }
 
 // Full groups gi, gi+step, ... < end when all Nd = R slices fit in one
@@ -436,7 +424,7 @@ __device__ __forceinline__ void pf_finish(const hvec (&w)[R], const fvec& pv, co
 // is summed and updated, so its memory latency overlaps this group's fp64
 // work.  The last iteration re-reads its own group instead of running past
 // the end (the values are not used).
-template <int R, bool kNt>
+template <int R>
 __device__ void pf_run(int64_t gi, int64_t end, int64_t step, const SrcArgs& src, const FusedPtrs& f,
                        const AdamScalars& c, double& sq, int& bad) {
     if (gi >= end) return;
@@ -452,26 +440,25 @@ __device__ void pf_run(int64_t gi, int64_t end, int64_t step, const SrcArgs& src
         const fvec pc = p, mc = m, vc = v;
         pf_load<R>(w, p, m, v, src, f, gl * kV);
         __builtin_amdgcn_sched_barrier(0);  // keep the next group's loads ahead of this group's work
-        pf_finish<R, kNt>(wc, pc, mc, vc, src, f, c, gi * kV, sq, bad);
+        pf_finish<R>(wc, pc, mc, vc, src, f, c, gi * kV, sq, bad);
         if (gn >= end) break;
         gi = gn;
     }
 }
 
-template <int R, bool kNt>
+template <int R>
 __device__ __forceinline__ bool pf_dispatch(int nd, int64_t gi, int64_t end, int64_t step, const SrcArgs& src,
                                             const FusedPtrs& f, const AdamScalars& c, double& sq, int& bad) {
     if constexpr (R >= 1) {
         if (nd == R) {
-            pf_run<R, kNt>(gi, end, step, src, f, c, sq, bad);
+            pf_run<R>(gi, end, step, src, f, c, sq, bad);
             return true;
         }
-        return pf_dispatch<R - 1, kNt>(nd, gi, end, step, src, f, c, sq, bad);
+        return pf_dispatch<R - 1>(nd, gi, end, step, src, f, c, sq, bad);
     }
     return false;
 }
 
-template <bool kNt>
 __global__ void __launch_bounds__(kBlock) ZDP_FUSED_ATTR fused_step_kernel(SrcArgs src, AdamArgs a, Partials ws) {
     // Scalars of the step being taken, t = committed + 1 (identical in every
     // lane and workgroup: the same IEEE operations on the same inputs).
@@ -506,7 +493,7 @@ __global__ void __launch_bounds__(kBlock) ZDP_FUSED_ATTR fused_step_kernel(SrcAr
         GroupIter it(ngroups);
         const FusedPtrs f{pin, min_, vin, pout, mout, vout, ag};
         const int64_t endf = it.end < nfull ? it.end : nfull;
-        done = pf_dispatch<kUnroll, kNt>(src.nd, it.gi, endf, it.step, src, f, c, sq, bad);
+        done = pf_dispatch<kUnroll>(src.nd, it.gi, endf, it.step, src, f, c, sq, bad);
         if (done && ngroups > nfull) {
             // the ragged tail group, by the lane whose sequence contains it
             const int64_t g = nfull;
@@ -550,10 +537,10 @@ __global__ void __launch_bounds__(kBlock) ZDP_FUSED_ATTR fused_step_kernel(SrcAr
                 mw[e] = mo[e];
                 vw[e] = vo[e];
             }
-            stg_p<kNt>(reinterpret_cast<fvec*>(pout + j), pw);
-            stg_p<kNt>(reinterpret_cast<fvec*>(mout + j), mw);
-            stg_p<kNt>(reinterpret_cast<fvec*>(vout + j), vw);
-            if (ag != nullptr) stg_p<kNt>(reinterpret_cast<hvec*>(ag + j), pack_v(po));
+            stg(reinterpret_cast<fvec*>(pout + j), pw);
+            stg(reinterpret_cast<fvec*>(mout + j), mw);
+            stg(reinterpret_cast<fvec*>(vout + j), vw);
+            if (ag != nullptr) stg(reinterpret_cast<hvec*>(ag + j), pack_v(po));
         } else {
             for (int64_t e = j; e < src.n; ++e) {
                 const double s = sum_slices1(src.win + e, src.stride, src.nd);
@@ -638,7 +625,7 @@ int resident_blocks(KernelId id) {
     const void* fn = nullptr;
     switch (id) {
         case kReduce: fn = reinterpret_cast<const void*>(reduce_owned_kernel); break;
-        case kFused: fn = reinterpret_cast<const void*>(fused_step_kernel<true>); break;
+        case kFused: fn = reinterpret_cast<const void*>(fused_step_kernel); break;
         case kEmit: fn = reinterpret_cast<const void*>(emit_kernel); break;
         case kRestore: fn = reinterpret_cast<const void*>(restore_kernel); break;
     }
@@ -803,14 +790,9 @@ int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st, const ze
     a.wd = hp->weight_decay;
     a.ag = ag;
     const int grid = grid_for(kFused, n);
-    const bool plain_stores = src->nd >= kPlainStoreMinNd && src->nd <= kPlainStoreMaxNd;
     (void)hipGetLastError();
-    if (plain_stores)
-        fused_step_kernel<false><<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(make_src(src), a,
-                                                                                     make_ws(workspace));
-    else
-        fused_step_kernel<true><<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(make_src(src), a,
-                                                                                    make_ws(workspace));
+    fused_step_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(make_src(src), a,
+                                                                              make_ws(workspace));
     return finish_launch();
 }
 
