@@ -43,6 +43,10 @@ def parse():
                     help="gradient sets cycled through (0 = enough to exceed 1 GB of slices)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--max-grad-norm", type=float, default=0.0,
+                    help="> 0: time the two-pass clipped step instead of the fused step")
+    ap.add_argument("--dynamic-scale", type=int, default=0,
+                    help="> 0: dynamic loss scaling with this growth interval")
     return ap.parse_args()
 
 
@@ -158,7 +162,8 @@ def main():
         master = torch.empty(S, dtype=torch.float32, device=dev)
         gen.device_fill_params(master, w.seed + roff, w.param_sigma, rvalid)
         shards.append(OwnedShard(master, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
-                                 weight_decay=w.weight_decay))
+                                 weight_decay=w.weight_decay, max_grad_norm=args.max_grad_norm,
+                                 scale_interval=args.dynamic_scale, loss_scale=w.loss_scale))
         ag_offs.append(roff if full else r * S)
         shards[r].emit(ag, ag_offs[r])
         del master
@@ -168,8 +173,14 @@ def main():
     stream = torch.cuda.current_stream()
     srcs = [B.grad_src(t, S, 0, S, w.nd, w.loss_scale) for t in gsets]
 
+    clipped = args.max_grad_norm > 0
+
     def launch(i, restore=True):
         sh = shards[i % n_shards]
+        if clipped:  # two passes; a skipped step leaves the window untouched
+            B.adam_step_clipped(srcs[i % rot], sh.state, sh.hp, sh.grad_buf, ag, ag_offs[i % n_shards],
+                                sh.workspace, stream)
+            return
         B.adam_step(srcs[i % rot], sh.state, sh.hp, ag, ag_offs[i % n_shards], sh.workspace, stream)
         if restore:
             B.restore_skipped(sh.state, S, ag, ag_offs[i % n_shards], stream)
@@ -203,10 +214,12 @@ def main():
         sys.exit(1)
 
     calibration_copy(torch, dev)
-    traffic = measured_traffic(w.key)
+    traffic = None if clipped else measured_traffic(w.key)
 
     ms_step = wall * 1e3 / args.steps
-    bytes_elem = 2 * w.nd + 26
+    # algorithmic bytes per owned element: fused 2*Nd + 26; clipped
+    # (2*Nd + 4) for the reduce pass + 30 for the update pass
+    bytes_elem = 2 * w.nd + (34 if clipped else 26)
     achieved = bytes_elem * S / (kern_avg * 1e-3) / 1e9
     log(f"fused kernel: avg {kern_avg * 1e3:.1f} us over {args.steps} back-to-back launches; "
         f"step {ms_step * 1e3:.1f} us; {achieved:.0f} GB/s")
@@ -240,6 +253,8 @@ def main():
             "shards_rotated": n_shards,
             "allgather": "full flat buffer" if full else "one window per shard",
             "step_hbm_gbs": bytes_elem * S / (ms_step * 1e-3) / 1e9,
+            "max_grad_norm": args.max_grad_norm,
+            "dynamic_scale_interval": args.dynamic_scale,
         },
         "roofline": {
             "bound": "hbm",
@@ -252,7 +267,7 @@ def main():
             "traffic": None if traffic is None else traffic / (kern_avg * 1e-3) / 1e9,
             "traffic_bytes_per_launch": traffic,
             "algorithmic_bytes_per_launch": bytes_elem * S,
-            "kernel": "fused_step_kernel",
+            "kernel": "reduce_owned_kernel + clipped_update_kernel" if clipped else "fused_step_kernel",
             "kernel_avg_us": kern_avg * 1e3,
             "kernel_fingerprint": kernel_fingerprint(),
         },

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define ZERO_DP_ABI_VERSION 1
+#define ZERO_DP_ABI_VERSION 2
 
 /* ---- status codes --------------------------------------------------- */
 #define ZERO_OK          0
@@ -181,18 +181,21 @@ int zero_reduce_owned(const zero_grad_src* src, float* grad_out, int32_t* overfl
  * zero_ctl_init() on the host and copy it to the device.
  */
 typedef struct zero_step_ctl {
-    int32_t cur;        /* index (0/1) of the buffers holding the committed state */
-    int32_t t;          /* committed optimizer steps */
-    int32_t overflow;   /* 1 if the last step was skipped (inf/NaN gradient) */
-    int32_t reserved;
-    double beta1_pow;   /* beta1^t, as t successive products from 1.0 */
-    double beta2_pow;   /* beta2^t */
-    double sumsq;       /* sum g^2 of the last step (meaningful when overflow == 0) */
-    int64_t skipped;    /* number of skipped steps */
+    int32_t cur;         /* index (0/1) of the buffers holding the committed state */
+    int32_t t;           /* committed optimizer steps */
+    int32_t overflow;    /* 1 if the last step was skipped (inf/NaN gradient) */
+    int32_t good_steps;  /* dynamic loss scaling: consecutive clean steps since the last change */
+    double beta1_pow;    /* beta1^t, as t successive products from 1.0 */
+    double beta2_pow;    /* beta2^t */
+    double sumsq;        /* sum g^2 of the last step (meaningful when overflow == 0) */
+    int64_t skipped;     /* number of skipped steps */
+    double loss_scale;   /* dynamic loss scaling: the scale the next step's gradients carry */
+    double clip_coef;    /* coefficient the last clipped step applied (1 = not clipped) */
 } zero_step_ctl;
 
-/* Fills *ctl (host) with t = 0, cur = 0, powers 1.0. */
-void zero_ctl_init(zero_step_ctl* ctl);
+/* Fills *ctl (host) with t = 0, cur = 0, powers 1.0, loss_scale as given
+ * (used only with dynamic loss scaling), clip_coef 1. */
+void zero_ctl_init(zero_step_ctl* ctl, double loss_scale);
 
 typedef struct zero_adam_state {
     float* master[2];      /* device float[n] each, 16-byte aligned */
@@ -202,13 +205,28 @@ typedef struct zero_adam_state {
 } zero_adam_state;
 
 /* Hyperparameters; beta1/beta2 must stay constant over the life of a ctl.
- * weight_decay is decoupled (AdamW): p <- p*(1 - lr*wd) - ... ; 0 = Adam. */
+ * weight_decay is decoupled (AdamW): p <- p*(1 - lr*wd) - ... ; 0 = Adam.
+ *
+ * Dynamic loss scaling (scale_interval > 0; the practice of the
+ * mixed-precision training the anthology note's "Connections" cites): the
+ * gradients carry ctl->loss_scale (src->loss_scale is then ignored); after
+ * each step the last workgroup multiplies the scale by scale_backoff if the
+ * step overflowed (and resets good_steps), else counts the clean step and
+ * multiplies the scale by scale_growth after scale_interval of them.
+ *
+ * Global-norm clipping (max_grad_norm > 0) is applied only by
+ * zero_adam_step_clipped, which needs the norm before the update. */
 typedef struct zero_adam_hp {
     double lr;
-    double beta1;         /* in [0, 1) */
-    double beta2;         /* in [0, 1) */
-    double eps;           /* > 0 */
-    double weight_decay;  /* >= 0 */
+    double beta1;          /* in [0, 1) */
+    double beta2;          /* in [0, 1) */
+    double eps;            /* > 0 */
+    double weight_decay;   /* >= 0 */
+    double max_grad_norm;  /* > 0 for zero_adam_step_clipped; must be 0 for zero_adam_step */
+    double scale_growth;   /* > 0 (e.g. 2), used when scale_interval > 0 */
+    double scale_backoff;  /* > 0 (e.g. 0.5), used when scale_interval > 0 */
+    int32_t scale_interval;/* 0: static scale src->loss_scale; > 0: dynamic scaling */
+    int32_t reserved;      /* must be 0 */
 } zero_adam_hp;
 
 /* ---- fused step (hot path) -------------------------------------------
@@ -235,6 +253,28 @@ typedef struct zero_adam_hp {
 int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st,
                    const zero_adam_hp* hp, uint16_t* allgather, int64_t allgather_off,
                    void* workspace, void* stream);
+/* (hp->max_grad_norm must be 0 here; dynamic loss scaling is applied when
+ * hp->scale_interval > 0.) */
+
+/* ---- clipped step (two passes) ----------------------------------------
+ * Global-norm clipping needs the norm of the whole gradient before any
+ * element is updated, so this path materialises the reduced gradient:
+ *   pass 1: g32_j = fp32(s_j * (1/L)) into grad_buf, flag, sumsq = sum g32^2
+ *           (float64, deterministic order);
+ *   pass 2: if the flag is set, the step is skipped (state and all-gather
+ *           window untouched, no restore needed); otherwise
+ *           coef = min(1, max_grad_norm / (sqrt(sumsq) + 1e-6)) and the
+ *           update of zero_adam_step runs on g = g32 * coef (float64), then
+ *           the commit; ctl->clip_coef records coef.
+ * L is src->loss_scale or, with dynamic scaling, ctl->loss_scale.
+ * Traffic (2*Nd + 4) + 30 bytes per element instead of 2*Nd + 26.
+ *   grad_buf: device float[n], 16-byte aligned, must not overlap any other
+ *   operand.  Other arguments as for zero_adam_step; hp->max_grad_norm > 0.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EALIAS, ZERO_EHIP.
+ */
+int zero_adam_step_clipped(const zero_grad_src* src, const zero_adam_state* st,
+                           const zero_adam_hp* hp, float* grad_buf, uint16_t* allgather,
+                           int64_t allgather_off, void* workspace, void* stream);
 
 /* Re-emits allgather[off + j] = fp16_RNE(master[ctl->cur][j]) for j < n when
  * ctl->overflow == 1 (the step was skipped), and does nothing otherwise; the

@@ -14,4 +14,7 @@ from .zero_oracle import (  # noqa: F401
     adam_update,
     emit,
     OwnedShard,
+    scaler_update,
+    clip_coefficient,
+    clipped_gradient,
 )

@@ -40,6 +40,15 @@ accumulation precision, the overflow policy) the plainest reading is taken:
                 p' = p*(1-lr*wd) - (lr/(1-b1^t)) * q
             b1^t and b2^t are running products (t multiplications from 1.0).
 * skip:     an overflowing step stores nothing and does not advance t.
+* scaler:   dynamic loss scaling (mixed-precision practice): an overflowing
+            step multiplies the scale by the backoff factor and resets the
+            clean-step count; every `interval` consecutive clean steps
+            multiply it by the growth factor.  The gradients of a step carry
+            the scale in force when the step starts.
+* clip:     global-norm clipping needs the norm before the update, so the
+            reduced gradient is materialised as fp32 (g32 = fp32(s * (1/L))),
+            its norm is sqrt(sum g32^2) (exact sum, rounded once), and the
+            update uses g32 * min(1, max_norm / (norm + 1e-6)) in float64.
 * emit:     allgather[off + j] = fp16 round-to-nearest-even of the fp32 master.
 * plan:     tensors packed in list order; S = A*ceil(Psi/(Nd*A)); rank r owns
             [r*S, (r+1)*S); the padding sits at the tail of rank Nd-1.
@@ -229,13 +238,55 @@ def emit(master: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # One rank's owned shard across steps, with the skip/commit rule.
 # --------------------------------------------------------------------------
+# --------------------------------------------------------------------------
+# Dynamic loss scaling and global-norm clipping (the pages cite
+# mixed-precision training -- anthology note, "Connections" -- whose loss
+# scale these implement; the pages themselves give no policy).
+# --------------------------------------------------------------------------
+def scaler_update(scale: float, good: int, overflow: bool, growth: float, backoff: float,
+                  interval: int):
+    """Next (scale, good_steps) after a step with the given overflow flag."""
+    if overflow:
+        return scale * backoff, 0
+    good += 1
+    if good == interval:
+        return scale * growth, 0
+    return scale, good
+
+
+CLIP_EPS = 1e-6
+
+
+def clip_coefficient(sumsq: float, max_norm: float) -> float:
+    """min(1, max_norm / (sqrt(sumsq) + 1e-6)), each step one IEEE float64
+    operation."""
+    c = max_norm / (math.sqrt(sumsq) + CLIP_EPS)
+    return c if c < 1.0 else 1.0
+
+
+def clipped_gradient(s: np.ndarray, loss_scale: float, max_norm: float):
+    """Two-pass gradient of the clipping path: returns (g, overflow, sumsq,
+    coef) with g the float64 gradient the update uses."""
+    inv = 1.0 / float(loss_scale)
+    overflow = bool(np.any(~np.isfinite(s)))
+    with np.errstate(invalid="ignore", over="ignore"):
+        g32 = (s * inv).astype(F32)
+    if overflow:
+        return None, True, float("nan"), float("nan")
+    g64 = g32.astype(F64)
+    sumsq = math.fsum((g64 * g64).tolist())
+    coef = clip_coefficient(sumsq, max_norm)
+    return g64 * coef, False, sumsq, coef
+
+
 class OwnedShard:
     """Owned-partition state of one rank: fp32 master/m/v of S elements, the
     committed step count t and the running beta powers.  ``step`` performs
     reduce -> unscale/flag/sumsq -> Adam -> commit (or skip) -> emit."""
 
     def __init__(self, master: np.ndarray, lr=1e-3, beta1=0.9, beta2=0.999,
-                 eps=1e-8, weight_decay=0.0, state_dtype=F32):
+                 eps=1e-8, weight_decay=0.0, state_dtype=F32, max_grad_norm=0.0,
+                 scale_interval=0, scale_growth=2.0, scale_backoff=0.5, loss_scale=65536.0):
         self.p = np.array(master, dtype=state_dtype, copy=True)
         self.m = np.zeros_like(self.p)
         self.v = np.zeros_like(self.p)
@@ -246,17 +297,39 @@ class OwnedShard:
         self.b2_pow = 1.0
         self.flags: List[int] = []
         self.sumsq: List[float] = []
+        self.max_grad_norm = float(max_grad_norm)
+        self.scale_interval = int(scale_interval)
+        self.scale_growth = float(scale_growth)
+        self.scale_backoff = float(scale_backoff)
+        self.scale = float(loss_scale)   # used when scale_interval > 0
+        self.good_steps = 0
+        self.scales: List[float] = []
+        self.coefs: List[float] = []
 
     def window(self) -> np.ndarray:
         return emit(self.p.astype(F32))
 
-    def step(self, slices: np.ndarray, loss_scale: float):
+    def step(self, slices: np.ndarray, loss_scale: float = None):
+        """One step.  With dynamic scaling (scale_interval > 0) the slices
+        carry self.scale and `loss_scale` is ignored."""
+        dynamic = self.scale_interval > 0
+        L = self.scale if dynamic else float(loss_scale)
+        self.scales.append(L)
         s = reduce_owned(slices)
         if s.shape[0] != self.p.shape[0]:
             raise ValueError("window size mismatch")
-        g, overflow, sq = unscale(s, loss_scale)
+        if self.max_grad_norm > 0:
+            g, overflow, sq, coef = clipped_gradient(s, L, self.max_grad_norm)
+        else:
+            g, overflow, sq = unscale(s, L)
+            coef = 1.0
         self.flags.append(int(overflow))
         self.sumsq.append(sq)
+        self.coefs.append(coef)
+        if dynamic:
+            self.scale, self.good_steps = scaler_update(self.scale, self.good_steps, overflow,
+                                                        self.scale_growth, self.scale_backoff,
+                                                        self.scale_interval)
         if overflow:
             return True, sq
         sc = step_scalars(self.hp["lr"], self.hp["beta1"], self.hp["beta2"],

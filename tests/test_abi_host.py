@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(L):
     for name in declared:
         assert hasattr(L, name), name
     assert declared == set(B.EXPORTED)
-    assert L.zero_abi_version() == 1
+    assert L.zero_abi_version() == B.ABI_VERSION == 2
 
 
 def test_strerror(L):
@@ -122,10 +122,10 @@ def test_memory_model_errors(L):
 
 
 def test_ctl_init():
-    c = B.ctl_from_bytes(B.ctl_init_bytes())
-    assert c == {"cur": 0, "t": 0, "overflow": 0, "beta1_pow": 1.0, "beta2_pow": 1.0, "sumsq": 0.0,
-                 "skipped": 0}
-    assert B.CTL_BYTES == 48
+    c = B.ctl_from_bytes(B.ctl_init_bytes(4096.0))
+    assert c == {"cur": 0, "t": 0, "overflow": 0, "good_steps": 0, "beta1_pow": 1.0, "beta2_pow": 1.0,
+                 "sumsq": 0.0, "skipped": 0, "loss_scale": 4096.0, "clip_coef": 1.0}
+    assert B.CTL_BYTES == 64
 
 
 # Argument validation of the asynchronous calls: every case below fails
@@ -158,8 +158,15 @@ def test_step_validation(L):
     assert step(src=B.grad_src(A, 2**62, 0, 64, 4, 1024.0)) == B.ZERO_EOVERFLOW
     for bad in (B.adam_hp(-1, 0.9, 0.999, 1e-8, 0), B.adam_hp(1e-3, 1.0, 0.999, 1e-8, 0),
                 B.adam_hp(1e-3, 0.9, 1.0, 1e-8, 0), B.adam_hp(1e-3, 0.9, 0.999, 0.0, 0),
-                B.adam_hp(1e-3, 0.9, 0.999, 1e-8, -0.1), B.adam_hp(float("nan"), 0.9, 0.999, 1e-8, 0)):
+                B.adam_hp(1e-3, 0.9, 0.999, 1e-8, -0.1), B.adam_hp(float("nan"), 0.9, 0.999, 1e-8, 0),
+                B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0, max_grad_norm=1.0),  # clipping needs the 2-pass call
+                B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0, scale_interval=-1),
+                B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0, scale_interval=5, scale_growth=0.0),
+                B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0, scale_interval=5, scale_backoff=float("inf"))):
         assert step(hpp=bad) == B.ZERO_EINVAL
+    odd = B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0)
+    odd.reserved = 1
+    assert step(hpp=odd) == B.ZERO_EINVAL
     assert step(state=_state(ctl=None)) == B.ZERO_EINVAL
     assert step(state=_state(base=(1 << 24) + 4)) == B.ZERO_EALIGN
     assert step(ws=None) == B.ZERO_EINVAL
@@ -174,6 +181,22 @@ def test_step_validation(L):
     assert step(state=_state(base=A)) == B.ZERO_EALIAS
     # misaligned all-gather window
     assert step(ag=1 << 29, off=3) == B.ZERO_EALIGN
+
+
+def test_clipped_validation(L):
+    hp = B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0, max_grad_norm=1.0)
+    src = B.grad_src(A, 64, 0, 64, 4, 1024.0)
+    st = _state()
+
+    def step(hpp=hp, gbuf=1 << 27, ag=None, off=0, ws=1 << 28):
+        return L.zero_adam_step_clipped(C.byref(src), C.byref(st), C.byref(hpp), gbuf, ag, off, ws, None)
+
+    assert step(gbuf=None) == B.ZERO_EINVAL
+    assert step(gbuf=(1 << 27) + 4) == B.ZERO_EALIGN
+    assert step(gbuf=1 << 24) == B.ZERO_EALIAS          # overlaps the master
+    assert step(gbuf=A) == B.ZERO_EALIAS                # overlaps the gradient slices
+    assert step(hpp=B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0)) == B.ZERO_EINVAL  # max_grad_norm must be > 0
+    assert step(hpp=B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0, max_grad_norm=float("inf"))) == B.ZERO_EINVAL
 
 
 def test_other_validation(L):

@@ -1,0 +1,88 @@
+"""GPU parity of dynamic loss scaling and global-norm clipping against the
+oracle.  Same bar as the fused step: flags, step counts and the scale
+trajectory bit-exact; fp32 state within 1e-5 relative per element; fp16
+window within 1 ulp; sum of g^2 and the clip coefficient within 1e-12."""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import gen
+
+from gpu_util import F16, F32, GpuShardRun, assert_fp16_close, assert_state_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(n, nd, steps, seed, hp, bad_steps=(), sigma=1e-3, static_L=1024.0):
+    g = np.random.default_rng(seed)
+    master0 = (g.standard_normal(n) * 0.02).astype(F32)
+    sh = oracle.OwnedShard(master0, **hp)
+    run = GpuShardRun(master0, nd, hp)
+    dynamic = hp.get("scale_interval", 0) > 0
+    for step in range(1, steps + 1):
+        L = sh.scale if dynamic else static_L
+        sl = gen.host_grad_slices(seed, step, 0, nd, n, 0, n, sigma, L)
+        if step in bad_steps:
+            sl[step % nd, (step * 7919) % max(n, 1)] = np.nan if step % 2 else np.inf
+        ovf, sq = sh.step(sl, static_L)
+        ctl, p, m, v, bits = run.step(sl, static_L)
+        tag = f"n={n} nd={nd} step={step}"
+        assert ctl["overflow"] == int(ovf) and ctl["t"] == sh.t, tag
+        if dynamic:
+            assert ctl["loss_scale"] == sh.scale and ctl["good_steps"] == sh.good_steps, tag
+        for got, want, nm in ((p, sh.p, "p"), (m, sh.m, "m"), (v, sh.v, "v")):
+            assert_state_close(got, want, f"{tag} {nm}")
+        assert_fp16_close(run.window(bits), sh.window().view(np.uint16), f"{tag} window")
+        assert run.guards_intact(bits), tag
+        if not ovf:
+            assert ctl["sumsq"] == pytest.approx(sq, rel=1e-12, abs=1e-300), tag
+            assert ctl["clip_coef"] == pytest.approx(sh.coefs[-1], rel=1e-12), tag
+    return sh, run
+
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+
+
+@pytest.mark.parametrize("nd", [1, 4, 9])
+def test_dynamic_scaling_fused(nd):
+    hp = dict(HP, scale_interval=2, loss_scale=4096.0)
+    sh, _ = _run(20003, nd, 9, 40 + nd, hp, bad_steps=(2, 6, 7))
+    assert sh.flags == [0, 1, 0, 0, 0, 1, 1, 0, 0]
+    assert sh.scales == [4096.0, 4096.0, 2048.0, 2048.0, 4096.0, 4096.0, 2048.0, 1024.0, 1024.0]
+
+
+@pytest.mark.parametrize("max_norm", [1e-3, 1e9])
+@pytest.mark.parametrize("n,nd", [(5003, 3), (65536 + 12, 8)])
+def test_clipped_step(n, nd, max_norm):
+    hp = dict(HP, max_grad_norm=max_norm)
+    sh, _ = _run(n, nd, 5, 50 + nd, hp, bad_steps=(3,))
+    assert sh.flags == [0, 0, 1, 0, 0]
+    if max_norm < 1:
+        assert max(c for c in sh.coefs if c == c) < 1.0  # clipping was active
+    else:
+        assert all(c == 1.0 for c in sh.coefs if c == c)
+
+
+def test_clipped_adamw_dynamic_scaling():
+    hp = dict(HP, weight_decay=0.01, max_grad_norm=5e-3, scale_interval=3, loss_scale=8192.0)
+    sh, _ = _run(30000, 16, 8, 61, hp, bad_steps=(4,), sigma=1e-4)
+    assert sh.flags == [0, 0, 0, 1, 0, 0, 0, 0]
+    assert sh.scales[-1] != sh.scales[0]
+
+
+def test_clipped_skip_leaves_window_and_state():
+    """An overflowing clipped step touches neither the state nor the fp16
+    window (no restore launch is made for the clipped path)."""
+    n, nd = 4099, 5
+    g = np.random.default_rng(7)
+    master0 = (g.standard_normal(n) * 0.02).astype(F32)
+    run = GpuShardRun(master0, nd, dict(HP, max_grad_norm=0.01))
+    sl = gen.host_grad_slices(7, 1, 0, nd, n, 0, n, 1e-3, 1024.0)
+    _, p1, m1, v1, bits1 = run.step(sl, 1024.0)
+    sl2 = sl.copy()
+    sl2[4, n - 1] = -np.inf
+    ctl, p2, m2, v2, bits2 = run.step(sl2, 1024.0)
+    assert ctl["overflow"] == 1 and ctl["t"] == 1 and ctl["skipped"] == 1
+    for a, b in ((p1, p2), (m1, m2), (v1, v2)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(bits1, bits2)

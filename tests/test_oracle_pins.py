@@ -425,3 +425,103 @@ def test_planted_reduce_mistakes_are_caught():
         assert not np.array_equal(fp16_sum(sl), exact)
     assert not np.array_equal(oracle.reduce_owned(sl[:-1]), exact)
     assert np.array_equal(oracle.reduce_owned(sl), exact)
+
+
+# ----------------------------------------------------------------- loss scaling and clipping
+def test_scaler_matches_torch_amp_update():
+    """The dynamic loss-scale rule against torch's own scaler update
+    (torch._amp_update_scale_), over random overflow sequences."""
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(31)
+    for interval in (1, 3, 7):
+        flags = g.random(60) < 0.25
+        scale, good = 2.0 ** 16, 0
+        ts = torch.tensor([scale], dtype=torch.float32)
+        tt = torch.zeros(1, dtype=torch.int32)
+        for f in flags:
+            scale, good = oracle.scaler_update(scale, good, bool(f), 2.0, 0.5, interval)
+            torch._amp_update_scale_(ts, tt, torch.tensor([float(f)]), 2.0, 0.5, interval)
+            assert scale == float(ts.item()) and good == int(tt.item())
+
+
+def test_clip_matches_torch_clip_grad_norm():
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(32)
+    for max_norm in (1e-4, 0.05, 1.0, 1e9):
+        sl = (g.standard_normal((5, 3000)) * 0.3 * 1024).astype(F16)
+        s = oracle.reduce_owned(sl)
+        gg, ovf, sq, coef = oracle.clipped_gradient(s, 1024.0, max_norm)
+        assert not ovf
+        g32 = (s / 1024.0).astype(F32)
+        t = torch.zeros(3000, dtype=torch.float64, requires_grad=True)
+        t.grad = torch.tensor(g32.astype(F64))
+        norm = torch.nn.utils.clip_grad_norm_([t], max_norm, foreach=False)
+        assert float(norm) == pytest.approx(math.sqrt(sq), rel=1e-15)
+        assert np.allclose(gg, t.grad.numpy(), rtol=1e-15, atol=0)
+        assert coef == (1.0 if max_norm >= math.sqrt(sq) + 1e-6 else pytest.approx(max_norm / (math.sqrt(sq) + 1e-6), rel=1e-15))
+    bad = (g.standard_normal((3, 50)) * 100).astype(F16)
+    bad[1, 7] = np.inf
+    assert oracle.clipped_gradient(oracle.reduce_owned(bad), 1024.0, 1.0)[1]
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.01])
+def test_clipped_adam_matches_torch(wd):
+    """float64 state: oracle's clipped steps against torch clip_grad_norm_
+    followed by torch Adam/AdamW, 8 steps."""
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(33)
+    n, L, max_norm = 400, 1024.0, 0.02
+    p0 = g.standard_normal(n) * 0.02
+    sh = oracle.OwnedShard(p0, weight_decay=wd, state_dtype=F64, max_grad_norm=max_norm)
+    t = torch.tensor(p0, dtype=torch.float64, requires_grad=True)
+    opt = (torch.optim.AdamW([t], lr=1e-3, weight_decay=wd, foreach=False) if wd else
+           torch.optim.Adam([t], lr=1e-3, foreach=False))
+    for _ in range(8):
+        sl = (g.standard_normal((4, n)) * 1e-3 * L).astype(F16)
+        sh.step(sl, L)
+        t.grad = torch.tensor((oracle.reduce_owned(sl) / L).astype(F32).astype(F64))
+        torch.nn.utils.clip_grad_norm_([t], max_norm, foreach=False)
+        opt.step()
+    assert min(sh.coefs) < 1.0
+    assert np.all(np.abs(sh.p - t.detach().numpy()) <= 1e-12)
+
+
+def test_dynamic_scaling_sequence():
+    """Overflows back the scale off and skip the step; clean runs grow it."""
+    g = np.random.default_rng(34)
+    n = 64
+    sh = oracle.OwnedShard(np.zeros(n, F32), scale_interval=2, loss_scale=1024.0)
+    flags = [0, 1, 0, 0, 0, 1, 1, 0, 0]
+    for f in flags:
+        sl = (g.standard_normal((3, n)) * 1e-3 * sh.scale).astype(F16)
+        if f:
+            sl[0, 5] = np.nan
+        sh.step(sl)
+    assert sh.flags == flags and sh.t == flags.count(0)
+    assert sh.scales == [1024.0, 1024.0, 512.0, 512.0, 1024.0, 1024.0, 512.0, 256.0, 256.0]
+    assert sh.scale == 512.0
+
+
+@pytest.mark.parametrize("kind", ["eps_inside_sqrt", "max_instead_of_min", "clip_before_unscale"])
+def test_planted_clip_mistakes_are_caught(kind):
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(35)
+    sl = (g.standard_normal((5, 2000)) * 0.3 * 1024).astype(F16)
+    s = oracle.reduce_owned(sl)
+    g32 = (s / 1024.0).astype(F32).astype(F64)
+    sq = math.fsum((g32 * g32).tolist())
+    caught = False
+    for max_norm in (1e-3, 1e9):
+        if kind == "eps_inside_sqrt":
+            c = min(1.0, max_norm / math.sqrt(sq + 1e-6))
+            mine = g32 * c
+        elif kind == "max_instead_of_min":
+            mine = g32 * max(1.0, max_norm / (math.sqrt(sq) + 1e-6))
+        else:
+            c = min(1.0, max_norm / (math.sqrt(sq) * 1024.0 + 1e-6))
+            mine = g32 * c
+        t = torch.zeros(2000, dtype=torch.float64, requires_grad=True)
+        t.grad = torch.tensor(g32.copy())
+        torch.nn.utils.clip_grad_norm_([t], max_norm, foreach=False)
+        caught |= not np.allclose(mine, t.grad.numpy(), rtol=1e-15, atol=0)
+    assert caught

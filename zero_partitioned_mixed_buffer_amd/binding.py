@@ -25,8 +25,9 @@ ZERO_EHIP = -6
 EXPORTED = (
     "zero_strerror", "zero_last_hip_error", "zero_abi_version", "zero_plan_partitions",
     "zero_memory_model", "zero_workspace_bytes", "zero_reduce_owned", "zero_ctl_init",
-    "zero_adam_step", "zero_restore_skipped", "zero_emit_fp16",
+    "zero_adam_step", "zero_adam_step_clipped", "zero_restore_skipped", "zero_emit_fp16",
 )
+ABI_VERSION = 2
 
 
 class ZeroError(RuntimeError):
@@ -59,9 +60,9 @@ class GradSrc(C.Structure):
 
 
 class StepCtl(C.Structure):
-    _fields_ = [("cur", C.c_int32), ("t", C.c_int32), ("overflow", C.c_int32), ("reserved", C.c_int32),
+    _fields_ = [("cur", C.c_int32), ("t", C.c_int32), ("overflow", C.c_int32), ("good_steps", C.c_int32),
                 ("beta1_pow", C.c_double), ("beta2_pow", C.c_double), ("sumsq", C.c_double),
-                ("skipped", C.c_int64)]
+                ("skipped", C.c_int64), ("loss_scale", C.c_double), ("clip_coef", C.c_double)]
 
 
 class AdamState(C.Structure):
@@ -70,7 +71,9 @@ class AdamState(C.Structure):
 
 
 class AdamHp(C.Structure):
-    _fields_ = [(k, C.c_double) for k in ("lr", "beta1", "beta2", "eps", "weight_decay")]
+    _fields_ = [(k, C.c_double) for k in ("lr", "beta1", "beta2", "eps", "weight_decay", "max_grad_norm",
+                                          "scale_growth", "scale_backoff")] + \
+               [("scale_interval", C.c_int32), ("reserved", C.c_int32)]
 
 
 def lib():
@@ -92,16 +95,18 @@ def lib():
     L.zero_memory_model.argtypes = [C.c_double, C.c_int32, C.c_int32, C.c_int32, C.POINTER(MemReport)]
     L.zero_workspace_bytes.restype = C.c_int64
     L.zero_reduce_owned.argtypes = [C.POINTER(GradSrc), P, P, P, P, P]
-    L.zero_ctl_init.argtypes = [C.POINTER(StepCtl)]
+    L.zero_ctl_init.argtypes = [C.POINTER(StepCtl), C.c_double]
     L.zero_ctl_init.restype = None
     L.zero_adam_step.argtypes = [C.POINTER(GradSrc), C.POINTER(AdamState), C.POINTER(AdamHp), P,
                                  C.c_int64, P, P]
+    L.zero_adam_step_clipped.argtypes = [C.POINTER(GradSrc), C.POINTER(AdamState), C.POINTER(AdamHp), P, P,
+                                         C.c_int64, P, P]
     L.zero_restore_skipped.argtypes = [C.POINTER(AdamState), C.c_int64, P, C.c_int64, P]
     L.zero_emit_fp16.argtypes = [P, C.c_int64, P, C.c_int64, P]
     for name in ("zero_plan_partitions", "zero_memory_model", "zero_reduce_owned", "zero_adam_step",
-                 "zero_restore_skipped", "zero_emit_fp16"):
+                 "zero_adam_step_clipped", "zero_restore_skipped", "zero_emit_fp16"):
         getattr(L, name).restype = C.c_int
-    if L.zero_abi_version() != 1:
+    if L.zero_abi_version() != ABI_VERSION:
         raise RuntimeError("libzero_dp.so ABI version mismatch")
     _lib = L
     return L
@@ -157,15 +162,15 @@ def workspace_bytes() -> int:
     return int(lib().zero_workspace_bytes())
 
 
-def ctl_init_bytes() -> bytes:
+def ctl_init_bytes(loss_scale: float = 65536.0) -> bytes:
     c = StepCtl()
-    lib().zero_ctl_init(C.byref(c))
+    lib().zero_ctl_init(C.byref(c), float(loss_scale))
     return bytes(c)
 
 
 def ctl_from_bytes(b: bytes) -> dict:
     c = StepCtl.from_buffer_copy(b)
-    return {name: getattr(c, name) for name, _ in StepCtl._fields_ if name != "reserved"}
+    return {name: getattr(c, name) for name, _ in StepCtl._fields_}
 
 
 CTL_BYTES = C.sizeof(StepCtl)
@@ -186,8 +191,11 @@ def adam_state(master: Sequence, exp_avg: Sequence, exp_avg_sq: Sequence, ctl) -
     return s
 
 
-def adam_hp(lr: float, beta1: float, beta2: float, eps: float, weight_decay: float) -> AdamHp:
-    return AdamHp(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay))
+def adam_hp(lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+            max_grad_norm: float = 0.0, scale_interval: int = 0, scale_growth: float = 2.0,
+            scale_backoff: float = 0.5) -> AdamHp:
+    return AdamHp(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                  float(max_grad_norm), float(scale_growth), float(scale_backoff), int(scale_interval), 0)
 
 
 def reduce_owned(src: GradSrc, grad_out, overflow, sumsq, workspace, stream=None):
@@ -199,6 +207,13 @@ def adam_step(src: GradSrc, state: AdamState, hp: AdamHp, allgather, allgather_o
               stream=None):
     _check(lib().zero_adam_step(C.byref(src), C.byref(state), C.byref(hp), _ptr(allgather),
                                 int(allgather_off), _ptr(workspace), _stream(stream)), "zero_adam_step")
+
+
+def adam_step_clipped(src: GradSrc, state: AdamState, hp: AdamHp, grad_buf, allgather, allgather_off: int,
+                      workspace, stream=None):
+    _check(lib().zero_adam_step_clipped(C.byref(src), C.byref(state), C.byref(hp), _ptr(grad_buf),
+                                        _ptr(allgather), int(allgather_off), _ptr(workspace), _stream(stream)),
+           "zero_adam_step_clipped")
 
 
 def restore_skipped(state: AdamState, n: int, allgather, allgather_off: int, stream=None):

@@ -135,11 +135,13 @@ int zero_memory_model(double psi, int32_t nd, int32_t stage, int32_t k, zero_mem
     return ZERO_OK;
 }
 
-void zero_ctl_init(zero_step_ctl* ctl) {
+void zero_ctl_init(zero_step_ctl* ctl, double loss_scale) {
     if (ctl == nullptr) return;
     std::memset(ctl, 0, sizeof(*ctl));
     ctl->beta1_pow = 1.0;
     ctl->beta2_pow = 1.0;
+    ctl->loss_scale = loss_scale;
+    ctl->clip_coef = 1.0;
 }
 
 }  // extern "C"

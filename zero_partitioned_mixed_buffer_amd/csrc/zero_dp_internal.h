@@ -15,9 +15,12 @@ constexpr int kWaves = kBlock / 64;
 // Upper bound on workgroups of the reducing kernels (one partial each).
 constexpr int kMaxBlocks = 8192;
 
-// Workspace layout (bytes): completion counter, then per-workgroup partial
-// sums of g^2 (double) and overflow flags (int32).
+// Workspace layout (bytes): completion counter, the totals the clipped
+// path passes from its first to its second kernel, then per-workgroup
+// partial sums of g^2 (double) and overflow flags (int32).
 constexpr int64_t kWsTicket = 0;
+constexpr int64_t kWsTotSq = 64;
+constexpr int64_t kWsTotFlag = 72;
 constexpr int64_t kWsPartSq = 256;
 constexpr int64_t kWsPartFlag = kWsPartSq + 8 * kMaxBlocks;
 constexpr int64_t kWsBytes = kWsPartFlag + 4 * kMaxBlocks;

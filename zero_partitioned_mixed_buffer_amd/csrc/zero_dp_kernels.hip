@@ -290,18 +290,31 @@ __device__ __forceinline__ bool last_block_totals(const Partials& ws, double& sq
 
 // ---------------------------------------------------------------- kernels
 struct SrcArgs {
-    const uint16_t* win;   // base + elem_off: slice 0 of the window
+    const uint16_t* win;       // base + elem_off: slice 0 of the window
     int64_t stride;
     int64_t n;
     int32_t nd;
-    double inv_scale;
+    double inv_scale;          // 1/L of a static loss scale
+    const zero_step_ctl* dyn;  // non-null: L = dyn->loss_scale (dynamic loss scaling)
 };
+
+// The kernel's view of the source with 1/L resolved (the same IEEE division
+// as the host's 1.0 / L in every workgroup).
+__device__ __forceinline__ SrcArgs resolve_scale(const SrcArgs& src) {
+    SrcArgs s = src;
+    if (src.dyn != nullptr) s.inv_scale = 1.0 / src.dyn->loss_scale;
+    return s;
+}
 
 constexpr int kUnroll = ZDP_UNROLL;
 
-__global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src, float* grad_out,
+// kNormOfStored: sum g^2 over the fp32-rounded g written to grad_out (the
+// clipping path's norm) instead of the float64 g.
+template <bool kNormOfStored>
+__global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src_in, float* grad_out,
                                                               int32_t* overflow, double* sumsq,
                                                               Partials ws) {
+    const SrcArgs src = resolve_scale(src_in);
     const int64_t ngroups = (src.n + kV - 1) / kV;
     const int64_t nfull = src.n / kV;
     double sq = 0.0;
@@ -317,8 +330,9 @@ __global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src, float
             for (int e = 0; e < kV; ++e) {
                 bad |= !finite(acc[e]);
                 const double g = acc[e] * src.inv_scale;
-                sq += g * g;
                 gf[e] = static_cast<float>(g);
+                const double gn = kNormOfStored ? static_cast<double>(gf[e]) : g;
+                sq += gn * gn;
             }
             if (grad_out != nullptr) {
                 fvec o;
@@ -331,8 +345,10 @@ __global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src, float
                 const double s = sum_slices1(src.win + e, src.stride, src.nd);
                 bad |= !finite(s);
                 const double g = s * src.inv_scale;
-                sq += g * g;
-                if (grad_out != nullptr) grad_out[e] = static_cast<float>(g);
+                const float g32 = static_cast<float>(g);
+                const double gn = kNormOfStored ? static_cast<double>(g32) : g;
+                sq += gn * gn;
+                if (grad_out != nullptr) grad_out[e] = g32;
             }
         }
     }
@@ -342,6 +358,11 @@ __global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src, float
     }
 }
 
+// Per-element Adam/AdamW update (float64 arithmetic, fp32 storage).
+struct AdamScalars {
+    double b1, b2, omb1, omb2, ss, isb, dcy, eps;
+};
+
 struct AdamArgs {
     float* p[2];
     float* m[2];
@@ -349,12 +370,58 @@ struct AdamArgs {
     zero_step_ctl* ctl;
     double lr, b1, b2, eps, wd;
     uint16_t* ag;  // all-gather window start, or null
+    double growth, backoff;  // dynamic loss scaling factors
+    int32_t interval;        // > 0: dynamic loss scaling
 };
 
-// Per-element Adam/AdamW update (float64 arithmetic, fp32 storage).
-struct AdamScalars {
-    double b1, b2, omb1, omb2, ss, isb, dcy, eps;
-};
+// Scalars of the step being taken, t = committed + 1 (identical in every
+// lane and workgroup: the same IEEE operations on the same inputs).
+__device__ __forceinline__ AdamScalars step_scalars(const AdamArgs& a, double& b1t, double& b2t) {
+    const zero_step_ctl* ctl = a.ctl;
+    b1t = ctl->beta1_pow * a.b1;
+    b2t = ctl->beta2_pow * a.b2;
+    AdamScalars c;
+    c.b1 = a.b1;
+    c.b2 = a.b2;
+    c.omb1 = 1.0 - a.b1;
+    c.omb2 = 1.0 - a.b2;
+    c.ss = a.lr / (1.0 - b1t);
+    c.isb = 1.0 / __builtin_sqrt(1.0 - b2t);
+    c.dcy = 1.0 - a.lr * a.wd;
+    c.eps = a.eps;
+    return c;
+}
+
+// Commit (or skip) a step for the whole window, and advance the dynamic
+// loss scale; run by one lane after every workgroup has finished.
+__device__ __forceinline__ void commit_step(const AdamArgs& a, int cur, double b1t, double b2t, int bad,
+                                            double sq, double coef) {
+    zero_step_ctl* w = a.ctl;
+    w->overflow = bad;
+    w->sumsq = sq;
+    if (!bad) {
+        w->cur = cur ^ 1;
+        w->t = w->t + 1;
+        w->beta1_pow = b1t;
+        w->beta2_pow = b2t;
+        w->clip_coef = coef;
+    } else {
+        w->skipped = w->skipped + 1;
+    }
+    if (a.interval > 0) {
+        if (bad) {
+            w->loss_scale = w->loss_scale * a.backoff;
+            w->good_steps = 0;
+        } else {
+            int g = w->good_steps + 1;
+            if (g == a.interval) {
+                w->loss_scale = w->loss_scale * a.growth;
+                g = 0;
+            }
+            w->good_steps = g;
+        }
+    }
+}
 
 __device__ __forceinline__ void adam1(const AdamScalars& c, double g, float p, float m, float v,
                                       float& po, float& mo, float& vo) {
@@ -459,22 +526,11 @@ __device__ __forceinline__ bool pf_dispatch(int nd, int64_t gi, int64_t end, int
     return false;
 }
 
-__global__ void __launch_bounds__(kBlock) ZDP_FUSED_ATTR fused_step_kernel(SrcArgs src, AdamArgs a, Partials ws) {
-    // Scalars of the step being taken, t = committed + 1 (identical in every
-    // lane and workgroup: the same IEEE operations on the same inputs).
-    const zero_step_ctl* ctl = a.ctl;
-    const int cur = ctl->cur;
-    const double b1t = ctl->beta1_pow * a.b1;
-    const double b2t = ctl->beta2_pow * a.b2;
-    AdamScalars c;
-    c.b1 = a.b1;
-    c.b2 = a.b2;
-    c.omb1 = 1.0 - a.b1;
-    c.omb2 = 1.0 - a.b2;
-    c.ss = a.lr / (1.0 - b1t);
-    c.isb = 1.0 / __builtin_sqrt(1.0 - b2t);
-    c.dcy = 1.0 - a.lr * a.wd;
-    c.eps = a.eps;
+__global__ void __launch_bounds__(kBlock) ZDP_FUSED_ATTR fused_step_kernel(SrcArgs src_in, AdamArgs a, Partials ws) {
+    const SrcArgs src = resolve_scale(src_in);
+    const int cur = a.ctl->cur;
+    double b1t, b2t;
+    const AdamScalars c = step_scalars(a, b1t, b2t);
 
     const float* __restrict__ pin = a.p[cur];
     const float* __restrict__ min_ = a.m[cur];
@@ -559,20 +615,72 @@ __global__ void __launch_bounds__(kBlock) ZDP_FUSED_ATTR fused_step_kernel(SrcAr
             }
         }
     }
-    if (last_block_totals(ws, sq, bad) && threadIdx.x == 0) {
-        // Commit (or skip) the step for the whole window.
-        zero_step_ctl* w = a.ctl;
-        w->overflow = bad;
-        w->sumsq = sq;
-        if (!bad) {
-            w->cur = cur ^ 1;
-            w->t = ctl->t + 1;
-            w->beta1_pow = b1t;
-            w->beta2_pow = b2t;
+    if (last_block_totals(ws, sq, bad) && threadIdx.x == 0) commit_step(a, cur, b1t, b2t, bad, sq, 1.0);
+}
+
+// Second pass of the clipped step: g = g32 * coef from the materialised
+// fp32 gradient, then the update, emit and commit of the fused step.  A
+// step whose first pass found an inf/NaN touches nothing but the control
+// block (so its all-gather window needs no restore).
+__global__ void __launch_bounds__(kBlock) ZDP_FUSED_ATTR clipped_update_kernel(
+    const float* __restrict__ grad, int64_t n, AdamArgs a, double max_norm, const double* tot_sq,
+    const int32_t* tot_flag, Partials ws) {
+    if (*tot_flag != 0) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) commit_step(a, a.ctl->cur, 0.0, 0.0, 1, *tot_sq, 1.0);
+        return;
+    }
+    const double sq_in = *tot_sq;
+    const double r = max_norm / (__builtin_sqrt(sq_in) + 1e-6);
+    const double coef = r < 1.0 ? r : 1.0;
+    const int cur = a.ctl->cur;
+    double b1t, b2t;
+    const AdamScalars c = step_scalars(a, b1t, b2t);
+    const float* __restrict__ pin = a.p[cur];
+    const float* __restrict__ min_ = a.m[cur];
+    const float* __restrict__ vin = a.v[cur];
+    float* __restrict__ pout = a.p[cur ^ 1];
+    float* __restrict__ mout = a.m[cur ^ 1];
+    float* __restrict__ vout = a.v[cur ^ 1];
+    uint16_t* __restrict__ ag = a.ag;
+    const int64_t ngroups = (n + kV - 1) / kV;
+    const int64_t nfull = n / kV;
+    for (GroupIter it(ngroups); it.gi < it.end; it.gi += it.step) {
+        const int64_t gi = it.gi;
+        const int64_t j = gi * kV;
+        if (gi < nfull) {
+            const fvec gv = ldg(reinterpret_cast<const fvec*>(grad + j));
+            const fvec pv = ldg(reinterpret_cast<const fvec*>(pin + j));
+            const fvec mv = ldg(reinterpret_cast<const fvec*>(min_ + j));
+            const fvec vv = ldg(reinterpret_cast<const fvec*>(vin + j));
+            float po[kV], mo[kV], vo[kV];
+#pragma unroll
+            for (int e = 0; e < kV; ++e)
+                adam1(c, static_cast<double>(gv[e]) * coef, pv[e], mv[e], vv[e], po[e], mo[e], vo[e]);
+            fvec pw, mw, vw;
+#pragma unroll
+            for (int e = 0; e < kV; ++e) {
+                pw[e] = po[e];
+                mw[e] = mo[e];
+                vw[e] = vo[e];
+            }
+            stg(reinterpret_cast<fvec*>(pout + j), pw);
+            stg(reinterpret_cast<fvec*>(mout + j), mw);
+            stg(reinterpret_cast<fvec*>(vout + j), vw);
+            if (ag != nullptr) stg(reinterpret_cast<hvec*>(ag + j), pack_v(po));
         } else {
-            w->skipped = ctl->skipped + 1;
+            for (int64_t e = j; e < n; ++e) {
+                float po, mo, vo;
+                adam1(c, static_cast<double>(grad[e]) * coef, pin[e], min_[e], vin[e], po, mo, vo);
+                pout[e] = po;
+                mout[e] = mo;
+                vout[e] = vo;
+                if (ag != nullptr) ag[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(po));
+            }
         }
     }
+    double unused = 0.0;
+    int none = 0;
+    if (last_block_totals(ws, unused, none) && threadIdx.x == 0) commit_step(a, cur, b1t, b2t, 0, sq_in, coef);
 }
 
 __device__ __forceinline__ void emit_range(const float* __restrict__ src, uint16_t* __restrict__ ag,
@@ -610,9 +718,8 @@ __global__ void __launch_bounds__(kBlock) restore_kernel(const float* p0, const 
 
 // ---------------------------------------------------------------- host glue
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_grid_cache[4][kMaxDevices];  // 0 = not computed yet
-
-enum KernelId { kReduce = 0, kFused = 1, kEmit = 2, kRestore = 3 };
+enum KernelId { kReduce = 0, kFused = 1, kEmit = 2, kRestore = 3, kClip = 4, kKernels = 5 };
+std::atomic<int> g_grid_cache[kKernels][kMaxDevices];  // 0 = not computed yet
 
 // Workgroups that keep every CU of the current device busy at the kernel's
 // occupancy (grid-stride loops then cover any n).
@@ -624,10 +731,12 @@ int resident_blocks(KernelId id) {
     int cus = 0, per_cu = 0;
     const void* fn = nullptr;
     switch (id) {
-        case kReduce: fn = reinterpret_cast<const void*>(reduce_owned_kernel); break;
+        case kReduce: fn = reinterpret_cast<const void*>(reduce_owned_kernel<true>); break;
         case kFused: fn = reinterpret_cast<const void*>(fused_step_kernel); break;
         case kEmit: fn = reinterpret_cast<const void*>(emit_kernel); break;
         case kRestore: fn = reinterpret_cast<const void*>(restore_kernel); break;
+        case kClip: fn = reinterpret_cast<const void*>(clipped_update_kernel); break;
+        default: return 1024;
     }
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlock, 0) != hipSuccess ||
@@ -635,7 +744,7 @@ int resident_blocks(KernelId id) {
         (void)hipGetLastError();
         return 1024;
     }
-    if (ZDP_BPC > 0 && per_cu > ZDP_BPC && (id == kReduce || id == kFused)) per_cu = ZDP_BPC;
+    if (ZDP_BPC > 0 && per_cu > ZDP_BPC && (id == kReduce || id == kFused || id == kClip)) per_cu = ZDP_BPC;
     int blocks = cus * per_cu;
     if (blocks > zdp::kMaxBlocks) blocks = zdp::kMaxBlocks;
     g_grid_cache[id][dev].store(blocks, std::memory_order_relaxed);
@@ -688,13 +797,14 @@ int check_src(const zero_grad_src* src, Range* span) {
     return ZERO_OK;
 }
 
-SrcArgs make_src(const zero_grad_src* src) {
+SrcArgs make_src(const zero_grad_src* src, const zero_step_ctl* dyn = nullptr) {
     SrcArgs s;
     s.win = src->base + src->elem_off;
     s.stride = src->nd > 1 ? src->slice_stride : 0;
     s.n = src->n;
     s.nd = src->nd;
     s.inv_scale = 1.0 / src->loss_scale;
+    s.dyn = dyn;
     return s;
 }
 
@@ -710,6 +820,71 @@ Partials make_ws(void* workspace) {
 Range bytes_of(const void* p, int64_t n, int64_t elem) {
     const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
     return Range{lo, lo + static_cast<uintptr_t>(n) * static_cast<uintptr_t>(elem)};
+}
+
+// Validates the arguments of a step (fused or clipped) and fills the kernel
+// arguments.  `grad_buf` (the clipped path's fp32 gradient) may be null.
+int check_step(const zero_grad_src* src, const zero_adam_state* st, const zero_adam_hp* hp,
+               uint16_t* allgather, int64_t allgather_off, void* workspace, float* grad_buf,
+               AdamArgs* a, uint16_t** ag_out) {
+    Range span{};
+    int rc = check_src(src, &span);
+    if (rc != ZERO_OK) return rc;
+    if (st == nullptr || hp == nullptr || st->ctl == nullptr || workspace == nullptr) return ZERO_EINVAL;
+    if (!(hp->lr >= 0.0) || !__builtin_isfinite(hp->lr) || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
+        !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps > 0.0) || !__builtin_isfinite(hp->eps) ||
+        !(hp->weight_decay >= 0.0) || !__builtin_isfinite(hp->weight_decay) ||
+        !(hp->max_grad_norm >= 0.0) || !__builtin_isfinite(hp->max_grad_norm) || hp->reserved != 0 ||
+        hp->scale_interval < 0)
+        return ZERO_EINVAL;
+    if (hp->scale_interval > 0 &&
+        (!(hp->scale_growth > 0.0) || !__builtin_isfinite(hp->scale_growth) || !(hp->scale_backoff > 0.0) ||
+         !__builtin_isfinite(hp->scale_backoff)))
+        return ZERO_EINVAL;
+    const int64_t n = src->n;
+    int64_t b4 = 0;
+    if (zdp::mul_overflows(n, 4, &b4)) return ZERO_EOVERFLOW;
+    float* arrs[7] = {st->master[0],     st->master[1],     st->exp_avg[0], st->exp_avg[1],
+                      st->exp_avg_sq[0], st->exp_avg_sq[1], grad_buf};
+    Range r[9];
+    int nr = 0;
+    for (int i = 0; i < 7; ++i) {
+        if (i == 6 && grad_buf == nullptr) continue;
+        if (arrs[i] == nullptr && n != 0) return ZERO_EINVAL;
+        if (!aligned16(arrs[i])) return ZERO_EALIGN;
+        r[nr++] = bytes_of(arrs[i], n, 4);
+    }
+    if (!aligned16(workspace)) return ZERO_EALIGN;
+    uint16_t* ag = nullptr;
+    if (allgather != nullptr) {
+        if (allgather_off < 0) return ZERO_EINVAL;
+        int64_t e = 0;
+        if (zdp::add_overflows(allgather_off, n, &e) || zdp::mul_overflows(e, 2, &e)) return ZERO_EOVERFLOW;
+        ag = allgather + allgather_off;
+        if (!aligned16(ag)) return ZERO_EALIGN;
+        r[nr++] = bytes_of(ag, n, 2);
+    }
+    r[nr++] = span;
+    for (int i = 0; i < nr; ++i)
+        for (int k = i + 1; k < nr; ++k)
+            if (overlap(r[i], r[k])) return ZERO_EALIAS;
+    for (int i = 0; i < 2; ++i) {
+        a->p[i] = st->master[i];
+        a->m[i] = st->exp_avg[i];
+        a->v[i] = st->exp_avg_sq[i];
+    }
+    a->ctl = st->ctl;
+    a->lr = hp->lr;
+    a->b1 = hp->beta1;
+    a->b2 = hp->beta2;
+    a->eps = hp->eps;
+    a->wd = hp->weight_decay;
+    a->ag = ag;
+    a->growth = hp->scale_growth;
+    a->backoff = hp->scale_backoff;
+    a->interval = hp->scale_interval;
+    *ag_out = ag;
+    return ZERO_OK;
 }
 
 }  // namespace
@@ -733,66 +908,47 @@ int zero_reduce_owned(const zero_grad_src* src, float* grad_out, int32_t* overfl
     }
     const int grid = grid_for(kReduce, src->n);
     (void)hipGetLastError();
-    reduce_owned_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
+    reduce_owned_kernel<false><<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
         make_src(src), grad_out, overflow, sumsq, make_ws(workspace));
     return finish_launch();
 }
 
 int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st, const zero_adam_hp* hp,
                    uint16_t* allgather, int64_t allgather_off, void* workspace, void* stream) {
-    Range span{};
-    int rc = check_src(src, &span);
-    if (rc != ZERO_OK) return rc;
-    if (st == nullptr || hp == nullptr || st->ctl == nullptr || workspace == nullptr)
-        return ZERO_EINVAL;
-    if (!(hp->lr >= 0.0) || !__builtin_isfinite(hp->lr) || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
-        !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps > 0.0) || !__builtin_isfinite(hp->eps) ||
-        !(hp->weight_decay >= 0.0) || !__builtin_isfinite(hp->weight_decay))
-        return ZERO_EINVAL;
-    const int64_t n = src->n;
-    int64_t b4 = 0;
-    if (zdp::mul_overflows(n, 4, &b4)) return ZERO_EOVERFLOW;
-    float* arrs[6] = {st->master[0], st->master[1], st->exp_avg[0],
-                      st->exp_avg[1], st->exp_avg_sq[0], st->exp_avg_sq[1]};
-    Range r[8];
-    for (int i = 0; i < 6; ++i) {
-        if (arrs[i] == nullptr && n != 0) return ZERO_EINVAL;
-        if (!aligned16(arrs[i])) return ZERO_EALIGN;
-        r[i] = bytes_of(arrs[i], n, 4);
-    }
-    if (!aligned16(workspace)) return ZERO_EALIGN;
-    int nr = 6;
-    uint16_t* ag = nullptr;
-    if (allgather != nullptr) {
-        if (allgather_off < 0) return ZERO_EINVAL;
-        int64_t e = 0;
-        if (zdp::add_overflows(allgather_off, n, &e) || zdp::mul_overflows(e, 2, &e)) return ZERO_EOVERFLOW;
-        ag = allgather + allgather_off;
-        if (!aligned16(ag)) return ZERO_EALIGN;
-        r[nr++] = bytes_of(ag, n, 2);
-    }
-    r[nr++] = span;
-    for (int i = 0; i < nr; ++i)
-        for (int k = i + 1; k < nr; ++k)
-            if (overlap(r[i], r[k])) return ZERO_EALIAS;
-
     AdamArgs a;
-    for (int i = 0; i < 2; ++i) {
-        a.p[i] = st->master[i];
-        a.m[i] = st->exp_avg[i];
-        a.v[i] = st->exp_avg_sq[i];
-    }
-    a.ctl = st->ctl;
-    a.lr = hp->lr;
-    a.b1 = hp->beta1;
-    a.b2 = hp->beta2;
-    a.eps = hp->eps;
-    a.wd = hp->weight_decay;
-    a.ag = ag;
-    const int grid = grid_for(kFused, n);
+    uint16_t* ag = nullptr;
+    const int rc = check_step(src, st, hp, allgather, allgather_off, workspace, nullptr, &a, &ag);
+    if (rc != ZERO_OK) return rc;
+    if (hp->max_grad_norm != 0.0) return ZERO_EINVAL;  // clipping needs the two-pass entry point
+    const int grid = grid_for(kFused, src->n);
     (void)hipGetLastError();
-    fused_step_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(make_src(src), a,
-                                                                              make_ws(workspace));
+    fused_step_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
+        make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), a, make_ws(workspace));
+    return finish_launch();
+}
+
+int zero_adam_step_clipped(const zero_grad_src* src, const zero_adam_state* st, const zero_adam_hp* hp,
+                           float* grad_buf, uint16_t* allgather, int64_t allgather_off, void* workspace,
+                           void* stream) {
+    AdamArgs a;
+    uint16_t* ag = nullptr;
+    if (grad_buf == nullptr && src != nullptr && src->n != 0) return ZERO_EINVAL;
+    const int rc = check_step(src, st, hp, allgather, allgather_off, workspace, grad_buf, &a, &ag);
+    if (rc != ZERO_OK) return rc;
+    if (!(hp->max_grad_norm > 0.0) || !__builtin_isfinite(hp->max_grad_norm)) return ZERO_EINVAL;
+    const int64_t n = src->n;
+    const Partials ws = make_ws(workspace);
+    char* w = static_cast<char*>(workspace);
+    int32_t* tot_flag = reinterpret_cast<int32_t*>(w + zdp::kWsTotFlag);
+    double* tot_sq = reinterpret_cast<double*>(w + zdp::kWsTotSq);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    reduce_owned_kernel<true><<<grid_for(kReduce, n), kBlock, 0, s>>>(
+        make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), grad_buf, tot_flag, tot_sq, ws);
+    int rc2 = finish_launch();
+    if (rc2 != ZERO_OK) return rc2;
+    clipped_update_kernel<<<grid_for(kClip, n), kBlock, 0, s>>>(grad_buf, n, a, hp->max_grad_norm, tot_sq,
+                                                                 tot_flag, ws);
     return finish_launch();
 }
 

@@ -13,7 +13,12 @@ from . import binding as B
 
 
 class OwnedShard:
-    def __init__(self, master, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0):
+    def __init__(self, master, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                 max_grad_norm=0.0, scale_interval=0, scale_growth=2.0, scale_backoff=0.5,
+                 loss_scale=65536.0):
+        """max_grad_norm > 0 selects the two-pass clipped step (an fp32
+        gradient buffer of n elements is allocated); scale_interval > 0
+        selects dynamic loss scaling starting at `loss_scale`."""
         import torch
         if master.dtype != torch.float32 or master.dim() != 1 or not master.is_cuda:
             raise ValueError("master must be a 1-D float32 device tensor")
@@ -23,18 +28,28 @@ class OwnedShard:
         self.master = [master.clone(), torch.empty(n, dtype=torch.float32, device=dev)]
         self.exp_avg = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(2)]
         self.exp_avg_sq = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(2)]
-        ctl0 = torch.frombuffer(bytearray(B.ctl_init_bytes()), dtype=torch.uint8)
+        ctl0 = torch.frombuffer(bytearray(B.ctl_init_bytes(loss_scale)), dtype=torch.uint8)
         self.ctl = ctl0.to(dev)
         self.workspace = torch.zeros(B.workspace_bytes(), dtype=torch.uint8, device=dev)
         self.state = B.adam_state(self.master, self.exp_avg, self.exp_avg_sq, self.ctl)
-        self.hp = B.adam_hp(lr, beta1, beta2, eps, weight_decay)
+        self.hp = B.adam_hp(lr, beta1, beta2, eps, weight_decay, max_grad_norm, scale_interval,
+                            scale_growth, scale_backoff)
+        self.clipped = max_grad_norm > 0
+        self.grad_buf = torch.empty(n, dtype=torch.float32, device=dev) if self.clipped else None
 
-    def step(self, slices, loss_scale: float, elem_off: int = 0, allgather=None, allgather_off: int = 0,
+    def step(self, slices, loss_scale: float = 1.0, elem_off: int = 0, allgather=None, allgather_off: int = 0,
              stream=None):
-        """One fused step; ``slices`` is a float16 device tensor [Nd, stride]
-        whose columns [elem_off, elem_off + n) are the owned window."""
+        """One step; ``slices`` is a float16 device tensor [Nd, stride] whose
+        columns [elem_off, elem_off + n) are the owned window.  With dynamic
+        loss scaling the slices carry the control block's scale and
+        ``loss_scale`` is ignored."""
         nd, stride = slices.shape
         src = B.grad_src(slices, stride, elem_off, self.n, nd, loss_scale)
+        if self.clipped:
+            # a skipped clipped step leaves the all-gather window untouched
+            B.adam_step_clipped(src, self.state, self.hp, self.grad_buf, allgather, allgather_off,
+                                self.workspace, stream)
+            return
         B.adam_step(src, self.state, self.hp, allgather, allgather_off, self.workspace, stream)
         if allgather is not None:
             B.restore_skipped(self.state, self.n, allgather, allgather_off, stream)
