@@ -100,7 +100,13 @@ __device__ __forceinline__ hvec pack_v(const float (&x)[kV]) {
 #define ZDP_FUSED_ATTR
 #endif
 #ifndef ZDP_BPC
-#define ZDP_BPC 1  // >0: at most this many workgroups per CU (reducing kernels)
+#define ZDP_BPC 1  // >0: at most this many workgroups per CU (fused step)
+#endif
+#ifndef ZDP_BPC_REDUCE
+#define ZDP_BPC_REDUCE 1  // the same cap for the reduce pass
+#endif
+#ifndef ZDP_BPC_CLIP
+#define ZDP_BPC_CLIP 1  // the same cap for the clipped update pass
 #endif
 #ifndef ZDP_XCD_REMAP
 #define ZDP_XCD_REMAP 1  // 1: consecutive logical workgroups on one XCD
@@ -140,6 +146,9 @@ __device__ __forceinline__ void sum_chunk(double (&acc)[kV], const uint16_t* p, 
     hvec w[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) w[u] = ldh(p + static_cast<int64_t>(k0 + u) * stride);
+    // keep the scheduler from interleaving the adds with the loads (left to
+    // itself it serialises half of them behind full vmcnt waits)
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (kFirst) {
         init_v(acc, w[0]);
 #pragma unroll
@@ -308,8 +317,86 @@ __device__ __forceinline__ SrcArgs resolve_scale(const SrcArgs& src) {
 
 constexpr int kUnroll = ZDP_UNROLL;
 
+// One reduced element group: g = (sum of slices) / L, the inf/NaN flag and
+// the sum of squares, and the fp32 g into grad_out (when non-null).
 // kNormOfStored: sum g^2 over the fp32-rounded g written to grad_out (the
 // clipping path's norm) instead of the float64 g.
+template <bool kNormOfStored>
+__device__ __forceinline__ void reduce_finish(const double (&acc)[kV], const SrcArgs& src, float* grad_out,
+                                              int64_t j, double& sq, int& bad) {
+    float gf[kV];
+#pragma unroll
+    for (int e = 0; e < kV; ++e) {
+        bad |= !finite(acc[e]);
+        const double g = acc[e] * src.inv_scale;
+        gf[e] = static_cast<float>(g);
+        const double gn = kNormOfStored ? static_cast<double>(gf[e]) : g;
+        sq += gn * gn;
+    }
+    if (grad_out != nullptr) {
+        fvec o;
+#pragma unroll
+        for (int e = 0; e < kV; ++e) o[e] = gf[e];
+        stg(reinterpret_cast<fvec*>(grad_out + j), o);
+    }
+}
+
+// Elements [j, n) of the ragged tail, one at a time.
+template <bool kNormOfStored>
+__device__ void reduce_tail(int64_t j, const SrcArgs& src, float* grad_out, double& sq, int& bad) {
+    for (int64_t e = j; e < src.n; ++e) {
+        const double s = sum_slices1(src.win + e, src.stride, src.nd);
+        bad |= !finite(s);
+        const double g = s * src.inv_scale;
+        const float g32 = static_cast<float>(g);
+        const double gn = kNormOfStored ? static_cast<double>(g32) : g;
+        sq += gn * gn;
+        if (grad_out != nullptr) grad_out[e] = g32;
+    }
+}
+
+// Full groups gi, gi+step, ... < end with Nd = R <= one chunk: the next
+// group's R loads are issued before the current group is summed, as in the
+// fused step's prefetch path.
+template <int R, bool kNormOfStored>
+__device__ void reduce_pf_run(int64_t gi, int64_t end, int64_t step, const SrcArgs& src, float* grad_out,
+                              double& sq, int& bad) {
+    if (gi >= end) return;
+    hvec w[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) w[u] = ldh(src.win + gi * kV + static_cast<int64_t>(u) * src.stride);
+    for (;;) {
+        const int64_t gn = gi + step;
+        const int64_t gl = gn < end ? gn : gi;
+        hvec wc[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) wc[u] = w[u];
+#pragma unroll
+        for (int u = 0; u < R; ++u) w[u] = ldh(src.win + gl * kV + static_cast<int64_t>(u) * src.stride);
+        __builtin_amdgcn_sched_barrier(0);
+        double acc[kV];
+        init_v(acc, wc[0]);
+#pragma unroll
+        for (int u = 1; u < R; ++u) add_v(acc, wc[u]);
+        reduce_finish<kNormOfStored>(acc, src, grad_out, gi * kV, sq, bad);
+        if (gn >= end) break;
+        gi = gn;
+    }
+}
+
+template <int R, bool kNormOfStored>
+__device__ __forceinline__ bool reduce_pf_dispatch(int nd, int64_t gi, int64_t end, int64_t step,
+                                                   const SrcArgs& src, float* grad_out, double& sq, int& bad) {
+    if constexpr (R >= 1) {
+        if (nd == R) {
+            reduce_pf_run<R, kNormOfStored>(gi, end, step, src, grad_out, sq, bad);
+            return true;
+        }
+        return reduce_pf_dispatch<R - 1, kNormOfStored>(nd, gi, end, step, src, grad_out, sq, bad);
+    }
+    return false;
+}
+
 template <bool kNormOfStored>
 __global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src_in, float* grad_out,
                                                               int32_t* overflow, double* sumsq,
@@ -319,37 +406,27 @@ __global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src_in, fl
     const int64_t nfull = src.n / kV;
     double sq = 0.0;
     int bad = 0;
-    for (GroupIter it(ngroups); it.gi < it.end; it.gi += it.step) {
+    bool done = false;
+    if (src.nd <= kUnroll) {
+        GroupIter it(ngroups);
+        const int64_t endf = it.end < nfull ? it.end : nfull;
+        done = reduce_pf_dispatch<kUnroll, kNormOfStored>(src.nd, it.gi, endf, it.step, src, grad_out, sq, bad);
+        if (done && ngroups > nfull) {
+            // the ragged tail group, by the lane whose sequence contains it
+            const int64_t g = nfull;
+            if (g >= it.gi && g < it.end && (g - it.gi) % it.step == 0)
+                reduce_tail<kNormOfStored>(g * kV, src, grad_out, sq, bad);
+        }
+    }
+    for (GroupIter it(ngroups); !done && it.gi < it.end; it.gi += it.step) {
         const int64_t gi = it.gi;
         const int64_t j = gi * kV;
         if (gi < nfull) {
             double acc[kV];
             sum_slices<kUnroll>(acc, src.win + j, src.stride, src.nd);
-            float gf[kV];
-#pragma unroll
-            for (int e = 0; e < kV; ++e) {
-                bad |= !finite(acc[e]);
-                const double g = acc[e] * src.inv_scale;
-                gf[e] = static_cast<float>(g);
-                const double gn = kNormOfStored ? static_cast<double>(gf[e]) : g;
-                sq += gn * gn;
-            }
-            if (grad_out != nullptr) {
-                fvec o;
-#pragma unroll
-                for (int e = 0; e < kV; ++e) o[e] = gf[e];
-                stg(reinterpret_cast<fvec*>(grad_out + j), o);
-            }
+            reduce_finish<kNormOfStored>(acc, src, grad_out, j, sq, bad);
         } else {
-            for (int64_t e = j; e < src.n; ++e) {
-                const double s = sum_slices1(src.win + e, src.stride, src.nd);
-                bad |= !finite(s);
-                const double g = s * src.inv_scale;
-                const float g32 = static_cast<float>(g);
-                const double gn = kNormOfStored ? static_cast<double>(g32) : g;
-                sq += gn * gn;
-                if (grad_out != nullptr) grad_out[e] = g32;
-            }
+            reduce_tail<kNormOfStored>(j, src, grad_out, sq, bad);
         }
     }
     if (last_block_totals(ws, sq, bad) && threadIdx.x == 0) {
@@ -744,7 +821,8 @@ int resident_blocks(KernelId id) {
         (void)hipGetLastError();
         return 1024;
     }
-    if (ZDP_BPC > 0 && per_cu > ZDP_BPC && (id == kReduce || id == kFused || id == kClip)) per_cu = ZDP_BPC;
+    const int cap = id == kFused ? ZDP_BPC : id == kReduce ? ZDP_BPC_REDUCE : id == kClip ? ZDP_BPC_CLIP : 0;
+    if (cap > 0 && per_cu > cap) per_cu = cap;
     int blocks = cus * per_cu;
     if (blocks > zdp::kMaxBlocks) blocks = zdp::kMaxBlocks;
     g_grid_cache[id][dev].store(blocks, std::memory_order_relaxed);
