@@ -47,7 +47,18 @@ def parse():
                     help="> 0: time the two-pass clipped step instead of the fused step")
     ap.add_argument("--dynamic-scale", type=int, default=0,
                     help="> 0: dynamic loss scaling with this growth interval")
-    return ap.parse_args()
+    ap.add_argument("--bucket-elems", type=int, default=0,
+                    help="> 0: bucketed step, the window ingested in buckets of this many elements")
+    ap.add_argument("--arrival", action="store_true",
+                    help="bucketed step: copy each bucket into one of two constant-size receive "
+                         "buffers on a side stream (the simulated reduce-scatter arrival), "
+                         "overlapped with the previous bucket's step")
+    a = ap.parse_args()
+    if a.bucket_elems < 0 or a.bucket_elems % 8 or (a.bucket_elems and a.max_grad_norm > 0):
+        ap.error("--bucket-elems must be a multiple of 8, and cannot be combined with clipping")
+    if a.arrival and not a.bucket_elems:
+        ap.error("--arrival needs --bucket-elems")
+    return a
 
 
 def kernel_fingerprint():
@@ -174,9 +185,47 @@ def main():
     srcs = [B.grad_src(t, S, 0, S, w.nd, w.loss_scale) for t in gsets]
 
     clipped = args.max_grad_norm > 0
+    bucketed = args.bucket_elems > 0
+    if bucketed:
+        nb_elems = min(args.bucket_elems, S)
+        buckets = [(o, min(nb_elems, S - o)) for o in range(0, S, nb_elems)]
+        side = torch.cuda.Stream(device=dev)  # default priority
+        recv = [torch.empty((w.nd, nb_elems), dtype=torch.float16, device=dev) for _ in range(2)]
+        arrived = [torch.cuda.Event() for _ in range(2)]
+        consumed = [torch.cuda.Event() for _ in range(2)]
+        for ev in consumed:
+            ev.record(stream)
+        log(f"bucketed: {len(buckets)} buckets of {nb_elems} elements"
+            + ("; arrival copies into 2 constant-size receive buffers on a side stream" if args.arrival else
+               "; buckets read in place"))
+
+    def launch_bucketed(i, restore=True):
+        sh = shards[i % n_shards]
+        gs = gsets[i % rot]
+        for b, (o, k) in enumerate(buckets):
+            phase = (B.BUCKET_FIRST if b == 0 else 0) | (B.BUCKET_LAST if b == len(buckets) - 1 else 0)
+            if args.arrival:
+                r = b % 2
+                side.wait_event(consumed[r])
+                with torch.cuda.stream(side):
+                    recv[r][:, :k].copy_(gs[:, o:o + k])
+                arrived[r].record(side)
+                stream.wait_event(arrived[r])
+                src = B.grad_src(recv[r], nb_elems, 0, k, w.nd, w.loss_scale)
+            else:
+                src = B.grad_src(gs, S, o, k, w.nd, w.loss_scale)
+            B.adam_step_bucket(src, sh.state, sh.hp, o, S, ag, ag_offs[i % n_shards], phase, sh.workspace,
+                               stream)
+            if args.arrival:
+                consumed[r].record(stream)
+        if restore:
+            B.restore_skipped(sh.state, S, ag, ag_offs[i % n_shards], stream)
 
     def launch(i, restore=True):
         sh = shards[i % n_shards]
+        if bucketed:
+            launch_bucketed(i, restore)
+            return
         if clipped:  # two passes; a skipped step leaves the window untouched
             B.adam_step_clipped(srcs[i % rot], sh.state, sh.hp, sh.grad_buf, ag, ag_offs[i % n_shards],
                                 sh.workspace, stream)
@@ -214,14 +263,15 @@ def main():
         sys.exit(1)
 
     calibration_copy(torch, dev)
-    traffic = None if clipped else measured_traffic(w.key)
+    traffic = None if (clipped or bucketed) else measured_traffic(w.key)
 
     ms_step = wall * 1e3 / args.steps
     # algorithmic bytes per owned element: fused 2*Nd + 26; clipped
     # (2*Nd + 4) for the reduce pass + 30 for the update pass
     bytes_elem = 2 * w.nd + (34 if clipped else 26)
     achieved = bytes_elem * S / (kern_avg * 1e-3) / 1e9
-    log(f"fused kernel: avg {kern_avg * 1e3:.1f} us over {args.steps} back-to-back launches; "
+    what = f"bucketed step ({len(buckets)} launches)" if bucketed else "fused kernel"
+    log(f"{what}: avg {kern_avg * 1e3:.1f} us over {args.steps} back-to-back launches; "
         f"step {ms_step * 1e3:.1f} us; {achieved:.0f} GB/s")
 
     cpu = None
@@ -255,6 +305,8 @@ def main():
             "step_hbm_gbs": bytes_elem * S / (ms_step * 1e-3) / 1e9,
             "max_grad_norm": args.max_grad_norm,
             "dynamic_scale_interval": args.dynamic_scale,
+            "bucket_elems": args.bucket_elems,
+            "bucket_arrival_copies": bool(args.arrival),
         },
         "roofline": {
             "bound": "hbm",
@@ -267,7 +319,8 @@ def main():
             "traffic": None if traffic is None else traffic / (kern_avg * 1e-3) / 1e9,
             "traffic_bytes_per_launch": traffic,
             "algorithmic_bytes_per_launch": bytes_elem * S,
-            "kernel": "reduce_owned_kernel + clipped_update_kernel" if clipped else "fused_step_kernel",
+            "kernel": ("reduce_owned_kernel + clipped_update_kernel" if clipped else
+                       f"fused_step_kernel x {len(buckets)} buckets" if bucketed else "fused_step_kernel"),
             "kernel_avg_us": kern_avg * 1e3,
             "kernel_fingerprint": kernel_fingerprint(),
         },

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define ZERO_DP_ABI_VERSION 2
+#define ZERO_DP_ABI_VERSION 3
 
 /* ---- status codes --------------------------------------------------- */
 #define ZERO_OK          0
@@ -183,7 +183,8 @@ int zero_reduce_owned(const zero_grad_src* src, float* grad_out, int32_t* overfl
 typedef struct zero_step_ctl {
     int32_t cur;         /* index (0/1) of the buffers holding the committed state */
     int32_t t;           /* committed optimizer steps */
-    int32_t overflow;    /* 1 if the last step was skipped (inf/NaN gradient) */
+    int32_t overflow;    /* 0: the last step was committed; 1: skipped (inf/NaN gradient);
+                            2: skipped (a bucketed step's buckets did not cover the window) */
     int32_t good_steps;  /* dynamic loss scaling: consecutive clean steps since the last change */
     double beta1_pow;    /* beta1^t, as t successive products from 1.0 */
     double beta2_pow;    /* beta2^t */
@@ -276,8 +277,44 @@ int zero_adam_step_clipped(const zero_grad_src* src, const zero_adam_state* st,
                            const zero_adam_hp* hp, float* grad_buf, uint16_t* allgather,
                            int64_t allgather_off, void* workspace, void* stream);
 
+/* ---- bucketed step (constant-size fused buffers) ---------------------
+ * The reduce-scatter delivers the owned gradient partition bucket by bucket
+ * (dmarx anthology note, "Method": constant-size fused buffers, CB); this
+ * steps one bucket as soon as it has arrived, so the step overlaps the rest
+ * of the ingest.  The buckets of one step partition the window
+ * [0, window_n): bucket b covers window elements [win_off, win_off + n)
+ * and its gradients come from src (n = src->n; typically the same
+ * constant-size receive buffer [Nd, B] for every bucket).  Each bucket runs
+ * the fused update of zero_adam_step on its elements, reading state
+ * buffer ctl->cur and writing the other one plus
+ * allgather[allgather_off + win_off + j]; nothing is committed until the
+ * last bucket.  Sum g^2, the overflow flag and the number of elements
+ * covered accumulate in the workspace in stream order (deterministic for a
+ * given bucket order).  The launch flagged ZERO_BUCKET_LAST commits the
+ * whole step as zero_adam_step would, or skips it if any bucket overflowed
+ * (ctl->overflow = 1, the loss scale backs off) or if the buckets covered
+ * fewer or more than window_n elements (ctl->overflow = 2, the loss scale
+ * is left alone).  After a skip, call zero_restore_skipped over the window.
+ *   st: the window's state, as for zero_adam_step (n = window_n).
+ *   win_off: multiple of 8.  phase: ZERO_BUCKET_FIRST on the step's first
+ *   bucket, ZERO_BUCKET_LAST on its last (both for a single bucket), 0 in
+ *   between.  Every bucket of a step runs on one stream with one
+ *   workspace; the buckets may come in any order but must not overlap
+ *   (an overlap that keeps the count equal to window_n is not detected).
+ *   hp->max_grad_norm must be 0: clipping needs the whole norm before any
+ *   bucket is updated.
+ * Errors: ZERO_EINVAL (also win_off + n > window_n), ZERO_EALIGN,
+ * ZERO_EOVERFLOW, ZERO_EALIAS, ZERO_EHIP.
+ */
+#define ZERO_BUCKET_FIRST 1
+#define ZERO_BUCKET_LAST  2
+int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st,
+                          const zero_adam_hp* hp, int64_t win_off, int64_t window_n,
+                          uint16_t* allgather, int64_t allgather_off, int32_t phase,
+                          void* workspace, void* stream);
+
 /* Re-emits allgather[off + j] = fp16_RNE(master[ctl->cur][j]) for j < n when
- * ctl->overflow == 1 (the step was skipped), and does nothing otherwise; the
+ * ctl->overflow != 0 (the step was skipped), and does nothing otherwise; the
  * decision is taken on the device, so no host synchronisation is needed.
  * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EHIP. */
 int zero_restore_skipped(const zero_adam_state* st, int64_t n, uint16_t* allgather,

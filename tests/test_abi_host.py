@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(L):
     for name in declared:
         assert hasattr(L, name), name
     assert declared == set(B.EXPORTED)
-    assert L.zero_abi_version() == B.ABI_VERSION == 2
+    assert L.zero_abi_version() == B.ABI_VERSION == 3
 
 
 def test_strerror(L):
@@ -197,6 +197,31 @@ def test_clipped_validation(L):
     assert step(gbuf=A) == B.ZERO_EALIAS                # overlaps the gradient slices
     assert step(hpp=B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0)) == B.ZERO_EINVAL  # max_grad_norm must be > 0
     assert step(hpp=B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0, max_grad_norm=float("inf"))) == B.ZERO_EINVAL
+
+
+def test_bucket_validation(L):
+    hp = B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    src = B.grad_src(A, 16, 0, 16, 4, 1024.0)  # a bucket of 16 elements
+    st = _state()                              # a window of 64 elements
+
+    def step(src=src, off=0, window_n=64, phase=B.BUCKET_FIRST, hpp=hp, state=st, ag=None, ag_off=0):
+        return L.zero_adam_step_bucket(C.byref(src), C.byref(state), C.byref(hpp), off, window_n, ag, ag_off,
+                                       phase, 1 << 28, None)
+
+    assert step(phase=4) == B.ZERO_EINVAL
+    assert step(phase=-1) == B.ZERO_EINVAL
+    assert step(off=-8) == B.ZERO_EINVAL
+    assert step(off=56) == B.ZERO_EINVAL                # 56 + 16 > 64
+    assert step(window_n=-1) == B.ZERO_EINVAL
+    assert step(off=4) == B.ZERO_EALIGN                 # bucket offsets are multiples of 8
+    assert step(off=2**62, window_n=2**62 + 64) == B.ZERO_EOVERFLOW
+    assert step(hpp=B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0, max_grad_norm=1.0)) == B.ZERO_EINVAL
+    assert step(state=_state(ctl=None)) == B.ZERO_EINVAL
+    assert step(state=_state(base=A)) == B.ZERO_EALIAS  # state inside the receive buffer
+    assert step(ag=1 << 29, ag_off=4) == B.ZERO_EALIGN  # window start + bucket offset misaligned
+    assert step(ag=1 << 29, ag_off=-8) == B.ZERO_EINVAL
+    assert L.zero_adam_step_bucket(None, C.byref(st), C.byref(hp), 0, 64, None, 0, 1, 1 << 28, None) == \
+        B.ZERO_EINVAL
 
 
 def test_other_validation(L):

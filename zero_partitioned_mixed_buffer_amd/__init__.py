@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     adam_hp,
     adam_state,
     adam_step,
+    adam_step_bucket,
     adam_step_clipped,
     emit_fp16,
     grad_src,

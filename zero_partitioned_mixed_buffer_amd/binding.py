@@ -25,9 +25,12 @@ ZERO_EHIP = -6
 EXPORTED = (
     "zero_strerror", "zero_last_hip_error", "zero_abi_version", "zero_plan_partitions",
     "zero_memory_model", "zero_workspace_bytes", "zero_reduce_owned", "zero_ctl_init",
-    "zero_adam_step", "zero_adam_step_clipped", "zero_restore_skipped", "zero_emit_fp16",
+    "zero_adam_step", "zero_adam_step_clipped", "zero_adam_step_bucket", "zero_restore_skipped",
+    "zero_emit_fp16",
 )
-ABI_VERSION = 2
+ABI_VERSION = 3
+BUCKET_FIRST = 1
+BUCKET_LAST = 2
 
 
 class ZeroError(RuntimeError):
@@ -101,10 +104,12 @@ def lib():
                                  C.c_int64, P, P]
     L.zero_adam_step_clipped.argtypes = [C.POINTER(GradSrc), C.POINTER(AdamState), C.POINTER(AdamHp), P, P,
                                          C.c_int64, P, P]
+    L.zero_adam_step_bucket.argtypes = [C.POINTER(GradSrc), C.POINTER(AdamState), C.POINTER(AdamHp), C.c_int64,
+                                        C.c_int64, P, C.c_int64, C.c_int32, P, P]
     L.zero_restore_skipped.argtypes = [C.POINTER(AdamState), C.c_int64, P, C.c_int64, P]
     L.zero_emit_fp16.argtypes = [P, C.c_int64, P, C.c_int64, P]
     for name in ("zero_plan_partitions", "zero_memory_model", "zero_reduce_owned", "zero_adam_step",
-                 "zero_adam_step_clipped", "zero_restore_skipped", "zero_emit_fp16"):
+                 "zero_adam_step_clipped", "zero_adam_step_bucket", "zero_restore_skipped", "zero_emit_fp16"):
         getattr(L, name).restype = C.c_int
     if L.zero_abi_version() != ABI_VERSION:
         raise RuntimeError("libzero_dp.so ABI version mismatch")
@@ -214,6 +219,13 @@ def adam_step_clipped(src: GradSrc, state: AdamState, hp: AdamHp, grad_buf, allg
     _check(lib().zero_adam_step_clipped(C.byref(src), C.byref(state), C.byref(hp), _ptr(grad_buf),
                                         _ptr(allgather), int(allgather_off), _ptr(workspace), _stream(stream)),
            "zero_adam_step_clipped")
+
+
+def adam_step_bucket(src: GradSrc, state: AdamState, hp: AdamHp, win_off: int, window_n: int, allgather,
+                     allgather_off: int, phase: int, workspace, stream=None):
+    _check(lib().zero_adam_step_bucket(C.byref(src), C.byref(state), C.byref(hp), int(win_off), int(window_n),
+                                       _ptr(allgather), int(allgather_off), int(phase), _ptr(workspace),
+                                       _stream(stream)), "zero_adam_step_bucket")
 
 
 def restore_skipped(state: AdamState, n: int, allgather, allgather_off: int, stream=None):

@@ -449,6 +449,13 @@ struct AdamArgs {
     uint16_t* ag;  // all-gather window start, or null
     double growth, backoff;  // dynamic loss scaling factors
     int32_t interval;        // > 0: dynamic loss scaling
+    // bucketed step: this launch covers one bucket of the window; running
+    // totals live in the workspace across the step's launches
+    int32_t bucket;          // 0: whole-window step; else ZERO_BUCKET_FIRST/LAST bits | 4
+    int64_t window_n;        // elements the step's buckets must cover
+    double* run_sq;
+    int32_t* run_flag;
+    int64_t* run_count;
 };
 
 // Scalars of the step being taken, t = committed + 1 (identical in every
@@ -470,7 +477,9 @@ __device__ __forceinline__ AdamScalars step_scalars(const AdamArgs& a, double& b
 }
 
 // Commit (or skip) a step for the whole window, and advance the dynamic
-// loss scale; run by one lane after every workgroup has finished.
+// loss scale; run by one lane after every workgroup has finished.  A
+// bucketed step whose buckets did not cover the window (bad == 2) is
+// skipped without touching the loss scale.
 __device__ __forceinline__ void commit_step(const AdamArgs& a, int cur, double b1t, double b2t, int bad,
                                             double sq, double coef) {
     zero_step_ctl* w = a.ctl;
@@ -485,7 +494,7 @@ __device__ __forceinline__ void commit_step(const AdamArgs& a, int cur, double b
     } else {
         w->skipped = w->skipped + 1;
     }
-    if (a.interval > 0) {
+    if (a.interval > 0 && bad != 2) {
         if (bad) {
             w->loss_scale = w->loss_scale * a.backoff;
             w->good_steps = 0;
@@ -498,6 +507,31 @@ __device__ __forceinline__ void commit_step(const AdamArgs& a, int cur, double b
             w->good_steps = g;
         }
     }
+}
+
+// End of a fused launch, in the one lane of the last workgroup: commit the
+// whole-window step, or fold this bucket's totals into the running ones
+// (in stream order, so the sum is deterministic) and commit after the last.
+__device__ __forceinline__ void finish_fused(const AdamArgs& a, int cur, double b1t, double b2t, int bad,
+                                             double sq, int64_t n) {
+    if (a.bucket == 0) {
+        commit_step(a, cur, b1t, b2t, bad, sq, 1.0);
+        return;
+    }
+    const bool first = (a.bucket & ZERO_BUCKET_FIRST) != 0;
+    double rs = first ? 0.0 : *a.run_sq;
+    int rf = first ? 0 : *a.run_flag;
+    int64_t rc = first ? 0 : *a.run_count;
+    rs += sq;
+    rf |= bad;
+    rc += n;
+    if ((a.bucket & ZERO_BUCKET_LAST) == 0) {
+        *a.run_sq = rs;
+        *a.run_flag = rf;
+        *a.run_count = rc;
+        return;
+    }
+    commit_step(a, cur, b1t, b2t, rc != a.window_n ? 2 : rf, rs, 1.0);
 }
 
 __device__ __forceinline__ void adam1(const AdamScalars& c, double g, float p, float m, float v,
@@ -692,7 +726,7 @@ __global__ void __launch_bounds__(kBlock) ZDP_FUSED_ATTR fused_step_kernel(SrcAr
             }
         }
     }
-    if (last_block_totals(ws, sq, bad) && threadIdx.x == 0) commit_step(a, cur, b1t, b2t, bad, sq, 1.0);
+    if (last_block_totals(ws, sq, bad) && threadIdx.x == 0) finish_fused(a, cur, b1t, b2t, bad, sq, src.n);
 }
 
 // Second pass of the clipped step: g = g32 * coef from the materialised
@@ -961,6 +995,12 @@ int check_step(const zero_grad_src* src, const zero_adam_state* st, const zero_a
     a->growth = hp->scale_growth;
     a->backoff = hp->scale_backoff;
     a->interval = hp->scale_interval;
+    a->bucket = 0;
+    a->window_n = n;
+    char* w = static_cast<char*>(workspace);
+    a->run_sq = reinterpret_cast<double*>(w + zdp::kWsRunSq);
+    a->run_flag = reinterpret_cast<int32_t*>(w + zdp::kWsRunFlag);
+    a->run_count = reinterpret_cast<int64_t*>(w + zdp::kWsRunCount);
     *ag_out = ag;
     return ZERO_OK;
 }
@@ -1027,6 +1067,44 @@ int zero_adam_step_clipped(const zero_grad_src* src, const zero_adam_state* st, 
     if (rc2 != ZERO_OK) return rc2;
     clipped_update_kernel<<<grid_for(kClip, n), kBlock, 0, s>>>(grad_buf, n, a, hp->max_grad_norm, tot_sq,
                                                                  tot_flag, ws);
+    return finish_launch();
+}
+
+int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st, const zero_adam_hp* hp,
+                          int64_t win_off, int64_t window_n, uint16_t* allgather, int64_t allgather_off,
+                          int32_t phase, void* workspace, void* stream) {
+    if (src == nullptr || st == nullptr || hp == nullptr) return ZERO_EINVAL;
+    if ((phase & ~(ZERO_BUCKET_FIRST | ZERO_BUCKET_LAST)) != 0 || win_off < 0 || window_n < 0 || src->n < 0)
+        return ZERO_EINVAL;
+    int64_t end = 0, b = 0;
+    if (zdp::add_overflows(win_off, src->n, &end) || zdp::mul_overflows(window_n, 4, &b)) return ZERO_EOVERFLOW;
+    if (end > window_n) return ZERO_EINVAL;
+    if (win_off % 8 != 0) return ZERO_EALIGN;
+    // the bucket's view of the state and of the all-gather window
+    zero_adam_state sub = *st;
+    for (int i = 0; i < 2; ++i) {
+        if (st->master[i] == nullptr || st->exp_avg[i] == nullptr || st->exp_avg_sq[i] == nullptr) {
+            if (window_n != 0) return ZERO_EINVAL;
+            continue;
+        }
+        sub.master[i] = st->master[i] + win_off;
+        sub.exp_avg[i] = st->exp_avg[i] + win_off;
+        sub.exp_avg_sq[i] = st->exp_avg_sq[i] + win_off;
+    }
+    int64_t ag_off = 0;
+    if (allgather != nullptr && (allgather_off < 0 || zdp::add_overflows(allgather_off, win_off, &ag_off)))
+        return allgather_off < 0 ? ZERO_EINVAL : ZERO_EOVERFLOW;
+    AdamArgs a;
+    uint16_t* ag = nullptr;
+    const int rc = check_step(src, &sub, hp, allgather, ag_off, workspace, nullptr, &a, &ag);
+    if (rc != ZERO_OK) return rc;
+    if (hp->max_grad_norm != 0.0) return ZERO_EINVAL;  // clipping needs the norm before any bucket
+    a.bucket = phase | 4;
+    a.window_n = window_n;
+    const int grid = grid_for(kFused, src->n);
+    (void)hipGetLastError();
+    fused_step_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
+        make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), a, make_ws(workspace));
     return finish_launch();
 }
 

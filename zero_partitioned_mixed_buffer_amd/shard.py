@@ -54,6 +54,22 @@ class OwnedShard:
         if allgather is not None:
             B.restore_skipped(self.state, self.n, allgather, allgather_off, stream)
 
+    def step_bucket(self, slices, win_off: int, n: int, phase: int, loss_scale: float = 1.0, elem_off: int = 0,
+                    allgather=None, allgather_off: int = 0, stream=None):
+        """One bucket of a bucketed step: columns [elem_off, elem_off + n) of
+        ``slices`` [Nd, stride] hold the gradients of window elements
+        [win_off, win_off + n).  ``phase`` carries B.BUCKET_FIRST on the
+        step's first bucket and B.BUCKET_LAST on its last; after the last,
+        the all-gather window is restored if the step was skipped."""
+        if self.clipped:
+            raise ValueError("a bucketed step cannot clip (the norm is needed before any bucket)")
+        nd, stride = slices.shape
+        src = B.grad_src(slices, stride, elem_off, n, nd, loss_scale)
+        B.adam_step_bucket(src, self.state, self.hp, win_off, self.n, allgather, allgather_off, phase,
+                           self.workspace, stream)
+        if allgather is not None and phase & B.BUCKET_LAST:
+            B.restore_skipped(self.state, self.n, allgather, allgather_off, stream)
+
     def emit(self, allgather, allgather_off: int = 0, stream=None):
         """fp16 copy of the committed master into the all-gather buffer."""
         B.emit_fp16(self.committed()[0], self.n, allgather, allgather_off, stream)
