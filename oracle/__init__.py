@@ -17,4 +17,5 @@ from .zero_oracle import (  # noqa: F401
     scaler_update,
     clip_coefficient,
     clipped_gradient,
+    gather,
 )

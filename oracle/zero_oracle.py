@@ -52,6 +52,11 @@ accumulation precision, the overflow policy) the plainest reading is taken:
 * emit:     allgather[off + j] = fp16 round-to-nearest-even of the fp32 master.
 * plan:     tensors packed in list order; S = A*ceil(Psi/(Nd*A)); rank r owns
             [r*S, (r+1)*S); the padding sits at the tail of rank Nd-1.
+* gather:   with the parameters partitioned too (Pos+g+p; dissection "ZeRO-3"
+            and "Forward/Backward Under ZeRO-3": a layer's parameters are
+            gathered when the computation reaches it, used, then released),
+            flat element f is read from its owner's window, window f // S at
+            position f % S; a layer is the flat range of its tensors.
 """
 from __future__ import annotations
 
@@ -243,6 +248,21 @@ def emit(master: np.ndarray) -> np.ndarray:
 # mixed-precision training -- anthology note, "Connections" -- whose loss
 # scale these implement; the pages themselves give no policy).
 # --------------------------------------------------------------------------
+def gather(windows: Sequence[np.ndarray], part: int, lo: int, hi: int) -> np.ndarray:
+    """Flat elements [lo, hi) of the partitioned parameters, read from the
+    owners' windows (each of `part` elements) one owner at a time."""
+    pieces = []
+    f = lo
+    while f < hi:
+        r = f // part
+        take = min(hi, (r + 1) * part) - f
+        pieces.append(windows[r][f - r * part:f - r * part + take])
+        f += take
+    if not pieces:
+        return np.empty(0, dtype=windows[0].dtype if len(windows) else np.float16)
+    return np.concatenate(pieces)
+
+
 def scaler_update(scale: float, good: int, overflow: bool, growth: float, backoff: float,
                   interval: int):
     """Next (scale, good_steps) after a step with the given overflow flag."""

@@ -525,3 +525,86 @@ def test_planted_clip_mistakes_are_caught(kind):
         torch.nn.utils.clip_grad_norm_([t], max_norm, foreach=False)
         caught |= not np.allclose(mine, t.grad.numpy(), rtol=1e-15, atol=0)
     assert caught
+
+
+# ----------------------------------------------------------------- Pos+g+p gather
+def _partitioned(numels, nd, align, seed):
+    """Tensors of random fp16 values placed into the owners' windows by the
+    planner's fragments (tensor_off -> rank, local_off): a placement written
+    from the fragment description, independent of the gather's indexing."""
+    g = np.random.default_rng(seed)
+    tensors = [g.standard_normal(n).astype(F16) for n in numels]
+    p = oracle.plan(numels, nd, align)
+    windows = [np.zeros(p.part, dtype=F16) for _ in range(nd)]
+    for f in p.frags:
+        windows[f.rank][f.local_off:f.local_off + f.length] = tensors[f.tensor][f.tensor_off:f.tensor_off + f.length]
+    return tensors, p, windows
+
+
+def _gather_round_trips(gather, trials=60):
+    """True if every run of consecutive tensors of random tensor lists,
+    placed through the planner's fragments, gathers back unchanged and the
+    padding gathers as zeros."""
+    g = np.random.default_rng(41)
+    for trial in range(trials):
+        nt = int(g.integers(1, 12))
+        numels = [int(x) for x in g.integers(0, 300, nt)]
+        nd = int(g.integers(1, 9))
+        align = int(g.choice([8, 16, 64]))
+        tensors, p, windows = _partitioned(numels, nd, align, trial)
+        offs = np.concatenate([[0], np.cumsum(numels)]).astype(int)
+        for i in range(nt):
+            for j in range(i + 1, nt + 1):
+                got = gather(windows, p.part, int(offs[i]), int(offs[j]))
+                want = np.concatenate([tensors[k] for k in range(i, j)])
+                if got.shape != want.shape or not np.array_equal(got.view(np.uint16), want.view(np.uint16)):
+                    return False
+        pad = gather(windows, p.part, p.psi, p.padded)
+        if pad.size != p.pad or np.any(pad.view(np.uint16)):
+            return False
+        # short ranges around every window boundary, against the tensors
+        # laid end to end (plus the zero padding)
+        flat = np.concatenate(tensors + [np.zeros(p.pad, dtype=F16)])
+        for r in range(1, nd):
+            b0 = r * p.part
+            for lo, hi in ((b0 - 1, b0), (b0 - 1, b0 + 1), (b0 - 2, b0 + 3), (b0, b0 + 1)):
+                lo, hi = max(lo, 0), min(hi, p.padded)
+                got = gather(windows, p.part, lo, hi)
+                if got.shape != (hi - lo,) or not np.array_equal(got.view(np.uint16), flat[lo:hi].view(np.uint16)):
+                    return False
+    return True
+
+
+def test_gather_round_trip_through_plan():
+    """Every tensor (and every run of consecutive tensors, a 'layer')
+    gathered from the windows equals the tensor(s) placed there through the
+    planner's fragments; the padding gathers as zeros."""
+    assert _gather_round_trips(oracle.gather)
+
+
+def test_gather_special_cases():
+    tensors, p, windows = _partitioned([1000, 3, 2500, 17], 4, 8, 7)
+    assert oracle.gather(windows, p.part, 5, 5).size == 0
+    r = 2
+    lo = r * p.part + 3
+    assert np.array_equal(oracle.gather(windows, p.part, lo, lo + 10), windows[r][3:13])
+    whole = oracle.gather(windows, p.part, 0, p.padded)
+    assert np.array_equal(whole, np.concatenate(windows))
+    # a range that starts and ends exactly on window boundaries
+    assert np.array_equal(oracle.gather(windows, p.part, p.part, 3 * p.part), np.concatenate(windows[1:3]))
+
+
+@pytest.mark.parametrize("kind", ["global_offset", "window_of_next_element", "last_piece_dropped"])
+def test_planted_gather_mistakes_are_caught(kind):
+    def bad_gather(windows, part, lo, hi):
+        pieces, f = [], lo
+        while f < hi:
+            r = (f + 1) // part if kind == "window_of_next_element" else f // part
+            off = f if kind == "global_offset" else f - r * part
+            take = min(hi, (r + 1) * part) - f  # >= 1: every variant advances
+            if not (kind == "last_piece_dropped" and f + take >= hi and f > lo):
+                pieces.append(windows[r][max(off, 0):max(off, 0) + take])
+            f += take
+        return np.concatenate(pieces) if pieces else np.empty(0, F16)
+
+    assert not _gather_round_trips(bad_gather)
