@@ -53,6 +53,9 @@ def parse():
                     help="bucketed step: copy each bucket into one of two constant-size receive "
                          "buffers on a side stream (the simulated reduce-scatter arrival), "
                          "overlapped with the previous bucket's step")
+    ap.add_argument("--gather-layers", action="store_true",
+                    help="time the Pos+g+p on-demand gather of every layer (GPT-2 shaped workloads) "
+                         "instead of the step")
     a = ap.parse_args()
     if a.bucket_elems < 0 or a.bucket_elems % 8 or (a.bucket_elems and a.max_grad_norm > 0):
         ap.error("--bucket-elems must be a multiple of 8, and cannot be combined with clipping")
@@ -123,12 +126,90 @@ def cpu_baseline(w, n_sample, budget_s):
             "gbs": rate * (2 * w.nd + 26) / 1e9}
 
 
+def bench_gather(args):
+    """Pos+g+p: gather every layer of a GPT-2 shaped list (one forward's
+    worth of on-demand gathers, Psi elements) from the Nd owners' windows
+    into two constant-size layer buffers used alternately (a layer buffer is
+    released by reusing it two layers later)."""
+    import torch
+    from workloads import configs, gen
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    w = configs.ALL[args.workload]
+    if len(w.numels) < 16:
+        log(f"--gather-layers needs a GPT-2 shaped workload (c2 or c3), not {w.key}")
+        sys.exit(2)
+    plan, _ = B.plan_partitions(list(w.numels), w.nd, 256)
+    part = plan["part"]
+    n_layer = (len(w.numels) - 4) // 12
+    ranges = configs.layer_ranges(w.numels, configs.gpt2_layers(n_layer))
+    dev = torch.device("cuda", 0)
+    # enough copies of the windows that one pass reads more than 1.5 GB of
+    # windows no earlier pass left in the MALL
+    copies = max(1, min(8, -(-int(1.5e9) // (2 * plan["padded"]))))
+    sets = []
+    for c in range(copies):
+        ws = []
+        for r in range(w.nd):
+            t = torch.empty(part, dtype=torch.float32, device=dev)
+            gen.device_fill_params(t, w.seed + 97 * c + r, w.param_sigma, max(0, min(part, w.psi - r * part)))
+            ws.append(t.to(torch.float16))
+            del t
+        sets.append(ws)
+    biggest = max(hi - lo for lo, hi in ranges)
+    bufs = [torch.empty(biggest, dtype=torch.float16, device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream()
+    log(f"gather: {w.key}, {len(ranges)} layers (largest {biggest} elements), Nd={w.nd} windows of {part}, "
+        f"{copies} window set(s)")
+
+    def one_pass(i):
+        ws = sets[i % copies]
+        for k, (lo, hi) in enumerate(ranges):
+            B.gather_params(ws, part, lo, hi, bufs[k % 2], stream)
+
+    for i in range(args.warmup):
+        one_pass(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        one_pass(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    launches = sum(1 + (hi - 1) // part - lo // part for lo, hi in ranges if hi > lo)
+    gbs = 4 * w.psi / (ms * 1e-3) / 1e9
+    log(f"gather pass: {ms * 1e3:.1f} us ({launches} launches), {gbs:.0f} GB/s")
+    out = {
+        "metric": "parameter elements gathered/sec (Pos+g+p on-demand layer gather), 1 MI355X",
+        "value": w.psi / (ms * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "wall_ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.key}: every layer of {w.title}", "layers": len(ranges),
+                   "largest_layer": biggest, "nd": w.nd, "window": part, "launches_per_pass": launches,
+                   "window_sets_rotated": copies},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                     "algorithmic_bytes_per_pass": 4 * w.psi, "kernel": "copy_f16_kernel",
+                     "kernel_fingerprint": kernel_fingerprint()},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the step of one rank runs on one MI355X and no "
               f"collective is part of this path (asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
+    if args.gather_layers:
+        bench_gather(args)
+        return
 
     import torch
     from workloads import configs, gen

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define ZERO_DP_ABI_VERSION 3
+#define ZERO_DP_ABI_VERSION 4
 
 /* ---- status codes --------------------------------------------------- */
 #define ZERO_OK          0
@@ -319,6 +319,33 @@ int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st,
  * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EHIP. */
 int zero_restore_skipped(const zero_adam_state* st, int64_t n, uint16_t* allgather,
                          int64_t allgather_off, void* stream);
+
+/* ---- Pos+g+p on-demand parameter gather -------------------------------
+ * With the parameters partitioned too (Pos+g+p), rank r keeps only its
+ * fp16 window of the flat parameter buffer, and a layer's parameters are
+ * gathered when the computation reaches the layer, used, then released
+ * (trishampatil dissection, sections "ZeRO-3" and "Forward/Backward Under
+ * ZeRO-3"; the two gathers per step are the extra Psi of the 3Psi volume).
+ * This copies flat elements [lo, hi) from their owners' windows into dst:
+ *   dst[i] = windows[f / part][f % part] with f = lo + i, for i < hi - lo.
+ * A layer is the flat range of its tensors (the fragments
+ * zero_plan_partitions reports give the offsets).  Release is the caller
+ * reusing dst (a constant-size layer buffer) for the next layer.
+ *   windows: host array of nd device pointers, each to `part` fp16
+ *     elements (2-byte aligned); only the windows that [lo, hi) touches
+ *     are read, the others may be NULL.
+ *   part: S, elements per window (zero_plan.part).  0 <= lo <= hi <= nd*part.
+ *   dst: device, hi - lo elements, 2-byte aligned, overlapping no window
+ *     piece it reads.  A piece whose source and dst addresses agree modulo
+ *     16 bytes moves 16-byte vectors (always the case for windows and dst
+ *     that are 16-byte aligned and lo a multiple of 8); others move
+ *     element-wise.
+ * One launch per window touched, in stream order.  Errors: ZERO_EINVAL,
+ * ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EALIAS, ZERO_EHIP (nothing is launched
+ * unless every piece is valid).
+ */
+int zero_gather_params(const uint16_t* const* windows, int32_t nd, int64_t part,
+                       int64_t lo, int64_t hi, uint16_t* dst, void* stream);
 
 /* ---- emit (all-gather half) ------------------------------------------
  * allgather[allgather_off + j] = fp16_RNE(master[j]) for j < n (IEEE

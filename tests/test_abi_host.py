@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(L):
     for name in declared:
         assert hasattr(L, name), name
     assert declared == set(B.EXPORTED)
-    assert L.zero_abi_version() == B.ABI_VERSION == 3
+    assert L.zero_abi_version() == B.ABI_VERSION == 4
 
 
 def test_strerror(L):
@@ -133,11 +133,24 @@ def test_ctl_init():
 A = 1 << 20  # fake, 16-byte aligned "device" addresses; never dereferenced
 
 
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+# fake addresses must never reach a real device, even through a validation bug
+no_gpu = pytest.mark.skipif(_gpu_visible(), reason="uses fake device addresses; host-only check")
+
+
 def _state(base=1 << 24, n=64, ctl=1 << 30):
     return B.adam_state([base, base + 4 * n * 2], [base + 4 * n * 4, base + 4 * n * 6],
                         [base + 4 * n * 8, base + 4 * n * 10], ctl)
 
 
+@no_gpu
 def test_step_validation(L):
     hp = B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0)
     ok_src = B.grad_src(A, 64, 0, 64, 4, 1024.0)
@@ -183,6 +196,7 @@ def test_step_validation(L):
     assert step(ag=1 << 29, off=3) == B.ZERO_EALIGN
 
 
+@no_gpu
 def test_clipped_validation(L):
     hp = B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0, max_grad_norm=1.0)
     src = B.grad_src(A, 64, 0, 64, 4, 1024.0)
@@ -199,6 +213,7 @@ def test_clipped_validation(L):
     assert step(hpp=B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0, max_grad_norm=float("inf"))) == B.ZERO_EINVAL
 
 
+@no_gpu
 def test_bucket_validation(L):
     hp = B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0)
     src = B.grad_src(A, 16, 0, 16, 4, 1024.0)  # a bucket of 16 elements
@@ -224,6 +239,32 @@ def test_bucket_validation(L):
         B.ZERO_EINVAL
 
 
+@no_gpu
+def test_gather_validation(L):
+    part = 1024
+    wins = (C.c_void_p * 4)(1 << 24, 1 << 25, 1 << 26, 1 << 27)
+
+    def g(lo, hi, dst=1 << 29, w=wins, nd=4, prt=part):
+        return L.zero_gather_params(w, nd, prt, lo, hi, dst, None)
+
+    assert g(0, 10, w=None) == B.ZERO_EINVAL
+    assert g(0, 10, nd=0) == B.ZERO_EINVAL
+    assert g(0, 10, prt=0) == B.ZERO_EINVAL
+    assert g(-1, 10) == B.ZERO_EINVAL
+    assert g(10, 9) == B.ZERO_EINVAL
+    assert g(0, 4 * part + 1) == B.ZERO_EINVAL          # past the last window
+    assert g(0, 10, dst=None) == B.ZERO_EINVAL
+    assert g(0, 10, dst=(1 << 29) + 1) == B.ZERO_EALIGN  # fp16 elements are 2-byte aligned
+    assert g(0, 10, prt=2**62) == B.ZERO_EOVERFLOW     # 4 windows of 2^62 elements
+    odd = (C.c_void_p * 4)(1 << 24, (1 << 25) + 1, 1 << 26, 1 << 27)
+    assert g(part, part + 8, w=odd) == B.ZERO_EALIGN
+    holes = (C.c_void_p * 4)(1 << 24, None, 1 << 26, 1 << 27)
+    assert g(part - 4, part + 4, w=holes) == B.ZERO_EINVAL  # window 1 is needed
+    assert g(0, 2 * part, dst=(1 << 25) + 100) == B.ZERO_EALIAS  # dst inside window 1's piece
+    assert g(7, 7) == B.ZERO_OK                          # empty: nothing launched
+
+
+@no_gpu
 def test_other_validation(L):
     src = B.grad_src(A, 64, 0, 64, 4, 1024.0)
     assert L.zero_reduce_owned(C.byref(src), None, None, 1 << 26, 1 << 28, None) == B.ZERO_EINVAL

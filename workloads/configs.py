@@ -23,6 +23,25 @@ def gpt2_numels(n_layer: int, d: int, vocab: int = 50257, n_ctx: int = 1024) -> 
     return out
 
 
+def gpt2_layers(n_layer: int) -> List[Tuple[int, int]]:
+    """Tensor index ranges [first, last) of the units a Pos+g+p forward
+    gathers one at a time: the embeddings (wte, wpe), each transformer block
+    (its 12 tensors), the final layer norm."""
+    out = [(0, 2)]
+    for i in range(n_layer):
+        out.append((2 + 12 * i, 14 + 12 * i))
+    out.append((2 + 12 * n_layer, 4 + 12 * n_layer))
+    return out
+
+
+def layer_ranges(numels, layers) -> List[Tuple[int, int]]:
+    """Flat element ranges [lo, hi) of tensor index ranges in a packed list."""
+    offs = [0]
+    for n in numels:
+        offs.append(offs[-1] + n)
+    return [(offs[a], offs[b]) for a, b in layers]
+
+
 @dataclass(frozen=True)
 class Workload:
     key: str

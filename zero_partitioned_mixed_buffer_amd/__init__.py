@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     adam_step_bucket,
     adam_step_clipped,
     emit_fp16,
+    gather_params,
     grad_src,
     memory_model,
     plan_partitions,

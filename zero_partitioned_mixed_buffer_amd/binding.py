@@ -26,9 +26,9 @@ EXPORTED = (
     "zero_strerror", "zero_last_hip_error", "zero_abi_version", "zero_plan_partitions",
     "zero_memory_model", "zero_workspace_bytes", "zero_reduce_owned", "zero_ctl_init",
     "zero_adam_step", "zero_adam_step_clipped", "zero_adam_step_bucket", "zero_restore_skipped",
-    "zero_emit_fp16",
+    "zero_emit_fp16", "zero_gather_params",
 )
-ABI_VERSION = 3
+ABI_VERSION = 4
 BUCKET_FIRST = 1
 BUCKET_LAST = 2
 
@@ -108,8 +108,10 @@ def lib():
                                         C.c_int64, P, C.c_int64, C.c_int32, P, P]
     L.zero_restore_skipped.argtypes = [C.POINTER(AdamState), C.c_int64, P, C.c_int64, P]
     L.zero_emit_fp16.argtypes = [P, C.c_int64, P, C.c_int64, P]
+    L.zero_gather_params.argtypes = [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int64, C.c_int64, P, P]
     for name in ("zero_plan_partitions", "zero_memory_model", "zero_reduce_owned", "zero_adam_step",
-                 "zero_adam_step_clipped", "zero_adam_step_bucket", "zero_restore_skipped", "zero_emit_fp16"):
+                 "zero_adam_step_clipped", "zero_adam_step_bucket", "zero_restore_skipped", "zero_emit_fp16",
+                 "zero_gather_params"):
         getattr(L, name).restype = C.c_int
     if L.zero_abi_version() != ABI_VERSION:
         raise RuntimeError("libzero_dp.so ABI version mismatch")
@@ -236,3 +238,11 @@ def restore_skipped(state: AdamState, n: int, allgather, allgather_off: int, str
 def emit_fp16(master, n: int, allgather, allgather_off: int, stream=None):
     _check(lib().zero_emit_fp16(_ptr(master), int(n), _ptr(allgather), int(allgather_off),
                                 _stream(stream)), "zero_emit_fp16")
+
+
+def gather_params(windows: Sequence, part: int, lo: int, hi: int, dst, stream=None):
+    """Flat elements [lo, hi) of the partitioned fp16 parameters into dst;
+    ``windows`` lists the Nd owners' windows (tensors, addresses or None)."""
+    arr = (C.c_void_p * max(len(windows), 1))(*[_ptr(w) for w in windows])
+    _check(lib().zero_gather_params(arr, len(windows), int(part), int(lo), int(hi), _ptr(dst), _stream(stream)),
+           "zero_gather_params")

@@ -108,6 +108,9 @@ __device__ __forceinline__ hvec pack_v(const float (&x)[kV]) {
 #ifndef ZDP_BPC_CLIP
 #define ZDP_BPC_CLIP 1  // the same cap for the clipped update pass
 #endif
+#ifndef ZDP_BPC_COPY
+#define ZDP_BPC_COPY 2  // workgroups per CU of the parameter gather copy
+#endif
 #ifndef ZDP_XCD_REMAP
 #define ZDP_XCD_REMAP 1  // 1: consecutive logical workgroups on one XCD
 #endif
@@ -827,9 +830,52 @@ __global__ void __launch_bounds__(kBlock) restore_kernel(const float* p0, const 
     emit_range(ctl->cur ? p1 : p0, ag, n);
 }
 
+// ------------------------------------------------- Pos+g+p parameter gather
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCopyU = 4;  // 16-byte vectors per lane per iteration
+
+// dst[i] = src[i] for i < n (fp16 bit patterns): one piece of a layer
+// gather, from one owner's window.  When src and dst agree modulo 16 bytes
+// the body moves 16-byte vectors, kCopyU per lane per iteration with all
+// loads issued before the stores, each instruction lane-contiguous, and
+// each workgroup a contiguous chunk; the head and tail go element-wise.
+// Otherwise every element moves on its own (2-byte accesses, coalesced).
+__global__ void __launch_bounds__(kBlock) copy_f16_kernel(const uint16_t* __restrict__ src,
+                                                          uint16_t* __restrict__ dst, int64_t n) {
+    const uintptr_t sa = reinterpret_cast<uintptr_t>(src), da = reinterpret_cast<uintptr_t>(dst);
+    if (((sa ^ da) & 15u) != 0) {
+        const int64_t nlanes = static_cast<int64_t>(gridDim.x) * kBlock;
+        for (int64_t i = logical_block() * kBlock + threadIdx.x; i < n; i += nlanes) dst[i] = src[i];
+        return;
+    }
+    int64_t head = static_cast<int64_t>(((16u - (da & 15u)) & 15u) / 2u);
+    if (head > n) head = n;
+    const int64_t nv = (n - head) / 8;
+    const u32x4* __restrict__ sv = reinterpret_cast<const u32x4*>(src + head);
+    u32x4* __restrict__ dv = reinterpret_cast<u32x4*>(dst + head);
+    // full chunks of kCopyU * kBlock vectors, one per workgroup at a time
+    // (no predicates, so all kCopyU loads are in flight together)
+    constexpr int64_t kChunk = static_cast<int64_t>(kCopyU) * kBlock;
+    const int64_t nfull = nv / kChunk;
+    for (int64_t c = logical_block(); c < nfull; c += gridDim.x) {
+        const int64_t base = c * kChunk + threadIdx.x;
+        u32x4 v[kCopyU];
+#pragma unroll
+        for (int u = 0; u < kCopyU; ++u) v[u] = ldg(sv + base + u * kBlock);
+#pragma unroll
+        for (int u = 0; u < kCopyU; ++u) stg(dv + base + u * kBlock, v[u]);
+    }
+    // the last partial chunk, the head and the tail: the last workgroup
+    if (blockIdx.x == gridDim.x - 1) {
+        for (int64_t i = nfull * kChunk + threadIdx.x; i < nv; i += kBlock) stg(dv + i, ldg(sv + i));
+        for (int64_t i = threadIdx.x; i < head; i += kBlock) dst[i] = src[i];
+        for (int64_t i = head + nv * 8 + threadIdx.x; i < n; i += kBlock) dst[i] = src[i];
+    }
+}
+
 // ---------------------------------------------------------------- host glue
 constexpr int kMaxDevices = 64;
-enum KernelId { kReduce = 0, kFused = 1, kEmit = 2, kRestore = 3, kClip = 4, kKernels = 5 };
+enum KernelId { kReduce = 0, kFused = 1, kEmit = 2, kRestore = 3, kClip = 4, kCopy = 5, kKernels = 6 };
 std::atomic<int> g_grid_cache[kKernels][kMaxDevices];  // 0 = not computed yet
 
 // Workgroups that keep every CU of the current device busy at the kernel's
@@ -847,6 +893,7 @@ int resident_blocks(KernelId id) {
         case kEmit: fn = reinterpret_cast<const void*>(emit_kernel); break;
         case kRestore: fn = reinterpret_cast<const void*>(restore_kernel); break;
         case kClip: fn = reinterpret_cast<const void*>(clipped_update_kernel); break;
+        case kCopy: fn = reinterpret_cast<const void*>(copy_f16_kernel); break;
         default: return 1024;
     }
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -855,7 +902,11 @@ int resident_blocks(KernelId id) {
         (void)hipGetLastError();
         return 1024;
     }
-    const int cap = id == kFused ? ZDP_BPC : id == kReduce ? ZDP_BPC_REDUCE : id == kClip ? ZDP_BPC_CLIP : 0;
+    const int cap = id == kFused    ? ZDP_BPC
+                    : id == kReduce ? ZDP_BPC_REDUCE
+                    : id == kClip   ? ZDP_BPC_CLIP
+                    : id == kCopy   ? ZDP_BPC_COPY
+                                    : 0;
     if (cap > 0 && per_cu > cap) per_cu = cap;
     int blocks = cus * per_cu;
     if (blocks > zdp::kMaxBlocks) blocks = zdp::kMaxBlocks;
@@ -869,6 +920,17 @@ int grid_for(KernelId id, int64_t n) {
     int64_t cap = static_cast<int64_t>(resident_blocks(id)) * ZDP_GRID_MULT;
     if (ZDP_GRID_MULT == 0 || cap > zdp::kMaxBlocks) cap = zdp::kMaxBlocks;
     int64_t g = need < cap ? need : cap;
+    return static_cast<int>(g < 1 ? 1 : g);
+}
+
+// Workgroups of one gather piece of n elements: enough chunks of kCopyU
+// vectors per lane, at most the resident limit (a multiple of 8, so the
+// XCD-contiguous order applies).
+int copy_grid(int64_t n) {
+    const int64_t chunk = static_cast<int64_t>(kCopyU) * kBlock * 8;
+    const int64_t need = (n + chunk - 1) / chunk;
+    const int64_t cap = resident_blocks(kCopy);
+    const int64_t g = need < cap ? need : cap;
     return static_cast<int>(g < 1 ? 1 : g);
 }
 
@@ -1106,6 +1168,41 @@ int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st, c
     fused_step_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
         make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), a, make_ws(workspace));
     return finish_launch();
+}
+
+int zero_gather_params(const uint16_t* const* windows, int32_t nd, int64_t part, int64_t lo, int64_t hi,
+                       uint16_t* dst, void* stream) {
+    if (windows == nullptr || nd < 1 || part < 1 || lo < 0 || hi < lo) return ZERO_EINVAL;
+    int64_t total = 0, bytes = 0;
+    if (zdp::mul_overflows(static_cast<int64_t>(nd), part, &total)) return ZERO_EOVERFLOW;
+    if (hi > total) return ZERO_EINVAL;
+    const int64_t n = hi - lo;
+    if (n == 0) return ZERO_OK;  // nothing to gather
+    if (dst == nullptr) return ZERO_EINVAL;
+    if (zdp::mul_overflows(n, 2, &bytes)) return ZERO_EOVERFLOW;
+    if ((reinterpret_cast<uintptr_t>(dst) & 1u) != 0) return ZERO_EALIGN;
+    const Range out = bytes_of(dst, n, 2);
+    // every piece is validated before anything is launched
+    for (int64_t f = lo; f < hi;) {
+        const int64_t r = f / part;
+        const int64_t take = ((r + 1) * part < hi ? (r + 1) * part : hi) - f;
+        const uint16_t* w = windows[r];
+        if (w == nullptr) return ZERO_EINVAL;
+        if ((reinterpret_cast<uintptr_t>(w) & 1u) != 0) return ZERO_EALIGN;
+        if (overlap(bytes_of(w + (f - r * part), take, 2), out)) return ZERO_EALIAS;
+        f += take;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    for (int64_t f = lo; f < hi;) {
+        const int64_t r = f / part;
+        const int64_t take = ((r + 1) * part < hi ? (r + 1) * part : hi) - f;
+        copy_f16_kernel<<<copy_grid(take), kBlock, 0, s>>>(windows[r] + (f - r * part), dst + (f - lo), take);
+        const int rc = finish_launch();
+        if (rc != ZERO_OK) return rc;
+        f += take;
+    }
+    return ZERO_OK;
 }
 
 int zero_restore_skipped(const zero_adam_state* st, int64_t n, uint16_t* allgather,
