@@ -109,7 +109,7 @@ __device__ __forceinline__ hvec pack_v(const float (&x)[kV]) {
 #define ZDP_BPC_CLIP 1  // the same cap for the clipped update pass
 #endif
 #ifndef ZDP_BPC_COPY
-#define ZDP_BPC_COPY 2  // workgroups per CU of the parameter gather copy
+#define ZDP_BPC_COPY 1  // workgroups per CU of the parameter gather copy
 #endif
 #ifndef ZDP_XCD_REMAP
 #define ZDP_XCD_REMAP 1  // 1: consecutive logical workgroups on one XCD
@@ -831,8 +831,11 @@ __global__ void __launch_bounds__(kBlock) restore_kernel(const float* p0, const 
 }
 
 // ------------------------------------------------- Pos+g+p parameter gather
+#ifndef ZDP_COPY_U
+#define ZDP_COPY_U 4
+#endif
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kCopyU = 4;  // 16-byte vectors per lane per iteration
+constexpr int kCopyU = ZDP_COPY_U;  // 16-byte vectors per lane per iteration
 
 // dst[i] = src[i] for i < n (fp16 bit patterns): one piece of a layer
 // gather, from one owner's window.  When src and dst agree modulo 16 bytes
