@@ -55,6 +55,16 @@ def test_fused_step_small(n, nd):
     assert min(s[0] for s in stats) >= 0.999
 
 
+@pytest.mark.parametrize("nd", list(range(1, 18)))
+def test_fused_step_every_nd_many_groups_per_lane(nd):
+    """Every slice count of the compile-time paths (one and two groups
+    ahead, and the chunked sum past 16), on a window where each lane owns 6
+    or 7 element groups (the prefetch rotations run several full cycles)
+    and the last group is ragged."""
+    n = 4 * 65536 * 6 + 4 * 1000 + 3
+    _run_case(n, nd, steps=2, seed=300 + nd)
+
+
 @pytest.mark.parametrize("nd", [4, 8, 64])
 def test_fused_step_adamw_many_steps(nd):
     hp = dict(HP, weight_decay=0.01)

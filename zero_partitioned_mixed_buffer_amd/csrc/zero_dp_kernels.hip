@@ -600,14 +600,24 @@ __device__ __forceinline__ void pf_finish(const hvec (&w)[R], const fvec& pv, co
     if (f.ag != nullptr) stg(reinterpret_cast<hvec*>(f.ag + j), pack_v(po));
 }
 
+#ifndef ZDP_PF_NB
+#define ZDP_PF_NB 4  // register sets of the two-ahead prefetch
+#endif
+#ifndef ZDP_PF2_MINR
+#define ZDP_PF2_MINR 7  // Nd range that prefetches two groups ahead
+#endif
+#ifndef ZDP_PF2_MAXR
+#define ZDP_PF2_MAXR 9
+#endif
+
 // Full groups gi, gi+step, ... < end when all Nd = R slices fit in one
 // chunk: the next group's R + 3 loads are issued before the current group
 // is summed and updated, so its memory latency overlaps this group's fp64
 // work.  The last iteration re-reads its own group instead of running past
 // the end (the values are not used).
 template <int R>
-__device__ void pf_run(int64_t gi, int64_t end, int64_t step, const SrcArgs& src, const FusedPtrs& f,
-                       const AdamScalars& c, double& sq, int& bad) {
+__device__ void pf_run1(int64_t gi, int64_t end, int64_t step, const SrcArgs& src, const FusedPtrs& f,
+                        const AdamScalars& c, double& sq, int& bad) {
     if (gi >= end) return;
     hvec w[R];
     fvec p, m, v;
@@ -625,6 +635,50 @@ __device__ void pf_run(int64_t gi, int64_t end, int64_t step, const SrcArgs& src
         if (gn >= end) break;
         gi = gn;
     }
+}
+
+// The same, two groups ahead: group gi + 2*step is loaded before group gi
+// is finished, from NB register sets used in rotation (the loop is unrolled
+// NB times, so no set is copied while its loads are in flight, and a set is
+// reloaded NB - 2 phases after its last use).  Measured faster for
+// 7 <= Nd <= 9 only; elsewhere one group ahead is as fast or faster.
+template <int R, int NB>
+__device__ void pf_run2(int64_t gi, int64_t end, int64_t step, const SrcArgs& src, const FusedPtrs& f,
+                        const AdamScalars& c, double& sq, int& bad) {
+    if (gi >= end) return;
+    hvec w[NB][R];
+    fvec p[NB], m[NB], v[NB];
+    pf_load<R>(w[0], p[0], m[0], v[0], src, f, gi * kV);
+    {
+        const int64_t g1 = gi + step;
+        pf_load<R>(w[1], p[1], m[1], v[1], src, f, (g1 < end ? g1 : gi) * kV);
+    }
+    bool more = true;
+    while (more) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            if (more) {
+                const int ld = (k + 2) % NB;
+                const int64_t g2 = gi + 2 * step;
+                pf_load<R>(w[ld], p[ld], m[ld], v[ld], src, f, (g2 < end ? g2 : gi) * kV);
+                __builtin_amdgcn_sched_barrier(0);
+                pf_finish<R>(w[k], p[k], m[k], v[k], src, f, c, gi * kV, sq, bad);
+                if (gi + step >= end)
+                    more = false;
+                else
+                    gi += step;
+            }
+        }
+    }
+}
+
+template <int R>
+__device__ void pf_run(int64_t gi, int64_t end, int64_t step, const SrcArgs& src, const FusedPtrs& f,
+                       const AdamScalars& c, double& sq, int& bad) {
+    if constexpr (ZDP_PF_NB >= 3 && R >= ZDP_PF2_MINR && R <= ZDP_PF2_MAXR)
+        pf_run2<R, ZDP_PF_NB>(gi, end, step, src, f, c, sq, bad);
+    else
+        pf_run1<R>(gi, end, step, src, f, c, sq, bad);
 }
 
 template <int R>
