@@ -92,6 +92,29 @@ def measured_traffic(workload):
     return None
 
 
+def attainable_copy(torch, dev, B, reps=5):
+    """Attainable streaming bandwidth on this machine: the library's own copy
+    kernel (zero_gather_params over one 4 GiB window) moving 4 GiB into
+    another 4 GiB buffer; GB/s of read + write."""
+    n = 1 << 31  # fp16 elements
+    src = torch.empty(n, dtype=torch.float16, device=dev)
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    B.gather_params([src], n, 0, n, dst, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        B.gather_params([src], n, 0, n, dst, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_gbs": 4 * n / (ms * 1e-3) / 1e9, "bytes_moved": 4 * n, "kernel": "copy_f16_kernel",
+            "note": "4 GiB read + 4 GiB written per copy, mean of 5 back-to-back copies"}
+
+
 def calibration_copy(torch, dev):
     """A plain device copy of known size (256 MiB -> 256 MiB) for scaling the
     FETCH_SIZE / WRITE_SIZE counters of a profiled run; not timed."""
@@ -336,14 +359,28 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     kern_avg = e0.elapsed_time(e1) / args.steps
+    # Distribution: the same launches, each between its own pair of events
+    # (the records add a little to every launch, so the mean above is the
+    # figure reported; these are its spread).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        launch(args.warmup + 2 * args.steps + i, restore=False)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    pct = lambda q: per[min(len(per) - 1, int(round(q * (len(per) - 1))))]
     for r in range(n_shards):
         B.restore_skipped(shards[r].state, S, ag, ag_offs[r], stream)
     ctls = [sh.control() for sh in shards]
-    if sum(c["t"] for c in ctls) != args.warmup + 2 * args.steps or any(c["skipped"] for c in ctls):
+    if sum(c["t"] for c in ctls) != args.warmup + 3 * args.steps or any(c["skipped"] for c in ctls):
         log(f"unexpected control state after timing: {ctls}")
         sys.exit(1)
 
     calibration_copy(torch, dev)
+    attain = attainable_copy(torch, dev, B)
+    log(f"attainable copy on this box: {attain['copy_gbs']:.0f} GB/s")
     traffic = None if (clipped or bucketed) else measured_traffic(w.key)
 
     ms_step = wall * 1e3 / args.steps
@@ -403,6 +440,9 @@ def main():
             "kernel": ("reduce_owned_kernel + clipped_update_kernel" if clipped else
                        f"fused_step_kernel x {len(buckets)} buckets" if bucketed else "fused_step_kernel"),
             "kernel_avg_us": kern_avg * 1e3,
+            "kernel_us_p10_p50_p90_per_launch_events": [pct(0.1), pct(0.5), pct(0.9)],
+            "attainable": attain,
+            "frac_of_attainable": achieved / attain["copy_gbs"],
             "kernel_fingerprint": kernel_fingerprint(),
         },
         "cpu_baseline": cpu,

@@ -133,6 +133,34 @@ def test_overflow_window_restored_bitwise():
     assert np.array_equal(bits1, bits2)
 
 
+@pytest.mark.parametrize("nd", list(range(1, 18)))
+def test_reduce_owned_every_nd_many_groups_per_lane(nd):
+    """The reduce pass for every slice count of its compile-time paths (two
+    groups ahead up to Nd = 8, one ahead to 16, chunked past 16), with 6 or
+    7 element groups per lane and a ragged tail: fp32 g bit-exact, flag
+    exact, sum of g^2 within 1e-12."""
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    n = 4 * 65536 * 6 + 4 * 1000 + 3
+    sl = gen.host_grad_slices(400 + nd, 1, 0, nd, n, 0, n, 1e-3, 1024.0)
+    s = oracle.reduce_owned(sl)
+    gg, ovf, sq = oracle.unscale(s, 1024.0)
+    stride = (n + 7) // 8 * 8
+    dsl = torch.zeros((nd, stride), dtype=torch.float16, device="cuda")
+    dsl[:, :n] = torch.from_numpy(sl).cuda()
+    out = torch.full((n + 8,), 123.0, dtype=torch.float32, device="cuda")
+    flag = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    ssq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(B.workspace_bytes(), dtype=torch.uint8, device="cuda")
+    B.reduce_owned(B.grad_src(dsl, stride, 0, n, nd, 1024.0), out, flag, ssq, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert int(flag.item()) == int(ovf) == 0
+    assert np.array_equal(got[:n].view(np.uint32), gg.astype(F32).view(np.uint32))
+    assert np.all(got[n:] == 123.0)  # nothing written past the window
+    assert float(ssq.item()) == pytest.approx(sq, rel=1e-12)
+
+
 def test_reduce_owned_parity():
     torch = torch_mod()
     from zero_partitioned_mixed_buffer_amd import binding as B
