@@ -63,6 +63,18 @@ def test_clipped_step(n, nd, max_norm):
         assert all(c == 1.0 for c in sh.coefs if c == c)
 
 
+@pytest.mark.parametrize("nd", [2, 8, 17])
+def test_clipped_many_groups_per_lane(nd):
+    """Both clipped passes on a window where each lane owns 6 or 7 element
+    groups (the prefetch rotations run several full cycles), ragged tail,
+    clipping active, one skipped step."""
+    n = 4 * 65536 * 6 + 4 * 1000 + 3
+    hp = dict(HP, weight_decay=0.01, max_grad_norm=0.05)
+    sh, _ = _run(n, nd, 3, 70 + nd, hp, bad_steps=(2,))
+    assert sh.flags == [0, 1, 0]
+    assert max(c for c in sh.coefs if c == c) < 1.0
+
+
 def test_clipped_adamw_dynamic_scaling():
     hp = dict(HP, weight_decay=0.01, max_grad_norm=5e-3, scale_interval=3, loss_scale=8192.0)
     sh, _ = _run(30000, 16, 8, 61, hp, bad_steps=(4,), sigma=1e-4)

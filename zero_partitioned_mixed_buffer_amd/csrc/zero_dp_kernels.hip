@@ -853,6 +853,64 @@ __global__ void __launch_bounds__(kBlock) ZDP_FUSED_ATTR fused_step_kernel(SrcAr
     if (last_block_totals(ws, sq, bad) && threadIdx.x == 0) finish_fused(a, cur, b1t, b2t, bad, sq, src.n);
 }
 
+// Second pass of the clipped step, per element group: g = g32 * coef from
+// the materialised fp32 gradient, then the fused step's update and emit.
+__device__ __forceinline__ void cu_load(fvec& g, fvec& p, fvec& m, fvec& v, const float* grad,
+                                        const FusedPtrs& f, int64_t j) {
+    g = ldg(reinterpret_cast<const fvec*>(grad + j));
+    p = ldg(reinterpret_cast<const fvec*>(f.pin + j));
+    m = ldg(reinterpret_cast<const fvec*>(f.min_ + j));
+    v = ldg(reinterpret_cast<const fvec*>(f.vin + j));
+}
+
+__device__ __forceinline__ void cu_finish(const fvec& gv, const fvec& pv, const fvec& mv, const fvec& vv,
+                                          const FusedPtrs& f, const AdamScalars& c, double coef, int64_t j) {
+    float po[kV], mo[kV], vo[kV];
+#pragma unroll
+    for (int e = 0; e < kV; ++e)
+        adam1(c, static_cast<double>(gv[e]) * coef, pv[e], mv[e], vv[e], po[e], mo[e], vo[e]);
+    fvec pw, mw, vw;
+#pragma unroll
+    for (int e = 0; e < kV; ++e) {
+        pw[e] = po[e];
+        mw[e] = mo[e];
+        vw[e] = vo[e];
+    }
+    stg(reinterpret_cast<fvec*>(f.pout + j), pw);
+    stg(reinterpret_cast<fvec*>(f.mout + j), mw);
+    stg(reinterpret_cast<fvec*>(f.vout + j), vw);
+    if (f.ag != nullptr) stg(reinterpret_cast<hvec*>(f.ag + j), pack_v(po));
+}
+
+// Full groups gi, gi+step, ... < end, two groups ahead from NB rotating
+// register sets (as the fused step's prefetch; past the end, group 0 is
+// loaded and ignored).
+template <int NB>
+__device__ void cu_run(int64_t gi, int64_t end, int64_t step, const float* grad, const FusedPtrs& f,
+                       const AdamScalars& c, double coef) {
+    if (gi >= end) return;
+    fvec g[NB], p[NB], m[NB], v[NB];
+    cu_load(g[0], p[0], m[0], v[0], grad, f, gi * kV);
+    cu_load(g[1], p[1], m[1], v[1], grad, f, (gi + step < end ? gi + step : 0) * kV);
+    bool more = true;
+    while (more) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            if (more) {
+                const int ld = (k + 2) % NB;
+                const int64_t g2 = gi + 2 * step < end ? gi + 2 * step : 0;
+                cu_load(g[ld], p[ld], m[ld], v[ld], grad, f, g2 * kV);
+                __builtin_amdgcn_sched_barrier(0);
+                cu_finish(g[k], p[k], m[k], v[k], f, c, coef, gi * kV);
+                if (gi + step >= end)
+                    more = false;
+                else
+                    gi += step;
+            }
+        }
+    }
+}
+
 // Second pass of the clipped step: g = g32 * coef from the materialised
 // fp32 gradient, then the update, emit and commit of the fused step.  A
 // step whose first pass found an inf/NaN touches nothing but the control
@@ -870,46 +928,22 @@ __global__ void __launch_bounds__(kBlock) ZDP_FUSED_ATTR clipped_update_kernel(
     const int cur = a.ctl->cur;
     double b1t, b2t;
     const AdamScalars c = step_scalars(a, b1t, b2t);
-    const float* __restrict__ pin = a.p[cur];
-    const float* __restrict__ min_ = a.m[cur];
-    const float* __restrict__ vin = a.v[cur];
-    float* __restrict__ pout = a.p[cur ^ 1];
-    float* __restrict__ mout = a.m[cur ^ 1];
-    float* __restrict__ vout = a.v[cur ^ 1];
-    uint16_t* __restrict__ ag = a.ag;
+    const FusedPtrs f{a.p[cur], a.m[cur], a.v[cur], a.p[cur ^ 1], a.m[cur ^ 1], a.v[cur ^ 1], a.ag};
     const int64_t ngroups = (n + kV - 1) / kV;
     const int64_t nfull = n / kV;
-    for (GroupIter it(ngroups); it.gi < it.end; it.gi += it.step) {
-        const int64_t gi = it.gi;
-        const int64_t j = gi * kV;
-        if (gi < nfull) {
-            const fvec gv = ldg(reinterpret_cast<const fvec*>(grad + j));
-            const fvec pv = ldg(reinterpret_cast<const fvec*>(pin + j));
-            const fvec mv = ldg(reinterpret_cast<const fvec*>(min_ + j));
-            const fvec vv = ldg(reinterpret_cast<const fvec*>(vin + j));
-            float po[kV], mo[kV], vo[kV];
-#pragma unroll
-            for (int e = 0; e < kV; ++e)
-                adam1(c, static_cast<double>(gv[e]) * coef, pv[e], mv[e], vv[e], po[e], mo[e], vo[e]);
-            fvec pw, mw, vw;
-#pragma unroll
-            for (int e = 0; e < kV; ++e) {
-                pw[e] = po[e];
-                mw[e] = mo[e];
-                vw[e] = vo[e];
-            }
-            stg(reinterpret_cast<fvec*>(pout + j), pw);
-            stg(reinterpret_cast<fvec*>(mout + j), mw);
-            stg(reinterpret_cast<fvec*>(vout + j), vw);
-            if (ag != nullptr) stg(reinterpret_cast<hvec*>(ag + j), pack_v(po));
-        } else {
-            for (int64_t e = j; e < n; ++e) {
+    GroupIter it(ngroups);
+    cu_run<4>(it.gi, it.end < nfull ? it.end : nfull, it.step, grad, f, c, coef);
+    if (ngroups > nfull) {
+        // the ragged tail group, by the lane whose sequence contains it
+        const int64_t g = nfull;
+        if (g >= it.gi && g < it.end && (g - it.gi) % it.step == 0) {
+            for (int64_t e = g * kV; e < n; ++e) {
                 float po, mo, vo;
-                adam1(c, static_cast<double>(grad[e]) * coef, pin[e], min_[e], vin[e], po, mo, vo);
-                pout[e] = po;
-                mout[e] = mo;
-                vout[e] = vo;
-                if (ag != nullptr) ag[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(po));
+                adam1(c, static_cast<double>(grad[e]) * coef, f.pin[e], f.min_[e], f.vin[e], po, mo, vo);
+                f.pout[e] = po;
+                f.mout[e] = mo;
+                f.vout[e] = vo;
+                if (f.ag != nullptr) f.ag[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(po));
             }
         }
     }
