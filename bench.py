@@ -201,9 +201,10 @@ def bench_gather(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
-    launches = sum(1 + (hi - 1) // part - lo // part for lo, hi in ranges if hi > lo)
+    pieces = sum(1 + (hi - 1) // part - lo // part for lo, hi in ranges if hi > lo)
+    launches = sum(-(-(1 + (hi - 1) // part - lo // part) // 16) for lo, hi in ranges if hi > lo)
     gbs = 4 * w.psi / (ms * 1e-3) / 1e9
-    log(f"gather pass: {ms * 1e3:.1f} us ({launches} launches), {gbs:.0f} GB/s")
+    log(f"gather pass: {ms * 1e3:.1f} us ({launches} launches, {pieces} window pieces), {gbs:.0f} GB/s")
     out = {
         "metric": "parameter elements gathered/sec (Pos+g+p on-demand layer gather), 1 MI355X",
         "value": w.psi / (ms * 1e-3),
@@ -214,6 +215,7 @@ def bench_gather(args):
         "data": "synthetic",
         "config": {"workload": f"{w.key}: every layer of {w.title}", "layers": len(ranges),
                    "largest_layer": biggest, "nd": w.nd, "window": part, "launches_per_pass": launches,
+                   "window_pieces_per_pass": pieces,
                    "window_sets_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": None,

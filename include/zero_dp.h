@@ -340,7 +340,8 @@ int zero_restore_skipped(const zero_adam_state* st, int64_t n, uint16_t* allgath
  *     16 bytes moves 16-byte vectors (always the case for windows and dst
  *     that are 16-byte aligned and lo a multiple of 8); others move
  *     element-wise.
- * One launch per window touched, in stream order.  Errors: ZERO_EINVAL,
+ * One launch for every 16 windows touched (one for any layer that spans
+ * at most 16 windows), in stream order.  Errors: ZERO_EINVAL,
  * ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EALIAS, ZERO_EHIP (nothing is launched
  * unless every piece is valid).
  */

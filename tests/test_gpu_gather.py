@@ -72,6 +72,19 @@ def test_gather_ranges():
             _gather_check(torch, B, ws, wh, part, lo, hi, dst_off, f"[{lo}, {hi}) dst+{dst_off}")
 
 
+def test_gather_spanning_more_windows_than_one_launch_holds():
+    """A range over 37 small windows (16 window pieces per launch, so three
+    launches), on both copy paths."""
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    nd, part = 40, 1000
+    ws = _windows(torch, nd, part, 9)
+    wh = [w.cpu().numpy() for w in ws]
+    for lo, hi in ((5, 37005), (0, nd * part), (16 * part - 3, 33 * part + 4)):
+        for dst_off in (0, 8, 3):
+            _gather_check(torch, B, ws, wh, part, lo, hi, dst_off, f"[{lo}, {hi}) dst+{dst_off}")
+
+
 def test_gather_unused_windows_may_be_null():
     torch = torch_mod()
     from zero_partitioned_mixed_buffer_amd import binding as B

@@ -993,13 +993,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCopyU = ZDP_COPY_U;  // 16-byte vectors per lane per iteration
 
 // dst[i] = src[i] for i < n (fp16 bit patterns): one piece of a layer
-// gather, from one owner's window.  When src and dst agree modulo 16 bytes
-// the body moves 16-byte vectors, kCopyU per lane per iteration with all
-// loads issued before the stores, each instruction lane-contiguous, and
-// each workgroup a contiguous chunk; the head and tail go element-wise.
-// Otherwise every element moves on its own (2-byte accesses, coalesced).
-__global__ void __launch_bounds__(kBlock) copy_f16_kernel(const uint16_t* __restrict__ src,
-                                                          uint16_t* __restrict__ dst, int64_t n) {
+// gather, from one owner's window, by the whole grid.  When src and dst
+// agree modulo 16 bytes the body moves 16-byte vectors, kCopyU per lane per
+// iteration with all loads issued before the stores, each instruction
+// lane-contiguous, and each workgroup a contiguous chunk; the head and tail
+// go element-wise.  Otherwise every element moves on its own (2-byte
+// accesses, coalesced).
+__device__ __forceinline__ void copy_piece(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                           int64_t n) {
     const uintptr_t sa = reinterpret_cast<uintptr_t>(src), da = reinterpret_cast<uintptr_t>(dst);
     if (((sa ^ da) & 15u) != 0) {
         const int64_t nlanes = static_cast<int64_t>(gridDim.x) * kBlock;
@@ -1029,6 +1030,20 @@ __global__ void __launch_bounds__(kBlock) copy_f16_kernel(const uint16_t* __rest
         for (int64_t i = threadIdx.x; i < head; i += kBlock) dst[i] = src[i];
         for (int64_t i = head + nv * 8 + threadIdx.x; i < n; i += kBlock) dst[i] = src[i];
     }
+}
+
+// The pieces of one gather (a layer's parts of consecutive windows), in
+// one launch: piece i copies len[i] elements from src[i] to dst + off[i].
+constexpr int kMaxPieces = 16;
+struct CopyPieces {
+    const uint16_t* src[kMaxPieces];
+    int64_t off[kMaxPieces];
+    int64_t len[kMaxPieces];
+    int32_t np;
+};
+
+__global__ void __launch_bounds__(kBlock) copy_f16_kernel(CopyPieces t, uint16_t* __restrict__ dst) {
+    for (int i = 0; i < t.np; ++i) copy_piece(t.src[i], dst + t.off[i], t.len[i]);
 }
 
 // ---------------------------------------------------------------- host glue
@@ -1350,15 +1365,25 @@ int zero_gather_params(const uint16_t* const* windows, int32_t nd, int64_t part,
         if (overlap(bytes_of(w + (f - r * part), take, 2), out)) return ZERO_EALIAS;
         f += take;
     }
+    // the pieces, kMaxPieces per launch (one launch for any layer that
+    // touches at most kMaxPieces windows)
     const hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     for (int64_t f = lo; f < hi;) {
-        const int64_t r = f / part;
-        const int64_t take = ((r + 1) * part < hi ? (r + 1) * part : hi) - f;
-        copy_f16_kernel<<<copy_grid(take), kBlock, 0, s>>>(windows[r] + (f - r * part), dst + (f - lo), take);
+        CopyPieces t{};
+        const int64_t first = f;
+        while (f < hi && t.np < kMaxPieces) {
+            const int64_t r = f / part;
+            const int64_t take = ((r + 1) * part < hi ? (r + 1) * part : hi) - f;
+            t.src[t.np] = windows[r] + (f - r * part);
+            t.off[t.np] = f - first;
+            t.len[t.np] = take;
+            ++t.np;
+            f += take;
+        }
+        copy_f16_kernel<<<copy_grid(f - first), kBlock, 0, s>>>(t, dst + (first - lo));
         const int rc = finish_launch();
         if (rc != ZERO_OK) return rc;
-        f += take;
     }
     return ZERO_OK;
 }
