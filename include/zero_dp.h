@@ -31,8 +31,10 @@
  *     return without synchronising.  Results are valid once the stream has
  *     reached them.  On a non-OK return nothing was enqueued, except for
  *     ZERO_EHIP, which reports a failed launch (see zero_last_hip_error).
- *   - The library allocates nothing, keeps no global mutable state and only
- *     borrows the caller's buffers for the duration of the enqueued work.
+ *   - The library allocates nothing and only borrows the caller's buffers for
+ *     the duration of the enqueued work.  Its only mutable state is a
+ *     per-device cache of launch sizes (filled once, thread-safe) and the
+ *     per-thread last HIP error.
  *   - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
  *   - Element counts and offsets are int64_t; sizes up to 2^62 elements.
  *   - A data pointer may be NULL when its element count is 0 (empty window).

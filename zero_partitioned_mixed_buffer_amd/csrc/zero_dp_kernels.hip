@@ -35,9 +35,10 @@
 //                          max_norm / (norm + 1e-6)), update, emit, commit
 //   emit_kernel, restore_kernel   fp16 window from the fp32 master (initial
 //                          fill; re-emit after a skipped step)
-//   copy_f16_kernel        one window's piece of a Pos+g+p layer gather
-//                          (trishampatil "ZeRO-3": parameters gathered on
-//                          demand, used, released)
+//   copy_f16_kernel        a Pos+g+p layer gather: the layer's pieces of up
+//                          to 16 owners' windows in one launch (trishampatil
+//                          "ZeRO-3": parameters gathered on demand, used,
+//                          released)
 #include <hip/hip_runtime.h>
 
 #include <atomic>
