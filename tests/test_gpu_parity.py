@@ -228,3 +228,97 @@ def test_determinism_two_runs():
             ctl, p, m, v, bits = run.step(sl, 1024.0)
         results.append((ctl["sumsq"], p.tobytes(), m.tobytes(), v.tobytes(), bits.tobytes()))
     assert results[0] == results[1]
+
+
+def test_fused_step_nd400_small_window():
+    """Nd = 400 (the largest configuration's slice count) on a small ragged
+    window: 25 chunks of 16 slices per group."""
+    _run_case(4099, 400, steps=2, seed=400, L=2048.0, sigma=1e-4, dist="student_t3")
+
+
+def test_all_padding_window():
+    """A window that is all padding (zero parameters and zero gradients)
+    stays exactly +0 in every buffer, step after step."""
+    n, nd = 4104, 5
+    master0 = np.zeros(n, dtype=F32)
+    sh = oracle.OwnedShard(master0, **HP)
+    run = GpuShardRun(master0, nd, HP)
+    for step in range(1, 4):
+        sl = np.zeros((nd, n), dtype=F16)
+        ovf, sq = sh.step(sl, 1024.0)
+        ctl, p, m, v, bits = run.step(sl, 1024.0)
+        _compare_step(run, sh, ctl, p, m, v, bits, ovf, sq, step, f"padding step {step}")
+        for x in (p, m, v):
+            assert not np.any(x.view(np.uint32)), "padding must stay +0"
+        assert not np.any(run.window(bits))
+
+
+def test_constant_gradient_twenty_steps():
+    """The same gradient every step for 20 steps (the bias corrections run
+    through their whole range), three slices with different values."""
+    n, nd = 3000, 3
+
+    def const(step, sl):
+        out = np.empty_like(sl)
+        out[0], out[1], out[2] = 0.25 * 1024, -0.125 * 1024, 2.0**-10 * 1024
+        return out.astype(F16)
+
+    _run_case(n, nd, steps=20, seed=9, mutate=const)
+
+
+@pytest.mark.parametrize("L", [1000.0, 3.7, 65537.0])
+def test_non_power_of_two_loss_scale(L):
+    """g = s * (1/L) with an inexact reciprocal: the device and the oracle
+    take the same two roundings."""
+    _run_case(20011, 6, steps=3, seed=int(L) % 97, L=L, sigma=1e-3)
+
+
+@pytest.mark.parametrize("hp", [
+    dict(lr=0.0, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0),     # no movement
+    dict(lr=1e-2, beta1=0.0, beta2=0.0, eps=1e-8, weight_decay=0.0),      # m = g, v = g^2
+    dict(lr=1e-3, beta1=0.99, beta2=0.9999, eps=1.0, weight_decay=0.5),   # large eps, strong decay
+    dict(lr=0.1, beta1=0.5, beta2=0.5, eps=1e-12, weight_decay=1e-4),
+])
+def test_hyperparameter_extremes(hp):
+    _run_case(9001, 4, steps=4, seed=11, hp=hp)
+
+
+def test_state_canaries():
+    """Canary elements right after every state array (both ping-pong sets)
+    and the fp32 gradient buffer are never written by the fused, clipped or
+    bucketed paths on a ragged window."""
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    n, nd, pad = 4 * 65536 * 2 + 4003, 4, 64
+    canary = float.fromhex("0x1.5555p+100")
+    g = np.random.default_rng(13)
+    arrays = []
+    for k in range(7):  # p0 p1 m0 m1 v0 v1 grad
+        t = torch.full((n + pad,), canary, dtype=torch.float32, device="cuda")
+        if k < 6:
+            t[:n] = 0.0
+        arrays.append(t)
+    arrays[0][:n] = torch.from_numpy((g.standard_normal(n) * 0.02).astype(F32)).cuda()
+    ctl = torch.frombuffer(bytearray(B.ctl_init_bytes(1024.0)), dtype=torch.uint8).cuda()
+    st = B.adam_state(arrays[0:2], arrays[2:4], arrays[4:6], ctl)
+    ws = torch.zeros(B.workspace_bytes(), dtype=torch.uint8, device="cuda")
+    ag = torch.zeros(n + pad, dtype=torch.float16, device="cuda")
+    stride = (n + 7) // 8 * 8
+    sl = torch.zeros((nd, stride), dtype=torch.float16, device="cuda")
+    sl[:, :n] = torch.from_numpy(gen.host_grad_slices(13, 1, 0, nd, n, 0, n, 1e-3, 1024.0)).cuda()
+    src = B.grad_src(sl, stride, 0, n, nd, 1024.0)
+    B.adam_step(src, st, B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0), ag, 0, ws)
+    B.adam_step_clipped(src, st, B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0, max_grad_norm=1e-3), arrays[6], ag, 0, ws)
+    hp = B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    bucket = 65536 * 4
+    for i, o in enumerate(range(0, n, bucket)):
+        k = min(bucket, n - o)
+        phase = (B.BUCKET_FIRST if o == 0 else 0) | (B.BUCKET_LAST if o + k >= n else 0)
+        B.adam_step_bucket(B.grad_src(sl, stride, o, k, nd, 1024.0), st, hp, o, n, ag, 0, phase, ws)
+    torch.cuda.synchronize()
+    c = B.ctl_from_bytes(bytes(ctl.cpu().numpy().tobytes()))
+    assert c["t"] == 3 and c["skipped"] == 0
+    for k, t in enumerate(arrays):
+        tail = t[n:].cpu().numpy()
+        assert np.all(tail == np.float32(canary)), f"array {k} written past its end"
+    assert not torch.count_nonzero(ag[n:].view(torch.int16)).item()
