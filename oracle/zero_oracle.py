@@ -284,9 +284,12 @@ def clip_coefficient(sumsq: float, max_norm: float) -> float:
     return c if c < 1.0 else 1.0
 
 
-def clipped_gradient(s: np.ndarray, loss_scale: float, max_norm: float):
+def clipped_gradient(s: np.ndarray, loss_scale: float, max_norm: float, window_sumsq: float = None):
     """Two-pass gradient of the clipping path: returns (g, overflow, sumsq,
-    coef) with g the float64 gradient the update uses."""
+    coef) with g the float64 gradient the update uses.  The norm is the
+    whole window's: when `s` holds only a sample of the window's elements,
+    `window_sumsq` supplies the window's sum of g32^2 (computed elsewhere
+    from the same inputs)."""
     inv = 1.0 / float(loss_scale)
     overflow = bool(np.any(~np.isfinite(s)))
     with np.errstate(invalid="ignore", over="ignore"):
@@ -294,7 +297,7 @@ def clipped_gradient(s: np.ndarray, loss_scale: float, max_norm: float):
     if overflow:
         return None, True, float("nan"), float("nan")
     g64 = g32.astype(F64)
-    sumsq = math.fsum((g64 * g64).tolist())
+    sumsq = math.fsum((g64 * g64).tolist()) if window_sumsq is None else float(window_sumsq)
     coef = clip_coefficient(sumsq, max_norm)
     return g64 * coef, False, sumsq, coef
 
@@ -329,9 +332,10 @@ class OwnedShard:
     def window(self) -> np.ndarray:
         return emit(self.p.astype(F32))
 
-    def step(self, slices: np.ndarray, loss_scale: float = None):
+    def step(self, slices: np.ndarray, loss_scale: float = None, window_sumsq: float = None):
         """One step.  With dynamic scaling (scale_interval > 0) the slices
-        carry self.scale and `loss_scale` is ignored."""
+        carry self.scale and `loss_scale` is ignored.  `window_sumsq`: see
+        clipped_gradient (a shard that holds a sample of a window)."""
         dynamic = self.scale_interval > 0
         L = self.scale if dynamic else float(loss_scale)
         self.scales.append(L)
@@ -339,7 +343,7 @@ class OwnedShard:
         if s.shape[0] != self.p.shape[0]:
             raise ValueError("window size mismatch")
         if self.max_grad_norm > 0:
-            g, overflow, sq, coef = clipped_gradient(s, L, self.max_grad_norm)
+            g, overflow, sq, coef = clipped_gradient(s, L, self.max_grad_norm, window_sumsq)
         else:
             g, overflow, sq = unscale(s, L)
             coef = 1.0

@@ -54,6 +54,18 @@ def _sumsq_torch(torch, slices, L):
     return float(tot.item())
 
 
+def _sumsq32_torch(torch, slices, L):
+    """sum(fp32((sum_k slices[k, j]) * (1/L))^2) in float64 with torch: the
+    clipping norm's sum over fp32 gradients, in column chunks."""
+    chunk = max(1 << 16, (1 << 28) // slices.shape[0])
+    tot = torch.zeros((), dtype=torch.float64, device=slices.device)
+    inv = 1.0 / L
+    for c in range(0, slices.shape[1], chunk):
+        g = (slices[:, c:c + chunk].to(torch.float64).sum(0) * inv).to(torch.float32).to(torch.float64)
+        tot += (g * g).sum()
+    return float(tot.item())
+
+
 def test_c1_every_rank_full():
     """Flat Psi = 1,000,003, Nd = 4: every rank's window stepped 3 times into
     one padded flat fp16 buffer; padding (445 elements of rank 3) stays 0."""
@@ -139,34 +151,49 @@ def _sample_idx(S, n=1 << 16, extra=()):
     return idx[(idx >= 0) & (idx < S)]
 
 
-def _sampled_run(w, owner=0, inject=None):
+def _sampled_run(w, owner=0, inject=None, clip=0.0, bucket=0, steps=None):
+    """Steps the workload's window on the device (whole-window fused step,
+    clipped step with max_grad_norm = clip, or buckets of `bucket` elements
+    read in place) and the oracle on sampled elements.  With clipping the
+    oracle takes the window's norm from a float64 torch sum over the same
+    slices."""
     torch, B, plan, S, valid = _setup(w, owner)
     from zero_partitioned_mixed_buffer_amd import OwnedShard
     idx = _sample_idx(S)
     tidx = torch.from_numpy(idx).cuda()
     master = torch.empty(S, dtype=torch.float32, device="cuda")
     gen.device_fill_params(master, w.seed + owner, w.param_sigma, valid)
-    ref = oracle.OwnedShard(master[tidx].cpu().numpy(), **_hp(w))
-    sh = OwnedShard(master, **_hp(w))
+    hp = dict(_hp(w), max_grad_norm=clip)
+    ref = oracle.OwnedShard(master[tidx].cpu().numpy(), **hp)
+    sh = OwnedShard(master, **hp)
     del master
     ag = torch.zeros(S + 16, dtype=torch.float16, device="cuda")
     sh.emit(ag, 8)
     say(f"{w.key}: S={S} Nd={w.nd}, {idx.size} sampled elements")
     dsl = torch.empty((w.nd, S), dtype=torch.float16, device="cuda")
     flags = []
-    for step in range(1, w.steps + 1):
+    for step in range(1, (steps or w.steps) + 1):
         say(f"{w.key} step {step}: filling {2 * w.nd * S / 1e9:.1f} GB of slices")
         gen.device_fill_grads(dsl, w.seed, step, w.grad_sigma, w.loss_scale, w.dist, valid)
         if inject is not None and inject[0] == step:
             dsl[inject[1], inject[2]] = float("inf")
-        ovf, _ = ref.step(dsl[:, tidx].cpu().numpy(), w.loss_scale)
-        if ovf or (inject is not None and inject[0] == step):
+        injected = inject is not None and inject[0] == step
+        sq32 = _sumsq32_torch(torch, dsl, w.loss_scale) if (clip and not injected) else None
+        ovf, _ = ref.step(dsl[:, tidx].cpu().numpy(), w.loss_scale, window_sumsq=sq32)
+        if ovf or injected:
             prev = [x.clone() for x in sh.committed()]
             prev_ag = ag.clone()
         else:
-            sq_want = _sumsq_torch(torch, dsl, w.loss_scale)
-        say(f"{w.key} step {step}: fused step")
-        sh.step(dsl, w.loss_scale, allgather=ag, allgather_off=8)
+            sq_want = sq32 if clip else _sumsq_torch(torch, dsl, w.loss_scale)
+        if bucket:
+            say(f"{w.key} step {step}: {-(-S // bucket)} buckets of {bucket}")
+            for o in range(0, S, bucket):
+                k = min(bucket, S - o)
+                phase = (B.BUCKET_FIRST if o == 0 else 0) | (B.BUCKET_LAST if o + k >= S else 0)
+                sh.step_bucket(dsl, o, k, phase, w.loss_scale, elem_off=o, allgather=ag, allgather_off=8)
+        else:
+            say(f"{w.key} step {step}: {'clipped' if clip else 'fused'} step")
+            sh.step(dsl, w.loss_scale, allgather=ag, allgather_off=8)
         torch.cuda.synchronize()
         ctl = sh.control()
         flags.append(ctl["overflow"])
@@ -179,6 +206,8 @@ def _sampled_run(w, owner=0, inject=None):
             del prev, prev_ag
         else:
             assert ctl["sumsq"] == pytest.approx(sq_want, rel=1e-12)
+            if clip:
+                assert ctl["clip_coef"] == pytest.approx(ref.coefs[-1], rel=1e-12)
         p, m, v = (x[tidx].cpu().numpy() for x in sh.committed(ctl))
         for got, want, nm in ((p, ref.p, "p"), (m, ref.m, "m"), (v, ref.v, "v")):
             assert_state_close(got, want, f"{w.key} step {step} {nm}")
@@ -220,3 +249,63 @@ def test_c5_60b_nd400_overflow_skip_sampled():
     assert S == 150000128
     flags, ref = _sampled_run(w, inject=(2, 17, S // 2))
     assert flags == [0, 1, 0, 0] and ref.t == 3
+
+
+def test_c2_clipped_full():
+    """The GPT-2-small shard, clipped step (max_grad_norm 1.0, active: the
+    window's norm is about 11), 3 steps, element by element against the
+    oracle on the whole window."""
+    w = configs.C2
+    owner = 3
+    torch, B, plan, S, valid = _setup(w, owner)
+    from zero_partitioned_mixed_buffer_amd import OwnedShard
+    master = torch.empty(S, dtype=torch.float32, device="cuda")
+    gen.device_fill_params(master, w.seed + owner, w.param_sigma, valid)
+    hp = dict(_hp(w), max_grad_norm=1.0)
+    ref = oracle.OwnedShard(master.cpu().numpy(), **hp)
+    sh = OwnedShard(master, **hp)
+    ag = torch.zeros(S, dtype=torch.float16, device="cuda")
+    dsl = torch.empty((w.nd, S), dtype=torch.float16, device="cuda")
+    for step in range(1, 4):
+        say(f"c2 clipped step {step}")
+        gen.device_fill_grads(dsl, w.seed, step, w.grad_sigma, w.loss_scale, w.dist, valid)
+        ovf, sq = ref.step(dsl.cpu().numpy(), w.loss_scale)
+        sh.step(dsl, w.loss_scale, allgather=ag)
+        torch.cuda.synchronize()
+        ctl = sh.control()
+        assert ctl["overflow"] == int(ovf) == 0 and ctl["t"] == ref.t == step
+        assert ctl["sumsq"] == pytest.approx(sq, rel=1e-12)
+        assert ctl["clip_coef"] == pytest.approx(ref.coefs[-1], rel=1e-12) and ref.coefs[-1] < 0.2
+        p, m, v = (x.cpu().numpy() for x in sh.committed(ctl))
+        for got, want, nm in ((p, ref.p, "p"), (m, ref.m, "m"), (v, ref.v, "v")):
+            assert_state_close(got, want, f"c2 clipped step {step} {nm}")
+    bits = ag.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert_fp16_close(bits, ref.window().view(np.uint16), "c2 clipped window")
+
+
+def test_c3_bucketed_sampled():
+    """GPT-2-XL shaped list, Nd = 16, AdamW: 3 steps ingested in 6 buckets of
+    2^24 elements (the benchmark's bucketed configuration), sampled."""
+    flags, ref = _sampled_run(configs.C3, bucket=1 << 24, steps=3)
+    assert flags == [0] * 3 and ref.t == 3
+
+
+def test_c3_clipped_sampled():
+    """GPT-2-XL shaped list, clipped step (max_grad_norm 1.0), 3 steps."""
+    flags, ref = _sampled_run(configs.C3, clip=1.0, steps=3)
+    assert flags == [0] * 3 and max(ref.coefs) < 1.0
+
+
+def test_c5_clipped_overflow_sampled():
+    """Nd = 400 Student-t(3) slices, clipped step (max_grad_norm 1.0), +inf
+    at step 2: flags [0, 1, 0], the clip coefficient from the window's norm."""
+    w = configs.C5
+    torch = torch_mod()
+    free, _ = torch.cuda.mem_get_info()
+    if free < 140e9:
+        pytest.skip(f"needs ~130 GB of free device memory ({free / 1e9:.0f} GB free)")
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    S = B.plan_partitions(list(w.numels), w.nd, 256)[0]["part"]
+    flags, ref = _sampled_run(w, inject=(2, 17, S // 2), clip=1.0, steps=3)
+    assert flags == [0, 1, 0] and ref.t == 2
+    assert all(c < 1.0 for c in ref.coefs if c == c)

@@ -608,3 +608,26 @@ def test_planted_gather_mistakes_are_caught(kind):
         return np.concatenate(pieces) if pieces else np.empty(0, F16)
 
     assert not _gather_round_trips(bad_gather)
+
+
+def test_clipped_sample_with_window_norm_matches_full_window():
+    """A shard holding a sample of a window's elements, given the window's
+    sum of g32^2, takes exactly the steps the full window takes at those
+    elements (the clip norm is the whole window's)."""
+    g = np.random.default_rng(51)
+    n, nd = 5000, 4
+    master = (g.standard_normal(n) * 0.02).astype(F32)
+    idx = np.sort(g.choice(n, 300, replace=False))
+    full = oracle.OwnedShard(master, max_grad_norm=0.05, weight_decay=0.01)
+    part = oracle.OwnedShard(master[idx], max_grad_norm=0.05, weight_decay=0.01)
+    for step in range(4):
+        sl = (g.standard_normal((nd, n)) * 1e-3 * 1024).astype(F16)
+        full.step(sl, 1024.0)
+        part.step(sl[:, idx], 1024.0, window_sumsq=full.sumsq[-1])
+        assert part.coefs[-1] == full.coefs[-1] < 1.0
+        for a, b in ((part.p, full.p[idx]), (part.m, full.m[idx]), (part.v, full.v[idx])):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # without the window's norm the sample clips differently
+    alone = oracle.OwnedShard(master[idx], max_grad_norm=0.05)
+    alone.step(sl[:, idx], 1024.0)
+    assert alone.coefs[-1] != full.coefs[-1]
