@@ -166,8 +166,9 @@ int64_t zero_workspace_bytes(void);
  * deterministic order).  Pos+g: "each gradient is reduced only on the
  * process that owns the partition" (upskillscore "How it works").
  *   grad_out: device float[n], 16-byte aligned, receives fp32(g); may be NULL.
- *   overflow: device int32, required.  sumsq: device double, required.
- *   workspace: see above.
+ *   overflow: device int32 (4-byte aligned), required.  sumsq: device double
+ *   (8-byte aligned), required.  workspace: see above.  No output may
+ *   overlap the slices, another output or the workspace.
  * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EALIAS, ZERO_EHIP.
  */
 int zero_reduce_owned(const zero_grad_src* src, float* grad_out, int32_t* overflow,
@@ -244,7 +245,8 @@ typedef struct zero_adam_hp {
  * ZeRO-3": reduce-scatter, update the shard, all-gather).
  *   src: gradient source, src->n = window length.
  *   st:  ping-pong state; neither set may overlap the other, the slices or
- *        the all-gather window.
+ *        the all-gather window.  st->ctl is 8-byte aligned, and neither it
+ *        nor the workspace may overlap any of these.
  *   allgather: device uint16 buffer; the window [allgather_off,
  *        allgather_off + n) is written (16-byte aligned start).  NULL skips
  *        the emit.

@@ -194,6 +194,13 @@ def test_step_validation(L):
     assert step(state=_state(base=A)) == B.ZERO_EALIAS
     # misaligned all-gather window
     assert step(ag=1 << 29, off=3) == B.ZERO_EALIGN
+    # control block: 8-byte aligned, outside every data array
+    assert step(state=_state(ctl=(1 << 30) + 4)) == B.ZERO_EALIGN
+    assert step(state=_state(ctl=(1 << 24) + 64)) == B.ZERO_EALIAS     # inside master[0]
+    assert step(state=_state(ctl=A + 8)) == B.ZERO_EALIAS              # inside the slices
+    # workspace outside every data array and the control block
+    assert step(ws=A) == B.ZERO_EALIAS
+    assert step(ws=(1 << 30) - 256) == B.ZERO_EALIAS                   # covers the control block
 
 
 @no_gpu
@@ -270,6 +277,11 @@ def test_other_validation(L):
     assert L.zero_reduce_owned(C.byref(src), None, None, 1 << 26, 1 << 28, None) == B.ZERO_EINVAL
     assert L.zero_reduce_owned(C.byref(src), A + 8, 1 << 25, 1 << 26, 1 << 28, None) == B.ZERO_EALIGN
     assert L.zero_reduce_owned(C.byref(src), A + 16, 1 << 25, 1 << 26, 1 << 28, None) == B.ZERO_EALIAS
+    assert L.zero_reduce_owned(C.byref(src), None, (1 << 25) + 2, 1 << 26, 1 << 28, None) == B.ZERO_EALIGN
+    assert L.zero_reduce_owned(C.byref(src), None, 1 << 25, (1 << 26) + 4, 1 << 28, None) == B.ZERO_EALIGN
+    assert L.zero_reduce_owned(C.byref(src), None, A + 8, 1 << 26, 1 << 28, None) == B.ZERO_EALIAS
+    assert L.zero_reduce_owned(C.byref(src), 1 << 24, (1 << 24) + 64, 1 << 26, 1 << 28, None) == B.ZERO_EALIAS
+    assert L.zero_reduce_owned(C.byref(src), None, 1 << 25, (1 << 28) + 1024, 1 << 28, None) == B.ZERO_EALIAS
     assert L.zero_emit_fp16(None, 8, 1 << 29, 0, None) == B.ZERO_EINVAL
     assert L.zero_emit_fp16(1 << 24, -1, 1 << 29, 0, None) == B.ZERO_EINVAL
     assert L.zero_emit_fp16(1 << 24, 8, 1 << 29, 1, None) == B.ZERO_EALIGN

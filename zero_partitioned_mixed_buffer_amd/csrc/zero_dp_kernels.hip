@@ -1171,7 +1171,7 @@ int check_step(const zero_grad_src* src, const zero_adam_state* st, const zero_a
     if (zdp::mul_overflows(n, 4, &b4)) return ZERO_EOVERFLOW;
     float* arrs[7] = {st->master[0],     st->master[1],     st->exp_avg[0], st->exp_avg[1],
                       st->exp_avg_sq[0], st->exp_avg_sq[1], grad_buf};
-    Range r[9];
+    Range r[11];
     int nr = 0;
     for (int i = 0; i < 7; ++i) {
         if (i == 6 && grad_buf == nullptr) continue;
@@ -1190,6 +1190,10 @@ int check_step(const zero_grad_src* src, const zero_adam_state* st, const zero_a
         r[nr++] = bytes_of(ag, n, 2);
     }
     r[nr++] = span;
+    // the control block and the workspace must not overlap any data either
+    if ((reinterpret_cast<uintptr_t>(st->ctl) & 7u) != 0) return ZERO_EALIGN;
+    r[nr++] = bytes_of(st->ctl, 1, static_cast<int64_t>(sizeof(zero_step_ctl)));
+    r[nr++] = bytes_of(workspace, 1, zdp::kWsBytes);
     for (int i = 0; i < nr; ++i)
         for (int k = i + 1; k < nr; ++k)
             if (overlap(r[i], r[k])) return ZERO_EALIAS;
@@ -1230,13 +1234,24 @@ int zero_reduce_owned(const zero_grad_src* src, float* grad_out, int32_t* overfl
     int rc = check_src(src, &span);
     if (rc != ZERO_OK) return rc;
     if (overflow == nullptr || sumsq == nullptr || workspace == nullptr) return ZERO_EINVAL;
-    if (!aligned16(workspace)) return ZERO_EALIGN;
+    if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(overflow) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(sumsq) & 7u) != 0)
+        return ZERO_EALIGN;
+    Range r[5];
+    int nr = 0;
+    r[nr++] = span;
+    r[nr++] = bytes_of(overflow, 1, 4);
+    r[nr++] = bytes_of(sumsq, 1, 8);
+    r[nr++] = bytes_of(workspace, 1, zdp::kWsBytes);
     if (grad_out != nullptr) {
         if (!aligned16(grad_out)) return ZERO_EALIGN;
         int64_t b = 0;
         if (zdp::mul_overflows(src->n, 4, &b)) return ZERO_EOVERFLOW;
-        if (overlap(bytes_of(grad_out, src->n, 4), span)) return ZERO_EALIAS;
+        r[nr++] = bytes_of(grad_out, src->n, 4);
     }
+    for (int i = 0; i < nr; ++i)
+        for (int k = i + 1; k < nr; ++k)
+            if (overlap(r[i], r[k])) return ZERO_EALIAS;
     const int grid = grid_for(kReduce, src->n);
     (void)hipGetLastError();
     reduce_owned_kernel<false><<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
