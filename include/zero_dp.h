@@ -320,7 +320,8 @@ int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st,
 /* Re-emits allgather[off + j] = fp16_RNE(master[ctl->cur][j]) for j < n when
  * ctl->overflow != 0 (the step was skipped), and does nothing otherwise; the
  * decision is taken on the device, so no host synchronisation is needed.
- * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EHIP. */
+ * The window must not overlap either master or the control block.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EALIAS, ZERO_EHIP. */
 int zero_restore_skipped(const zero_adam_state* st, int64_t n, uint16_t* allgather,
                          int64_t allgather_off, void* stream);
 

@@ -291,3 +291,6 @@ def test_other_validation(L):
     assert L.zero_restore_skipped(C.byref(st), -1, 1 << 29, 0, None) == B.ZERO_EINVAL
     assert L.zero_restore_skipped(C.byref(st), 8, None, 0, None) == B.ZERO_EINVAL
     assert L.zero_restore_skipped(C.byref(st), 8, 1 << 29, 1, None) == B.ZERO_EALIGN
+    assert L.zero_restore_skipped(C.byref(_state(ctl=(1 << 30) + 4)), 8, 1 << 29, 0, None) == B.ZERO_EALIGN
+    assert L.zero_restore_skipped(C.byref(st), 64, 1 << 24, 0, None) == B.ZERO_EALIAS   # window on master[0]
+    assert L.zero_restore_skipped(C.byref(st), 64, (1 << 30) - 64, 0, None) == B.ZERO_EALIAS  # covers the ctl

@@ -1392,7 +1392,13 @@ int zero_restore_skipped(const zero_adam_state* st, int64_t n, uint16_t* allgath
         return ZERO_EOVERFLOW;
     if (n == 0) return ZERO_OK;  // nothing to restore
     uint16_t* ag = allgather + allgather_off;
-    if (!aligned16(ag) || !aligned16(st->master[0]) || !aligned16(st->master[1])) return ZERO_EALIGN;
+    if (!aligned16(ag) || !aligned16(st->master[0]) || !aligned16(st->master[1]) ||
+        (reinterpret_cast<uintptr_t>(st->ctl) & 7u) != 0)
+        return ZERO_EALIGN;
+    const Range w = bytes_of(ag, n, 2);
+    if (overlap(w, bytes_of(st->master[0], n, 4)) || overlap(w, bytes_of(st->master[1], n, 4)) ||
+        overlap(w, bytes_of(st->ctl, 1, static_cast<int64_t>(sizeof(zero_step_ctl)))))
+        return ZERO_EALIAS;
     const int grid = grid_for(kRestore, n);
     (void)hipGetLastError();
     restore_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
