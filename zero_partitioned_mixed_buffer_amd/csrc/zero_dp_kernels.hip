@@ -263,20 +263,28 @@ struct Partials {
 // the workgroup that finishes last; that workgroup then holds the totals
 // (fixed summation order: lane i sums partials i, i+256, ..., then the
 // deterministic workgroup tree) in thread 0.
+//
+// Ordering: the ticket increment is an agent-scope acquire-release
+// operation, which publishes this workgroup's partial (the release writes
+// back the XCD's L2) and, in the last workgroup, acquires everyone else's;
+// the last workgroup's other threads then take an agent-scope acquire fence
+// (a cache invalidate, no write-back) before reading the partials.  Each
+// agent-scope release costs an L2 write-back, so there is exactly one per
+// workgroup: a full fence before the increment and another after it
+// doubled the end-of-kernel cost (about 7 us per launch).
 __device__ __forceinline__ bool last_block_totals(const Partials& ws, double& sq, int& flag) {
     __shared__ int s_last;
     block_reduce(sq, flag);
     if (threadIdx.x == 0) {
         ws.sq[blockIdx.x] = sq;
         ws.flag[blockIdx.x] = flag;
-        __threadfence();
         const uint32_t prev =
             __hip_atomic_fetch_add(ws.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == gridDim.x - 1);
     }
     __syncthreads();
     if (!s_last) return false;
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     double t = 0.0;
     int f = 0;
     for (uint32_t i = threadIdx.x; i < gridDim.x; i += kBlock) {
