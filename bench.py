@@ -3,16 +3,17 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
 
-A step is one pass of the whole hot path over one batch of gradients: the
-fused reduce + unscale/flag/sum-of-squares + Adam + commit + fp16 emit
-kernel (zero_adam_step) followed by the conditional all-gather restore
-(zero_restore_skipped).  Inputs are resident in HBM before timing starts.
-Prints one JSON line with the whole-step throughput (owned elements per
-second, K steps back to back between device synchronisations), the fused
-kernel's achieved HBM bandwidth against the 8 TB/s peak (algorithmic bytes
-(2*Nd + 26) per owned element over the kernel's average duration, from HIP
-events around K back-to-back launches on the launch stream), and the
-oracle's rate on a bounded sample of the same workload on the host cores.
+A step is one pass of the whole hot path over one batch of gradients:
+zero_adam_step, i.e. the fused reduce + unscale/flag/sum-of-squares + Adam +
+fp16 emit kernel and the small commit kernel after it (which also re-emits
+the all-gather window of a skipped step).  Inputs are resident in HBM
+before timing starts.  Prints one JSON line with the whole-step throughput
+(owned elements per second, K steps back to back between device
+synchronisations), the step's achieved HBM bandwidth against the 8 TB/s
+peak (algorithmic bytes (2*Nd + 26) per owned element over the average
+device time of the step's two kernels, from HIP events around K
+back-to-back steps on the launch stream), and the oracle's rate on a
+bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -305,7 +306,7 @@ def main():
             + ("; arrival copies into 2 constant-size receive buffers on a side stream" if args.arrival else
                "; buckets read in place"))
 
-    def launch_bucketed(i, restore=True):
+    def launch_bucketed(i):
         sh = shards[i % n_shards]
         gs = gsets[i % rot]
         for b, (o, k) in enumerate(buckets):
@@ -324,21 +325,19 @@ def main():
                                stream)
             if args.arrival:
                 consumed[r].record(stream)
-        if restore:
-            B.restore_skipped(sh.state, S, ag, ag_offs[i % n_shards], stream)
 
-    def launch(i, restore=True):
+    def launch(i):
         sh = shards[i % n_shards]
         if bucketed:
-            launch_bucketed(i, restore)
+            launch_bucketed(i)
             return
         if clipped:  # two passes; a skipped step leaves the window untouched
             B.adam_step_clipped(srcs[i % rot], sh.state, sh.hp, sh.grad_buf, ag, ag_offs[i % n_shards],
                                 sh.workspace, stream)
             return
+        # the fused kernel and the commit kernel (which also re-emits the
+        # window of a skipped step)
         B.adam_step(srcs[i % rot], sh.state, sh.hp, ag, ag_offs[i % n_shards], sh.workspace, stream)
-        if restore:
-            B.restore_skipped(sh.state, S, ag, ag_offs[i % n_shards], stream)
 
     for i in range(args.warmup):
         launch(i)
@@ -351,13 +350,13 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # Fused kernel alone: K launches back to back between two HIP events on
-    # the launch stream (per-launch event records would add a cache release
-    # and a dispatch gap to every launch).
+    # Device time of the step's kernels: K steps back to back between two
+    # HIP events on the launch stream (per-launch event records would add a
+    # cache release and a dispatch gap to every launch).
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
-        launch(args.warmup + args.steps + i, restore=False)
+        launch(args.warmup + args.steps + i)
     e1.record(stream)
     torch.cuda.synchronize()
     kern_avg = e0.elapsed_time(e1) / args.steps
@@ -368,13 +367,11 @@ def main():
            for _ in range(args.steps)]
     for i in range(args.steps):
         evs[i][0].record(stream)
-        launch(args.warmup + 2 * args.steps + i, restore=False)
+        launch(args.warmup + 2 * args.steps + i)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
     pct = lambda q: per[min(len(per) - 1, int(round(q * (len(per) - 1))))]
-    for r in range(n_shards):
-        B.restore_skipped(shards[r].state, S, ag, ag_offs[r], stream)
     ctls = [sh.control() for sh in shards]
     if sum(c["t"] for c in ctls) != args.warmup + 3 * args.steps or any(c["skipped"] for c in ctls):
         log(f"unexpected control state after timing: {ctls}")
@@ -390,7 +387,8 @@ def main():
     # (2*Nd + 4) for the reduce pass + 30 for the update pass
     bytes_elem = 2 * w.nd + (34 if clipped else 26)
     achieved = bytes_elem * S / (kern_avg * 1e-3) / 1e9
-    what = f"bucketed step ({len(buckets)} launches)" if bucketed else "fused kernel"
+    what = (f"bucketed step ({len(buckets)} launches + commit)" if bucketed else
+            "clipped step (2 kernels)" if clipped else "fused step (fused + commit kernels)")
     log(f"{what}: avg {kern_avg * 1e3:.1f} us over {args.steps} back-to-back launches; "
         f"step {ms_step * 1e3:.1f} us; {achieved:.0f} GB/s")
 
@@ -440,7 +438,8 @@ def main():
             "traffic_bytes_per_launch": traffic,
             "algorithmic_bytes_per_launch": bytes_elem * S,
             "kernel": ("reduce_owned_kernel + clipped_update_kernel" if clipped else
-                       f"fused_step_kernel x {len(buckets)} buckets" if bucketed else "fused_step_kernel"),
+                       f"fused_step_kernel x {len(buckets)} buckets + commit_kernel" if bucketed else
+                       "fused_step_kernel + commit_kernel"),
             "kernel_avg_us": kern_avg * 1e3,
             "kernel_us_p10_p50_p90_per_launch_events": [pct(0.1), pct(0.5), pct(0.9)],
             "attainable": attain,

@@ -15,16 +15,11 @@ constexpr int kWaves = kBlock / 64;
 // Upper bound on workgroups of the reducing kernels (one partial each).
 constexpr int kMaxBlocks = 8192;
 
-// Workspace layout (bytes): completion counter, the totals the clipped
-// path passes from its first to its second kernel, the running totals of a
-// bucketed step (sum g^2, flag, elements covered), then per-workgroup
-// partial sums of g^2 (double) and overflow flags (int32).
+// Workspace layout (bytes): completion counter, the elements a bucketed
+// step's buckets have covered, then one slot per workgroup of partial sums
+// of g^2 (double) and overflow flags (int32).
 constexpr int64_t kWsTicket = 0;
-constexpr int64_t kWsTotSq = 64;
-constexpr int64_t kWsTotFlag = 72;
-constexpr int64_t kWsRunSq = 128;
-constexpr int64_t kWsRunFlag = 136;
-constexpr int64_t kWsRunCount = 144;
+constexpr int64_t kWsRunCount = 64;
 constexpr int64_t kWsPartSq = 256;
 constexpr int64_t kWsPartFlag = kWsPartSq + 8 * kMaxBlocks;
 constexpr int64_t kWsBytes = kWsPartFlag + 4 * kMaxBlocks;

@@ -300,6 +300,59 @@ __device__ __forceinline__ bool last_block_totals(const Partials& ws, double& sq
     return true;
 }
 
+// Publishes this workgroup's partial in its own slot with plain stores (no
+// ticket, no fence): the kernel boundary makes the slots visible to the
+// next launch on the stream.  `accumulate` adds to the slot instead (a
+// bucket after the first of a step, which must run on the same grid).
+__device__ __forceinline__ void publish_partial(const Partials& ws, double sq, int flag, bool accumulate) {
+    block_reduce(sq, flag);
+    if (threadIdx.x == 0) {
+        if (accumulate) {
+            sq = ws.sq[blockIdx.x] + sq;
+            flag |= ws.flag[blockIdx.x];
+        }
+        ws.sq[blockIdx.x] = sq;
+        ws.flag[blockIdx.x] = flag;
+    }
+}
+
+// Sum of the `nparts` published partials in the fixed order of
+// last_block_totals (lane i sums slots i, i+256, ..., then the workgroup
+// tree), in every thread of the workgroup: every workgroup of a launch
+// computes the same bits.
+__device__ __forceinline__ void sum_partials(const Partials& ws, int nparts, double& sq, int& flag) {
+    __shared__ double s_sq;
+    __shared__ int s_flag;
+    double t = 0.0;
+    int f = 0;
+    for (int i = threadIdx.x; i < nparts; i += kBlock) {
+        t += ws.sq[i];
+        f |= ws.flag[i];
+    }
+    block_reduce(t, f);
+    if (threadIdx.x == 0) {
+        s_sq = t;
+        s_flag = f;
+    }
+    __syncthreads();
+    sq = s_sq;
+    flag = s_flag;
+}
+
+// True in every thread of the workgroup that finishes last (a ticket with
+// no partials: the caller only needs to know that every workgroup is done).
+__device__ __forceinline__ bool last_block_done(uint32_t* ticket) {
+    __shared__ int s_last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == gridDim.x - 1);
+        if (s_last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return s_last != 0;
+}
+
 // ---------------------------------------------------------------- kernels
 struct SrcArgs {
     const uint16_t* win;       // base + elem_off: slice 0 of the window
@@ -484,7 +537,10 @@ __global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src_in, fl
             reduce_tail<kNormOfStored>(j, src, grad_out, sq, bad);
         }
     }
-    if (last_block_totals(ws, sq, bad) && threadIdx.x == 0) {
+    if constexpr (kNormOfStored) {
+        // the clipped step's first pass: its second pass sums the partials
+        publish_partial(ws, sq, bad, false);
+    } else if (last_block_totals(ws, sq, bad) && threadIdx.x == 0) {
         *overflow = bad;
         *sumsq = sq;
     }
@@ -504,12 +560,11 @@ struct AdamArgs {
     uint16_t* ag;  // all-gather window start, or null
     double growth, backoff;  // dynamic loss scaling factors
     int32_t interval;        // > 0: dynamic loss scaling
-    // bucketed step: this launch covers one bucket of the window; running
-    // totals live in the workspace across the step's launches
+    // bucketed step: this launch covers one bucket of the window; the
+    // per-workgroup partials accumulate in their slots across the step's
+    // launches and the elements covered in run_count
     int32_t bucket;          // 0: whole-window step; else ZERO_BUCKET_FIRST/LAST bits | 4
     int64_t window_n;        // elements the step's buckets must cover
-    double* run_sq;
-    int32_t* run_flag;
     int64_t* run_count;
 };
 
@@ -562,31 +617,6 @@ __device__ __forceinline__ void commit_step(const AdamArgs& a, int cur, double b
             w->good_steps = g;
         }
     }
-}
-
-// End of a fused launch, in the one lane of the last workgroup: commit the
-// whole-window step, or fold this bucket's totals into the running ones
-// (in stream order, so the sum is deterministic) and commit after the last.
-__device__ __forceinline__ void finish_fused(const AdamArgs& a, int cur, double b1t, double b2t, int bad,
-                                             double sq, int64_t n) {
-    if (a.bucket == 0) {
-        commit_step(a, cur, b1t, b2t, bad, sq, 1.0);
-        return;
-    }
-    const bool first = (a.bucket & ZERO_BUCKET_FIRST) != 0;
-    double rs = first ? 0.0 : *a.run_sq;
-    int rf = first ? 0 : *a.run_flag;
-    int64_t rc = first ? 0 : *a.run_count;
-    rs += sq;
-    rf |= bad;
-    rc += n;
-    if ((a.bucket & ZERO_BUCKET_LAST) == 0) {
-        *a.run_sq = rs;
-        *a.run_flag = rf;
-        *a.run_count = rc;
-        return;
-    }
-    commit_step(a, cur, b1t, b2t, rc != a.window_n ? 2 : rf, rs, 1.0);
 }
 
 __device__ __forceinline__ void adam1(const AdamScalars& c, double g, float p, float m, float v,
@@ -836,8 +866,12 @@ __global__ void __launch_bounds__(kBlock) fused_step_kernel(SrcArgs src_in, Adam
             }
         }
     }
-    if (last_block_totals(ws, sq, bad) && threadIdx.x == 0) finish_fused(a, cur, b1t, b2t, bad, sq, src.n);
+    // partials for commit_kernel (a bucket after the first adds to its slot)
+    const bool more = a.bucket != 0 && (a.bucket & ZERO_BUCKET_FIRST) == 0;
+    publish_partial(ws, sq, bad, more);
+    if (a.bucket != 0 && blockIdx.x == 0 && threadIdx.x == 0) *a.run_count = (more ? *a.run_count : 0) + src.n;
 }
+
 
 // Second pass of the clipped step, per element group: g = g32 * coef from
 // the materialised fp32 gradient, then the fused step's update and emit.
@@ -902,13 +936,14 @@ __device__ void cu_run(int64_t gi, int64_t end, int64_t step, const float* grad,
 // step whose first pass found an inf/NaN touches nothing but the control
 // block (so its all-gather window needs no restore).
 __global__ void __launch_bounds__(kBlock) clipped_update_kernel(
-    const float* __restrict__ grad, int64_t n, AdamArgs a, double max_norm, const double* tot_sq,
-    const int32_t* tot_flag, Partials ws) {
-    if (*tot_flag != 0) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) commit_step(a, a.ctl->cur, 0.0, 0.0, 1, *tot_sq, 1.0);
+    const float* __restrict__ grad, int64_t n, AdamArgs a, double max_norm, Partials ws, int32_t nparts) {
+    double sq_in;
+    int flag;
+    sum_partials(ws, nparts, sq_in, flag);  // the first pass's, identical in every workgroup
+    if (flag != 0) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) commit_step(a, a.ctl->cur, 0.0, 0.0, 1, sq_in, 1.0);
         return;
     }
-    const double sq_in = *tot_sq;
     const double r = max_norm / (__builtin_sqrt(sq_in) + 1e-6);
     const double coef = r < 1.0 ? r : 1.0;
     const int cur = a.ctl->cur;
@@ -933,9 +968,9 @@ __global__ void __launch_bounds__(kBlock) clipped_update_kernel(
             }
         }
     }
-    double unused = 0.0;
-    int none = 0;
-    if (last_block_totals(ws, unused, none) && threadIdx.x == 0) commit_step(a, cur, b1t, b2t, 0, sq_in, coef);
+    // commit once every workgroup has read ctl->cur (a ticket only: the
+    // partial slots still hold the first pass's sums that others may read)
+    if (last_block_done(ws.ticket) && threadIdx.x == 0) commit_step(a, cur, b1t, b2t, 0, sq_in, coef);
 }
 
 __device__ __forceinline__ void emit_range(const float* __restrict__ src, uint16_t* __restrict__ ag,
@@ -969,6 +1004,25 @@ __global__ void __launch_bounds__(kBlock) restore_kernel(const float* p0, const 
                                                          int64_t n) {
     if (ctl->overflow == 0) return;
     emit_range(ctl->cur ? p1 : p0, ag, n);
+}
+
+// The commit of a fused (or bucketed) step, one launch after it: every
+// workgroup sums the step's partials in the same fixed order, workgroup 0
+// commits the step in the control block (or records the skip and backs
+// off the loss scale), and on a skip every workgroup re-emits its share of
+// the all-gather window from the committed master.  A skip never changes
+// ctl->cur, so the workgroups that read it race with no write.
+__global__ void __launch_bounds__(kBlock) commit_kernel(AdamArgs a, Partials ws, int32_t nparts, int64_t n) {
+    double sq;
+    int flag;
+    sum_partials(ws, nparts, sq, flag);
+    if (a.bucket != 0 && *a.run_count != a.window_n) flag = 2;  // the buckets missed part of the window
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        double b1t, b2t;
+        (void)step_scalars(a, b1t, b2t);
+        commit_step(a, a.ctl->cur, b1t, b2t, flag, sq, 1.0);
+    }
+    if (flag != 0 && a.ag != nullptr) emit_range(a.p[a.ctl->cur], a.ag, n);
 }
 
 // ------------------------------------------------- Pos+g+p parameter gather
@@ -1034,7 +1088,7 @@ __global__ void __launch_bounds__(kBlock) copy_f16_kernel(CopyPieces t, uint16_t
 
 // ---------------------------------------------------------------- host glue
 constexpr int kMaxDevices = 64;
-enum KernelId { kReduce = 0, kFused = 1, kEmit = 2, kRestore = 3, kClip = 4, kCopy = 5, kKernels = 6 };
+enum KernelId { kReduce = 0, kFused = 1, kEmit = 2, kRestore = 3, kClip = 4, kCopy = 5, kCommit = 6, kKernels = 7 };
 std::atomic<int> g_grid_cache[kKernels][kMaxDevices];  // 0 = not computed yet
 
 // Workgroups that keep every CU of the current device busy at the kernel's
@@ -1053,6 +1107,7 @@ int resident_blocks(KernelId id) {
         case kRestore: fn = reinterpret_cast<const void*>(restore_kernel); break;
         case kClip: fn = reinterpret_cast<const void*>(clipped_update_kernel); break;
         case kCopy: fn = reinterpret_cast<const void*>(copy_f16_kernel); break;
+        case kCommit: fn = reinterpret_cast<const void*>(commit_kernel); break;
         default: return 1024;
     }
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -1065,6 +1120,7 @@ int resident_blocks(KernelId id) {
                     : id == kReduce ? ZDP_BPC_REDUCE
                     : id == kClip   ? ZDP_BPC_CLIP
                     : id == kCopy   ? ZDP_BPC_COPY
+                    : id == kCommit ? 1
                                     : 0;
     if (cap > 0 && per_cu > cap) per_cu = cap;
     int blocks = cus * per_cu;
@@ -1222,10 +1278,7 @@ int check_step(const zero_grad_src* src, const zero_adam_state* st, const zero_a
     a->interval = hp->scale_interval;
     a->bucket = 0;
     a->window_n = n;
-    char* w = static_cast<char*>(workspace);
-    a->run_sq = reinterpret_cast<double*>(w + zdp::kWsRunSq);
-    a->run_flag = reinterpret_cast<int32_t*>(w + zdp::kWsRunFlag);
-    a->run_count = reinterpret_cast<int64_t*>(w + zdp::kWsRunCount);
+    a->run_count = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + zdp::kWsRunCount);
     *ag_out = ag;
     return ZERO_OK;
 }
@@ -1275,9 +1328,13 @@ int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st, const ze
     if (rc != ZERO_OK) return rc;
     if (hp->max_grad_norm != 0.0) return ZERO_EINVAL;  // clipping needs the two-pass entry point
     const int grid = grid_for(kFused, src->n);
+    const Partials ws = make_ws(workspace);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    fused_step_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
-        make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), a, make_ws(workspace));
+    fused_step_kernel<<<grid, kBlock, 0, s>>>(make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), a, ws);
+    const int rc2 = finish_launch();
+    if (rc2 != ZERO_OK) return rc2;
+    commit_kernel<<<grid_for(kCommit, src->n), kBlock, 0, s>>>(a, ws, grid, src->n);
     return finish_launch();
 }
 
@@ -1292,17 +1349,14 @@ int zero_adam_step_clipped(const zero_grad_src* src, const zero_adam_state* st, 
     if (!(hp->max_grad_norm > 0.0) || !__builtin_isfinite(hp->max_grad_norm)) return ZERO_EINVAL;
     const int64_t n = src->n;
     const Partials ws = make_ws(workspace);
-    char* w = static_cast<char*>(workspace);
-    int32_t* tot_flag = reinterpret_cast<int32_t*>(w + zdp::kWsTotFlag);
-    double* tot_sq = reinterpret_cast<double*>(w + zdp::kWsTotSq);
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int grid1 = grid_for(kReduce, n);
     (void)hipGetLastError();
-    reduce_owned_kernel<true><<<grid_for(kReduce, n), kBlock, 0, s>>>(
-        make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), grad_buf, tot_flag, tot_sq, ws);
+    reduce_owned_kernel<true><<<grid1, kBlock, 0, s>>>(make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr),
+                                                        grad_buf, nullptr, nullptr, ws);
     int rc2 = finish_launch();
     if (rc2 != ZERO_OK) return rc2;
-    clipped_update_kernel<<<grid_for(kClip, n), kBlock, 0, s>>>(grad_buf, n, a, hp->max_grad_norm, tot_sq,
-                                                                 tot_flag, ws);
+    clipped_update_kernel<<<grid_for(kClip, n), kBlock, 0, s>>>(grad_buf, n, a, hp->max_grad_norm, ws, grid1);
     return finish_launch();
 }
 
@@ -1335,12 +1389,34 @@ int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st, c
     const int rc = check_step(src, &sub, hp, allgather, ag_off, workspace, nullptr, &a, &ag);
     if (rc != ZERO_OK) return rc;
     if (hp->max_grad_norm != 0.0) return ZERO_EINVAL;  // clipping needs the norm before any bucket
+    // the whole window's all-gather range, for the re-emit of a skipped step
+    uint16_t* ag_window = nullptr;
+    if (allgather != nullptr) {
+        int64_t e = 0;
+        if (zdp::add_overflows(allgather_off, window_n, &e) || zdp::mul_overflows(e, 2, &e)) return ZERO_EOVERFLOW;
+        ag_window = allgather + allgather_off;
+        if (!aligned16(ag_window)) return ZERO_EALIGN;
+    }
     a.bucket = phase | 4;
     a.window_n = window_n;
-    const int grid = grid_for(kFused, src->n);
+    // every bucket of a step runs on the same grid: each workgroup adds its
+    // partial to its own slot
+    const int grid = resident_blocks(kFused) < zdp::kMaxBlocks ? resident_blocks(kFused) : zdp::kMaxBlocks;
+    const Partials ws = make_ws(workspace);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    fused_step_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
-        make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), a, make_ws(workspace));
+    fused_step_kernel<<<grid, kBlock, 0, s>>>(make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), a, ws);
+    const int rc2 = finish_launch();
+    if (rc2 != ZERO_OK || (phase & ZERO_BUCKET_LAST) == 0) return rc2;
+    // the commit, over the whole window
+    AdamArgs c = a;
+    for (int i = 0; i < 2; ++i) {
+        c.p[i] = st->master[i];
+        c.m[i] = st->exp_avg[i];
+        c.v[i] = st->exp_avg_sq[i];
+    }
+    c.ag = ag_window;
+    commit_kernel<<<grid_for(kCommit, window_n), kBlock, 0, s>>>(c, ws, grid, window_n);
     return finish_launch();
 }
 

@@ -1,8 +1,8 @@
 """Device buffers of one rank's owned shard, allocated with torch.
 
 Holds the ping-pong fp32 Adam state, the device control block and the
-workspace, and forwards each step to the library (zero_adam_step followed
-by zero_restore_skipped).  torch is used only to allocate device memory and
+workspace, and forwards each step to the library (zero_adam_step, which
+also restores the all-gather window of a skipped step).  torch is used only to allocate device memory and
 to name the stream.
 """
 from __future__ import annotations
@@ -51,24 +51,20 @@ class OwnedShard:
                                 self.workspace, stream)
             return
         B.adam_step(src, self.state, self.hp, allgather, allgather_off, self.workspace, stream)
-        if allgather is not None:
-            B.restore_skipped(self.state, self.n, allgather, allgather_off, stream)
 
     def step_bucket(self, slices, win_off: int, n: int, phase: int, loss_scale: float = 1.0, elem_off: int = 0,
                     allgather=None, allgather_off: int = 0, stream=None):
         """One bucket of a bucketed step: columns [elem_off, elem_off + n) of
         ``slices`` [Nd, stride] hold the gradients of window elements
         [win_off, win_off + n).  ``phase`` carries B.BUCKET_FIRST on the
-        step's first bucket and B.BUCKET_LAST on its last; after the last,
-        the all-gather window is restored if the step was skipped."""
+        step's first bucket and B.BUCKET_LAST on its last; the last also
+        commits the step (restoring the all-gather window if it is skipped)."""
         if self.clipped:
             raise ValueError("a bucketed step cannot clip (the norm is needed before any bucket)")
         nd, stride = slices.shape
         src = B.grad_src(slices, stride, elem_off, n, nd, loss_scale)
         B.adam_step_bucket(src, self.state, self.hp, win_off, self.n, allgather, allgather_off, phase,
                            self.workspace, stream)
-        if allgather is not None and phase & B.BUCKET_LAST:
-            B.restore_skipped(self.state, self.n, allgather, allgather_off, stream)
 
     def emit(self, allgather, allgather_off: int = 0, stream=None):
         """fp16 copy of the committed master into the all-gather buffer."""
