@@ -152,7 +152,8 @@ typedef struct zero_grad_src {
 } zero_grad_src;
 
 /* ---- workspace ----------------------------------------------------------
- * Device scratch for per-block partial results and a completion counter.
+ * Device scratch for per-workgroup partial results, a completion counter
+ * and the element count of a bucketed step.
  * Allocate zero_workspace_bytes() bytes of device memory (16-byte aligned),
  * zero it ONCE before first use, and never share one workspace between calls
  * that may run concurrently (different streams).  Every call leaves it ready
@@ -179,8 +180,8 @@ int zero_reduce_owned(const zero_grad_src* src, float* grad_out, int32_t* overfl
  * anthology note "Assumptions"; trishampatil "The Real Problem"), held twice
  * (ping-pong) so that a step found to overflow after its single pass can be
  * dropped: each step reads set ctl->cur and writes set 1 - ctl->cur, and the
- * step's last workgroup commits it (cur ^= 1, t += 1) only when no element
- * overflowed.  The control block lives in device memory; initialise it with
+ * step's commit (on the device, after the pass) sets cur ^= 1 and t += 1
+ * only when no element overflowed.  The control block lives in device memory; initialise it with
  * zero_ctl_init() on the host and copy it to the device.
  */
 typedef struct zero_step_ctl {
@@ -238,8 +239,11 @@ typedef struct zero_adam_hp {
  * flag and sum g^2 -> Adam/AdamW in float64 (m' = b1 m + (1-b1) g;
  * v' = b2 v + (1-b2) g^2; d = sqrt(v') / sqrt(1-b2^t) + eps;
  * p' = p (1 - lr wd) - lr/(1-b1^t) * m'/d; state stored as fp32, RNE) ->
- * allgather[allgather_off + j] = fp16_RNE(fp32 p'_j).  Then the commit in
- * ctl (see zero_adam_state).  "Each process updates only its own
+ * allgather[allgather_off + j] = fp16_RNE(fp32 p'_j).  Two launches: the
+ * fused pass (each workgroup leaves its partial sum of g^2 and flag in the
+ * workspace) and a small commit kernel that sums them in a fixed order and
+ * commits the step in ctl (see zero_adam_state), or skips it and re-emits
+ * the all-gather window from the committed master.  "Each process updates only its own
  * [partition] and an all-gather distributes the updated parameters"
  * (upskillscore "How it works"; trishampatil "Forward/Backward Under
  * ZeRO-3": reduce-scatter, update the shard, all-gather).
@@ -250,10 +254,10 @@ typedef struct zero_adam_hp {
  *   allgather: device uint16 buffer; the window [allgather_off,
  *        allgather_off + n) is written (16-byte aligned start).  NULL skips
  *        the emit.
- * On an overflowing step the state is untouched (not committed) but the
- * all-gather window has been overwritten: call zero_restore_skipped before
- * the window is read.  Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW,
- * ZERO_EALIAS, ZERO_EHIP.
+ * On an overflowing step the state is untouched (not committed) and the
+ * all-gather window holds the committed parameters again once the call's
+ * work has run; no host synchronisation or restore call is needed.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EALIAS, ZERO_EHIP.
  */
 int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st,
                    const zero_adam_hp* hp, uint16_t* allgather, int64_t allgather_off,
@@ -292,19 +296,25 @@ int zero_adam_step_clipped(const zero_grad_src* src, const zero_adam_state* st,
  * the fused update of zero_adam_step on its elements, reading state
  * buffer ctl->cur and writing the other one plus
  * allgather[allgather_off + win_off + j]; nothing is committed until the
- * last bucket.  Sum g^2, the overflow flag and the number of elements
- * covered accumulate in the workspace in stream order (deterministic for a
- * given bucket order).  The launch flagged ZERO_BUCKET_LAST commits the
- * whole step as zero_adam_step would, or skips it if any bucket overflowed
+ * last bucket.  Each workgroup's sum of g^2 and flag accumulate in its
+ * workspace slot across the step's buckets (all bucket launches run on the
+ * same grid), and the elements covered in a counter, in stream order
+ * (deterministic for a given bucket order).  The call flagged
+ * ZERO_BUCKET_LAST also launches the commit: the whole step is committed as
+ * zero_adam_step would, or skipped if any bucket overflowed
  * (ctl->overflow = 1, the loss scale backs off) or if the buckets covered
  * fewer or more than window_n elements (ctl->overflow = 2, the loss scale
- * is left alone).  After a skip, call zero_restore_skipped over the window.
+ * is left alone); a skip re-emits the whole all-gather window.
  *   st: the window's state, as for zero_adam_step (n = window_n).
+ *   allgather, allgather_off: the whole window's all-gather range (its
+ *   start 16-byte aligned); bucket b writes from allgather_off + win_off.
  *   win_off: multiple of 8.  phase: ZERO_BUCKET_FIRST on the step's first
  *   bucket, ZERO_BUCKET_LAST on its last (both for a single bucket), 0 in
  *   between.  Every bucket of a step runs on one stream with one
- *   workspace; the buckets may come in any order but must not overlap
- *   (an overlap that keeps the count equal to window_n is not detected).
+ *   workspace, and no other call may use that workspace between the step's
+ *   first and last bucket; the buckets may come in any order but must not
+ *   overlap (an overlap that keeps the count equal to window_n is not
+ *   detected).
  *   hp->max_grad_norm must be 0: clipping needs the whole norm before any
  *   bucket is updated.
  * Errors: ZERO_EINVAL (also win_off + n > window_n), ZERO_EALIGN,
@@ -320,6 +330,9 @@ int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st,
 /* Re-emits allgather[off + j] = fp16_RNE(master[ctl->cur][j]) for j < n when
  * ctl->overflow != 0 (the step was skipped), and does nothing otherwise; the
  * decision is taken on the device, so no host synchronisation is needed.
+ * The steps restore their window themselves; this call is for a window
+ * that must be re-derived from the committed master at another time (for
+ * example a second copy of the window).
  * The window must not overlap either master or the control block.
  * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EALIAS, ZERO_EHIP. */
 int zero_restore_skipped(const zero_adam_state* st, int64_t n, uint16_t* allgather,
