@@ -388,7 +388,7 @@ def main():
     bytes_elem = 2 * w.nd + (34 if clipped else 26)
     achieved = bytes_elem * S / (kern_avg * 1e-3) / 1e9
     what = (f"bucketed step ({len(buckets)} launches + commit)" if bucketed else
-            "clipped step (2 kernels)" if clipped else "fused step (fused + commit kernels)")
+            "clipped step (reduce + update + commit kernels)" if clipped else "fused step (fused + commit kernels)")
     log(f"{what}: avg {kern_avg * 1e3:.1f} us over {args.steps} back-to-back launches; "
         f"step {ms_step * 1e3:.1f} us; {achieved:.0f} GB/s")
 
@@ -437,7 +437,7 @@ def main():
             "traffic": None if traffic is None else traffic / (kern_avg * 1e-3) / 1e9,
             "traffic_bytes_per_launch": traffic,
             "algorithmic_bytes_per_launch": bytes_elem * S,
-            "kernel": ("reduce_owned_kernel + clipped_update_kernel" if clipped else
+            "kernel": ("reduce_owned_kernel + clipped_update_kernel + commit_kernel" if clipped else
                        f"fused_step_kernel x {len(buckets)} buckets + commit_kernel" if bucketed else
                        "fused_step_kernel + commit_kernel"),
             "kernel_avg_us": kern_avg * 1e3,

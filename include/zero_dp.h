@@ -273,8 +273,8 @@ int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st,
  *   pass 2: if the flag is set, the step is skipped (state and all-gather
  *           window untouched, no restore needed); otherwise
  *           coef = min(1, max_grad_norm / (sqrt(sumsq) + 1e-6)) and the
- *           update of zero_adam_step runs on g = g32 * coef (float64), then
- *           the commit; ctl->clip_coef records coef.
+ *           update of zero_adam_step runs on g = g32 * coef (float64);
+ *   then a one-workgroup commit; ctl->clip_coef records coef.
  * L is src->loss_scale or, with dynamic scaling, ctl->loss_scale.
  * Traffic (2*Nd + 4) + 30 bytes per element instead of 2*Nd + 26.
  *   grad_buf: device float[n], 16-byte aligned, must not overlap any other

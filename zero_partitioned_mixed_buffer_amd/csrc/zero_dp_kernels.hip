@@ -339,20 +339,6 @@ __device__ __forceinline__ void sum_partials(const Partials& ws, int nparts, dou
     flag = s_flag;
 }
 
-// True in every thread of the workgroup that finishes last (a ticket with
-// no partials: the caller only needs to know that every workgroup is done).
-__device__ __forceinline__ bool last_block_done(uint32_t* ticket) {
-    __shared__ int s_last;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == gridDim.x - 1);
-        if (s_last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    return s_last != 0;
-}
-
 // ---------------------------------------------------------------- kernels
 struct SrcArgs {
     const uint16_t* win;       // base + elem_off: slice 0 of the window
@@ -940,10 +926,7 @@ __global__ void __launch_bounds__(kBlock) clipped_update_kernel(
     double sq_in;
     int flag;
     sum_partials(ws, nparts, sq_in, flag);  // the first pass's, identical in every workgroup
-    if (flag != 0) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) commit_step(a, a.ctl->cur, 0.0, 0.0, 1, sq_in, 1.0);
-        return;
-    }
+    if (flag != 0) return;                  // skipped: commit_kernel records it
     const double r = max_norm / (__builtin_sqrt(sq_in) + 1e-6);
     const double coef = r < 1.0 ? r : 1.0;
     const int cur = a.ctl->cur;
@@ -968,9 +951,8 @@ __global__ void __launch_bounds__(kBlock) clipped_update_kernel(
             }
         }
     }
-    // commit once every workgroup has read ctl->cur (a ticket only: the
-    // partial slots still hold the first pass's sums that others may read)
-    if (last_block_done(ws.ticket) && threadIdx.x == 0) commit_step(a, cur, b1t, b2t, 0, sq_in, coef);
+    (void)b1t;  // the commit kernel recomputes the powers it commits
+    (void)b2t;
 }
 
 __device__ __forceinline__ void emit_range(const float* __restrict__ src, uint16_t* __restrict__ ag,
@@ -1012,7 +994,13 @@ __global__ void __launch_bounds__(kBlock) restore_kernel(const float* p0, const 
 // off the loss scale), and on a skip every workgroup re-emits its share of
 // the all-gather window from the committed master.  A skip never changes
 // ctl->cur, so the workgroups that read it race with no write.
-__global__ void __launch_bounds__(kBlock) commit_kernel(AdamArgs a, Partials ws, int32_t nparts, int64_t n) {
+//
+// Clipped mode (max_norm > 0, one workgroup, after the clipped step's second
+// pass): the partials are the first pass's; the coefficient is recomputed
+// with the same operations as the second pass used, and a skipped clipped
+// step wrote nothing, so there is nothing to re-emit.
+__global__ void __launch_bounds__(kBlock) commit_kernel(AdamArgs a, Partials ws, int32_t nparts, int64_t n,
+                                                        double max_norm) {
     double sq;
     int flag;
     sum_partials(ws, nparts, sq, flag);
@@ -1020,9 +1008,14 @@ __global__ void __launch_bounds__(kBlock) commit_kernel(AdamArgs a, Partials ws,
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         double b1t, b2t;
         (void)step_scalars(a, b1t, b2t);
-        commit_step(a, a.ctl->cur, b1t, b2t, flag, sq, 1.0);
+        double coef = 1.0;
+        if (max_norm > 0.0) {
+            const double r = max_norm / (__builtin_sqrt(sq) + 1e-6);
+            coef = r < 1.0 ? r : 1.0;
+        }
+        commit_step(a, a.ctl->cur, b1t, b2t, flag, sq, flag ? 1.0 : coef);
     }
-    if (flag != 0 && a.ag != nullptr) emit_range(a.p[a.ctl->cur], a.ag, n);
+    if (max_norm == 0.0 && flag != 0 && a.ag != nullptr) emit_range(a.p[a.ctl->cur], a.ag, n);
 }
 
 // ------------------------------------------------- Pos+g+p parameter gather
@@ -1334,7 +1327,7 @@ int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st, const ze
     fused_step_kernel<<<grid, kBlock, 0, s>>>(make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), a, ws);
     const int rc2 = finish_launch();
     if (rc2 != ZERO_OK) return rc2;
-    commit_kernel<<<grid_for(kCommit, src->n), kBlock, 0, s>>>(a, ws, grid, src->n);
+    commit_kernel<<<grid_for(kCommit, src->n), kBlock, 0, s>>>(a, ws, grid, src->n, 0.0);
     return finish_launch();
 }
 
@@ -1357,6 +1350,9 @@ int zero_adam_step_clipped(const zero_grad_src* src, const zero_adam_state* st, 
     int rc2 = finish_launch();
     if (rc2 != ZERO_OK) return rc2;
     clipped_update_kernel<<<grid_for(kClip, n), kBlock, 0, s>>>(grad_buf, n, a, hp->max_grad_norm, ws, grid1);
+    rc2 = finish_launch();
+    if (rc2 != ZERO_OK) return rc2;
+    commit_kernel<<<1, kBlock, 0, s>>>(a, ws, grid1, n, hp->max_grad_norm);
     return finish_launch();
 }
 
@@ -1416,7 +1412,7 @@ int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st, c
         c.v[i] = st->exp_avg_sq[i];
     }
     c.ag = ag_window;
-    commit_kernel<<<grid_for(kCommit, window_n), kBlock, 0, s>>>(c, ws, grid, window_n);
+    commit_kernel<<<grid_for(kCommit, window_n), kBlock, 0, s>>>(c, ws, grid, window_n, 0.0);
     return finish_launch();
 }
 
