@@ -389,7 +389,7 @@ def main():
     achieved = bytes_elem * S / (kern_avg * 1e-3) / 1e9
     what = (f"bucketed step ({len(buckets)} launches + commit)" if bucketed else
             "clipped step (reduce + update + commit kernels)" if clipped else "fused step (fused + commit kernels)")
-    log(f"{what}: avg {kern_avg * 1e3:.1f} us over {args.steps} back-to-back launches; "
+    log(f"{what}: avg {kern_avg * 1e3:.1f} us over {args.steps} back-to-back steps; "
         f"step {ms_step * 1e3:.1f} us; {achieved:.0f} GB/s")
 
     cpu = None

@@ -2,8 +2,8 @@
 
 Holds the ping-pong fp32 Adam state, the device control block and the
 workspace, and forwards each step to the library (zero_adam_step, which
-also restores the all-gather window of a skipped step).  torch is used only to allocate device memory and
-to name the stream.
+also restores the all-gather window of a skipped step).  torch is used
+only to allocate device memory and to name the stream.
 """
 from __future__ import annotations
 
