@@ -68,9 +68,9 @@ int zero_abi_version(void);
 
 /* ---- partition plan (host, synchronous) ------------------------------
  * The flat parameter buffer holds the tensors packed in list order; it is
- * split into Nd equal windows ("shard i" on GPU i: trishampatil "ZeRO's Core
- * Idea"; "the optimizer states are split into Nd parts": upskillscore "How
- * it works").  The pages leave padding open; this library pads the total to
+ * split into Nd equal windows, window i held by rank i (trishampatil "ZeRO's
+ * Core Idea"; upskillscore "How it works": the optimizer state is divided
+ * among the Nd data-parallel ranks).  The pages leave padding open; this library pads the total to
  * S = align * ceil(Psi / (Nd * align)) elements per rank, so rank r owns flat
  * elements [r*S, (r+1)*S) and all padding sits at the tail of rank Nd-1.
  */
@@ -164,8 +164,8 @@ int64_t zero_workspace_bytes(void);
 /* ---- reduce (decomposed path) ---------------------------------------
  * s_j = G_0[j] + ... + G_{Nd-1}[j] (exact, float64), g_j = s_j * (1/L),
  * *overflow = 1 if any s_j is inf/NaN else 0, *sumsq = sum_j g_j^2 (float64,
- * deterministic order).  Pos+g: "each gradient is reduced only on the
- * process that owns the partition" (upskillscore "How it works").
+ * deterministic order).  Pos+g: a gradient partition is summed on its
+ * owning rank alone (upskillscore "How it works").
  *   grad_out: device float[n], 16-byte aligned, receives fp32(g); may be NULL.
  *   overflow: device int32 (4-byte aligned), required.  sumsq: device double
  *   (8-byte aligned), required.  workspace: see above.  No output may
@@ -243,10 +243,14 @@ typedef struct zero_adam_hp {
  * fused pass (each workgroup leaves its partial sum of g^2 and flag in the
  * workspace) and a small commit kernel that sums them in a fixed order and
  * commits the step in ctl (see zero_adam_state), or skips it and re-emits
- * the all-gather window from the committed master.  "Each process updates only its own
- * [partition] and an all-gather distributes the updated parameters"
- * (upskillscore "How it works"; trishampatil "Forward/Backward Under
- * ZeRO-3": reduce-scatter, update the shard, all-gather).
+ * the all-gather window from the committed master.  A window of more than
+ * 2^25 elements takes its fused pass in consecutive launches of about 2^24
+ * elements each (measured faster than one long launch), whose partials
+ * accumulate in the workspace; the results are the same element for
+ * element, and the sum of g^2 differs only in its rounding order.  A rank steps its own
+ * partition alone and the new parameters then reach every rank by
+ * all-gather (upskillscore "How it works"; trishampatil "Forward/Backward
+ * Under ZeRO-3": reduce-scatter, update the shard, all-gather).
  *   src: gradient source, src->n = window length.
  *   st:  ping-pong state; neither set may overlap the other, the slices or
  *        the all-gather window.  st->ctl is 8-byte aligned, and neither it

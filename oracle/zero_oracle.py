@@ -7,10 +7,10 @@ no code with the HIP library: no kernels, headers, helpers or constants.
 What it computes follows the ZeRO pages:
 
 * "ZeRO: partitioning training state across GPUs" (upskillscore concept page),
-  section "How it works": the model states of Psi parameters are split into
-  Nd parts; the owner of a gradient partition reduces it (reduce-scatter),
-  updates only its own optimizer-state partition, and an all-gather
-  distributes the updated fp16 parameters.  Memory 16Psi / 4Psi+12Psi/Nd /
+  section "How it works": the model states of Psi parameters are divided
+  among Nd ranks; a gradient partition is summed by its owner
+  (reduce-scatter), which steps its own slice of the optimizer state, and
+  the new fp16 parameters reach every rank by all-gather.  Memory 16Psi / 4Psi+12Psi/Nd /
   2Psi+14Psi/Nd / 16Psi/Nd; communication 2Psi (stages 0-2) or 3Psi.
 * The trishampatil.com engineering dissection of ZeRO (page
   zero-memory-optimization-training-large-models), sections "The Real Problem" (2Psi + 2Psi + K Psi,
@@ -72,8 +72,8 @@ F64 = np.float64
 
 
 # --------------------------------------------------------------------------
-# Partition plan.  Upskillscore "How it works": optimizer states are split
-# into Nd parts, each process updating its own; trishampatil "ZeRO's Core
+# Partition plan.  Upskillscore "How it works": the optimizer state is
+# divided among the Nd ranks and each rank steps its own; trishampatil "ZeRO's Core
 # Idea" figure: GPU i holds shard i.  Padding/alignment is a reading (the
 # pages do not fix it): equal shards of S = A*ceil(Psi/(Nd*A)) elements.
 # --------------------------------------------------------------------------
@@ -157,8 +157,8 @@ def memory_model(psi: float, nd: int, stage: int, k: int = 12) -> dict:
 
 
 # --------------------------------------------------------------------------
-# Local half of the reduce-scatter.  Upskillscore "How it works" (Pos+g: each
-# gradient is reduced only on the process that owns the partition);
+# Local half of the reduce-scatter.  Upskillscore "How it works" (Pos+g: a
+# gradient partition is summed on its owning rank alone);
 # trishampatil "Forward/Backward Under ZeRO-3" (reduce-scatter gradients into
 # shards).  Reading: the reduction is an exact sum.
 # --------------------------------------------------------------------------
@@ -235,7 +235,7 @@ def adam_update(p, m, v, g, sc):
 
 def emit(master: np.ndarray) -> np.ndarray:
     """fp16 copy of the fp32 master for the all-gather buffer (upskillscore
-    "How it works": the all-gather distributes the updated parameters).
+    "How it works": the new parameters reach every rank by all-gather).
     IEEE round-to-nearest-even; overflow to +-inf."""
     return np.asarray(master, dtype=F32).astype(F16)
 

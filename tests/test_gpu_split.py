@@ -1,0 +1,97 @@
+"""GPU parity of a long window, whose fused pass the library runs as several
+consecutive launches (windows of more than 2^25 elements).
+
+The same window is stepped twice on the device: by zero_adam_step (split
+into launches) and in buckets of 2^20 elements (one launch each; the
+bucketed step is compared with the oracle element by element in
+test_gpu_buckets).  Every element of the state and of the all-gather
+window must agree bit for bit, flags and step counts exactly, the sum of
+g^2 within 1e-12 of a float64 torch sum.  Sampled elements, dense around
+every multiple of 1024 (where any split into 16-byte aligned launches
+puts its boundaries), are also compared with the oracle: flags and t
+exact, fp32 state within 1e-5 relative, fp16 window within 1 ulp.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import gen
+
+from gpu_util import assert_fp16_close, assert_state_close, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+N = (1 << 25) + 5003  # a ragged tail group after the last full one
+ND = 3
+L = 1024.0
+
+
+def say(msg):
+    print(f"[split] {msg}", file=sys.stderr, flush=True)
+
+
+def _sample_idx(n):
+    g = np.random.default_rng(5)
+    near = (np.arange(0, n, 1024, dtype=np.int64)[:, None] + np.arange(-4, 4, dtype=np.int64)).ravel()
+    idx = np.unique(np.concatenate([near, g.integers(0, n, 1 << 15, dtype=np.int64),
+                                    np.arange(n - 16, n, dtype=np.int64)]))
+    return idx[(idx >= 0) & (idx < n)]
+
+
+def _sumsq(torch, slices):
+    g = slices.to(torch.float64).sum(0) * (1.0 / L)
+    return float((g * g).sum().item())
+
+
+def test_long_window_split_launches():
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import OwnedShard
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    master = torch.empty(N, dtype=torch.float32, device="cuda")
+    gen.device_fill_params(master, 123, 0.02, N)
+    idx = _sample_idx(N)
+    tidx = torch.from_numpy(idx).cuda()
+    ref = oracle.OwnedShard(master[tidx].cpu().numpy(), **hp)
+    whole = OwnedShard(master, **hp)
+    buck = OwnedShard(master, **hp)
+    del master
+    ag_w = torch.zeros(N + 16, dtype=torch.float16, device="cuda")
+    ag_b = torch.zeros(N + 16, dtype=torch.float16, device="cuda")
+    whole.emit(ag_w, 8)
+    buck.emit(ag_b, 8)
+    # slice stride a multiple of 8 elements; the columns past N are zero
+    dsl = torch.empty((ND, (N + 7) // 8 * 8), dtype=torch.float16, device="cuda")
+    bucket = 1 << 20
+    say(f"n={N} nd={ND}: {idx.size} sampled elements")
+    for step in range(1, 4):
+        gen.device_fill_grads(dsl, 77, step, 1e-3, L, "normal", N)
+        if step == 2:
+            dsl[1, N - 10] = float("inf")  # in the last launch of the split (sampled)
+        ovf, _ = ref.step(dsl[:, tidx].cpu().numpy(), L)
+        sq_want = None if ovf else _sumsq(torch, dsl)
+        say(f"step {step}: split whole-window step, then {-(-N // bucket)} buckets")
+        whole.step(dsl, L, allgather=ag_w, allgather_off=8)
+        for o in range(0, N, bucket):
+            k = min(bucket, N - o)
+            phase = (B.BUCKET_FIRST if o == 0 else 0) | (B.BUCKET_LAST if o + k >= N else 0)
+            buck.step_bucket(dsl, o, k, phase, L, elem_off=o, allgather=ag_b, allgather_off=8)
+        torch.cuda.synchronize()
+        cw, cb = whole.control(), buck.control()
+        tag = f"step {step}"
+        assert cw["overflow"] == cb["overflow"] == int(ovf), tag
+        assert cw["t"] == cb["t"] == ref.t and cw["skipped"] == cb["skipped"], tag
+        for a, b in zip(whole.committed(cw), buck.committed(cb)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), tag
+        assert torch.equal(ag_w.view(torch.int16), ag_b.view(torch.int16)), tag
+        if not ovf:
+            assert cw["sumsq"] == pytest.approx(sq_want, rel=1e-12), tag
+            assert cb["sumsq"] == pytest.approx(sq_want, rel=1e-12), tag
+        p, m, v = (x[tidx].cpu().numpy() for x in whole.committed(cw))
+        for got, want, nm in ((p, ref.p, "p"), (m, ref.m, "m"), (v, ref.v, "v")):
+            assert_state_close(got, want, f"{tag} {nm}")
+        bits = ag_w.view(torch.int16)[8 + tidx].cpu().numpy().view(np.uint16)
+        assert_fp16_close(bits, ref.window().view(np.uint16), f"{tag} window")
+    assert ref.flags == [0, 1, 0] and ref.t == 2

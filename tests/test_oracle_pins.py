@@ -35,7 +35,7 @@ def test_memory_table_printed(golden):
 
 
 def test_memory_gpt2_1p5b():
-    """GPT-2 1.5B: at least 24 GB of model state vs 3 GB of fp16 weights
+    """GPT-2 1.5B: 24 GB or more of model state against 3 GB of fp16 weights
     (trishampatil "The Real Problem")."""
     r = oracle.memory_model(1.5e9, 1, 0)
     assert r["total_bytes"] == 24e9

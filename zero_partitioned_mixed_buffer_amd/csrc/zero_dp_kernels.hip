@@ -2,8 +2,8 @@
 //
 // One rank's step over its owned window, fused into a single streaming pass
 // (upskillscore "How it works": the owner reduces its gradient partition by
-// reduce-scatter, updates only its own optimizer-state partition, and an
-// all-gather distributes the updated parameters; trishampatil
+// reduce-scatter, steps its own slice of the optimizer state, and the new
+// parameters reach every rank by all-gather; trishampatil
 // "Forward/Backward Under ZeRO-3": reduce-scatter -> update shard ->
 // all-gather):
 //
@@ -26,15 +26,19 @@
 // in flight per CU, and a single pass over every array.
 //
 // Kernels:
-//   fused_step_kernel      the step above, whole window or one bucket of it
-//                          (running totals in the workspace; the last
-//                          bucket commits)
+//   fused_step_kernel      the step above over the whole window, one piece
+//                          of a long window, or one bucket (workgroup
+//                          partials in the workspace for commit_kernel)
 //   reduce_owned_kernel    the sum / unscale / flag / sum of g^2 alone; the
 //                          first pass of the clipped step (fp32 g stored)
 //   clipped_update_kernel  the clipped step's second pass: g * min(1,
-//                          max_norm / (norm + 1e-6)), update, emit, commit
+//                          max_norm / (norm + 1e-6)), update, emit
+//   commit_kernel          the launch after a step's passes: sums the
+//                          workgroup partials in a fixed order, commits or
+//                          skips the step in the control block, re-emits
+//                          the window of a skipped fused step
 //   emit_kernel, restore_kernel   fp16 window from the fp32 master (initial
-//                          fill; re-emit after a skipped step)
+//                          fill; re-emit on demand)
 //   copy_f16_kernel        a Pos+g+p layer gather: the layer's pieces of up
 //                          to 16 owners' windows in one launch (trishampatil
 //                          "ZeRO-3": parameters gathered on demand, used,
@@ -1276,6 +1280,61 @@ int check_step(const zero_grad_src* src, const zero_adam_state* st, const zero_a
     return ZERO_OK;
 }
 
+// The grid of every launch of a step that accumulates workgroup slots
+// (buckets, split windows): the same on every launch on a device.
+int fixed_grid() {
+    const int r = resident_blocks(kFused);
+    return r < zdp::kMaxBlocks ? r : zdp::kMaxBlocks;
+}
+
+#ifndef ZDP_SPLIT_LOG2
+#define ZDP_SPLIT_LOG2 24  // elements per launch of a long window: about 2^24 (0: one launch)
+#endif
+
+// A window longer than two launch lengths is stepped in launches of about
+// 2^24 elements.  One grid-stride launch over 10^8 elements measured 3-4%
+// slower than the same work in launches of 2^24 elements (Nd 16, 64 and
+// 400); shorter windows take one launch, where the few microseconds an
+// extra launch costs outweigh the gain.
+constexpr int64_t kSplitElems = ZDP_SPLIT_LOG2 > 0 ? (int64_t{1} << ZDP_SPLIT_LOG2) : 0;
+
+bool split_window(int64_t n) { return kSplitElems > 0 && n > 2 * kSplitElems; }
+
+// Launches the fused kernel over the elements of `src`, whose state and
+// all-gather pointers are those of `a`, as consecutive launches of at most
+// about kSplitElems elements when split_window(src.n), else one.  Every
+// launch accumulates into the workgroup slots except the first when `first`
+// (the first launch of a step).  a.window_n must be set.
+int launch_fused_range(const SrcArgs& src, const AdamArgs& a, bool first, int grid, const Partials& ws,
+                       hipStream_t s) {
+    const int64_t n = src.n;
+    int64_t len = n;
+    if (split_window(n)) {
+        const int64_t pieces = (n + kSplitElems - 1) / kSplitElems;
+        len = ((n + pieces - 1) / pieces + 1023) / 1024 * 1024;  // keeps every piece 16-byte aligned
+    }
+    int64_t off = 0;
+    do {
+        const int64_t k = n - off < len ? n - off : len;
+        SrcArgs sub = src;
+        sub.win = src.win + off;
+        sub.n = k;
+        AdamArgs b = a;
+        for (int i = 0; i < 2; ++i) {
+            b.p[i] = a.p[i] + off;
+            b.m[i] = a.m[i] + off;
+            b.v[i] = a.v[i] + off;
+        }
+        b.ag = a.ag != nullptr ? a.ag + off : nullptr;
+        b.bucket = 4 | (first && off == 0 ? ZERO_BUCKET_FIRST : 0);
+        fused_step_kernel<<<grid, kBlock, 0, s>>>(sub, b, ws);
+        const int rc = finish_launch();
+        if (rc != ZERO_OK) return rc;
+        off += k;
+    } while (off < n);
+    return ZERO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1320,14 +1379,27 @@ int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st, const ze
     const int rc = check_step(src, st, hp, allgather, allgather_off, workspace, nullptr, &a, &ag);
     if (rc != ZERO_OK) return rc;
     if (hp->max_grad_norm != 0.0) return ZERO_EINVAL;  // clipping needs the two-pass entry point
-    const int grid = grid_for(kFused, src->n);
+    const int64_t n = src->n;
     const Partials ws = make_ws(workspace);
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    const SrcArgs whole = make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr);
     (void)hipGetLastError();
-    fused_step_kernel<<<grid, kBlock, 0, s>>>(make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), a, ws);
-    const int rc2 = finish_launch();
+    if (!split_window(n)) {
+        const int grid = grid_for(kFused, n);
+        fused_step_kernel<<<grid, kBlock, 0, s>>>(whole, a, ws);
+        const int rc2 = finish_launch();
+        if (rc2 != ZERO_OK) return rc2;
+        commit_kernel<<<grid_for(kCommit, n), kBlock, 0, s>>>(a, ws, grid, n, 0.0);
+        return finish_launch();
+    }
+    // a long window: consecutive launches accumulating the workgroup slots,
+    // as the buckets of one step, then the commit
+    a.window_n = n;
+    const int grid = fixed_grid();
+    const int rc2 = launch_fused_range(whole, a, true, grid, ws, s);
     if (rc2 != ZERO_OK) return rc2;
-    commit_kernel<<<grid_for(kCommit, src->n), kBlock, 0, s>>>(a, ws, grid, src->n, 0.0);
+    a.bucket = ZERO_BUCKET_LAST | 4;
+    commit_kernel<<<grid_for(kCommit, n), kBlock, 0, s>>>(a, ws, grid, n, 0.0);
     return finish_launch();
 }
 
@@ -1393,16 +1465,16 @@ int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st, c
         ag_window = allgather + allgather_off;
         if (!aligned16(ag_window)) return ZERO_EALIGN;
     }
-    a.bucket = phase | 4;
+    a.bucket = phase | 4;  // the commit below checks the buckets' coverage
     a.window_n = window_n;
     // every bucket of a step runs on the same grid: each workgroup adds its
     // partial to its own slot
-    const int grid = resident_blocks(kFused) < zdp::kMaxBlocks ? resident_blocks(kFused) : zdp::kMaxBlocks;
+    const int grid = fixed_grid();
     const Partials ws = make_ws(workspace);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    fused_step_kernel<<<grid, kBlock, 0, s>>>(make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), a, ws);
-    const int rc2 = finish_launch();
+    const int rc2 = launch_fused_range(make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), a,
+                                       (phase & ZERO_BUCKET_FIRST) != 0, grid, ws, s);
     if (rc2 != ZERO_OK || (phase & ZERO_BUCKET_LAST) == 0) return rc2;
     // the commit, over the whole window
     AdamArgs c = a;
