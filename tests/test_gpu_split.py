@@ -95,3 +95,61 @@ def test_long_window_split_launches():
         bits = ag_w.view(torch.int16)[8 + tidx].cpu().numpy().view(np.uint16)
         assert_fp16_close(bits, ref.window().view(np.uint16), f"{tag} window")
     assert ref.flags == [0, 1, 0] and ref.t == 2
+
+
+def _sumsq32(torch, slices):
+    g = (slices.to(torch.float64).sum(0) * (1.0 / L)).to(torch.float32).to(torch.float64)
+    return float((g * g).sum().item())
+
+
+def test_long_window_clipped_split():
+    """The clipped step on a long window, both passes split into launches:
+    sampled elements (dense around every multiple of 1024) against the
+    oracle given the window's norm from a float64 torch sum of the fp32
+    gradients; the sum of squares and the clip coefficient within 1e-12
+    (a piece missing from the norm would move both); a skipped step leaves
+    state and window bit-identical."""
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import OwnedShard
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=0.5)
+    master = torch.empty(N, dtype=torch.float32, device="cuda")
+    gen.device_fill_params(master, 321, 0.02, N)
+    idx = _sample_idx(N)
+    tidx = torch.from_numpy(idx).cuda()
+    ref = oracle.OwnedShard(master[tidx].cpu().numpy(), **hp)
+    sh = OwnedShard(master, **hp)
+    del master
+    ag = torch.zeros(N + 16, dtype=torch.float16, device="cuda")
+    sh.emit(ag, 8)
+    dsl = torch.empty((ND, (N + 7) // 8 * 8), dtype=torch.float16, device="cuda")
+    for step in range(1, 4):
+        gen.device_fill_grads(dsl, 78, step, 1e-3, L, "normal", N)
+        injected = step == 2
+        if injected:
+            dsl[2, 2] = float("-inf")  # in the first launch of the split (sampled)
+        sq32 = None if injected else _sumsq32(torch, dsl)
+        ovf, _ = ref.step(dsl[:, tidx].cpu().numpy(), L, window_sumsq=sq32)
+        assert ovf == injected
+        if ovf:
+            prev = [x.clone() for x in sh.committed()]
+            prev_ag = ag.clone()
+        say(f"clipped step {step}")
+        sh.step(dsl, L, allgather=ag, allgather_off=8)
+        torch.cuda.synchronize()
+        ctl = sh.control()
+        tag = f"clipped step {step}"
+        assert ctl["overflow"] == int(ovf) and ctl["t"] == ref.t, tag
+        if ovf:
+            for a, b in zip(prev, sh.committed(ctl)):
+                assert torch.equal(a.view(torch.int32), b.view(torch.int32)), tag
+            assert torch.equal(prev_ag.view(torch.int16), ag.view(torch.int16)), tag
+            del prev, prev_ag
+        else:
+            assert ctl["sumsq"] == pytest.approx(sq32, rel=1e-12), tag
+            assert ctl["clip_coef"] == pytest.approx(ref.coefs[-1], rel=1e-12) and ref.coefs[-1] < 0.1, tag
+        p, m, v = (x[tidx].cpu().numpy() for x in sh.committed(ctl))
+        for got, want, nm in ((p, ref.p, "p"), (m, ref.m, "m"), (v, ref.v, "v")):
+            assert_state_close(got, want, f"{tag} {nm}")
+        bits = ag.view(torch.int16)[8 + tidx].cpu().numpy().view(np.uint16)
+        assert_fp16_close(bits, ref.window().view(np.uint16), f"{tag} window")
+    assert ref.flags == [0, 1, 0] and ref.t == 2

@@ -498,7 +498,7 @@ __device__ __forceinline__ bool reduce_pf_dispatch(int nd, int64_t gi, int64_t e
 template <bool kNormOfStored>
 __global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src_in, float* grad_out,
                                                               int32_t* overflow, double* sumsq,
-                                                              Partials ws) {
+                                                              Partials ws, int32_t accumulate) {
     const SrcArgs src = resolve_scale(src_in);
     const int64_t ngroups = (src.n + kV - 1) / kV;
     const int64_t nfull = src.n / kV;
@@ -529,7 +529,8 @@ __global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src_in, fl
     }
     if constexpr (kNormOfStored) {
         // the clipped step's first pass: its second pass sums the partials
-        publish_partial(ws, sq, bad, false);
+        // (a piece of a long window after the first adds to its slot)
+        publish_partial(ws, sq, bad, accumulate != 0);
     } else if (last_block_totals(ws, sq, bad) && threadIdx.x == 0) {
         *overflow = bad;
         *sumsq = sq;
@@ -1282,8 +1283,8 @@ int check_step(const zero_grad_src* src, const zero_adam_state* st, const zero_a
 
 // The grid of every launch of a step that accumulates workgroup slots
 // (buckets, split windows): the same on every launch on a device.
-int fixed_grid() {
-    const int r = resident_blocks(kFused);
+int fixed_grid(KernelId id) {
+    const int r = resident_blocks(id);
     return r < zdp::kMaxBlocks ? r : zdp::kMaxBlocks;
 }
 
@@ -1300,39 +1301,56 @@ constexpr int64_t kSplitElems = ZDP_SPLIT_LOG2 > 0 ? (int64_t{1} << ZDP_SPLIT_LO
 
 bool split_window(int64_t n) { return kSplitElems > 0 && n > 2 * kSplitElems; }
 
-// Launches the fused kernel over the elements of `src`, whose state and
-// all-gather pointers are those of `a`, as consecutive launches of at most
-// about kSplitElems elements when split_window(src.n), else one.  Every
-// launch accumulates into the workgroup slots except the first when `first`
-// (the first launch of a step).  a.window_n must be set.
-int launch_fused_range(const SrcArgs& src, const AdamArgs& a, bool first, int grid, const Partials& ws,
-                       hipStream_t s) {
-    const int64_t n = src.n;
+// Calls launch(off, k) for consecutive pieces [off, off + k) that cover
+// [0, n): one piece, or pieces of about kSplitElems elements (multiples of
+// 1024, so every piece starts 16-byte aligned) when split_window(n).
+template <class Launch>
+int for_each_piece(int64_t n, Launch&& launch) {
     int64_t len = n;
     if (split_window(n)) {
         const int64_t pieces = (n + kSplitElems - 1) / kSplitElems;
-        len = ((n + pieces - 1) / pieces + 1023) / 1024 * 1024;  // keeps every piece 16-byte aligned
+        len = ((n + pieces - 1) / pieces + 1023) / 1024 * 1024;
     }
     int64_t off = 0;
     do {
         const int64_t k = n - off < len ? n - off : len;
-        SrcArgs sub = src;
-        sub.win = src.win + off;
-        sub.n = k;
-        AdamArgs b = a;
-        for (int i = 0; i < 2; ++i) {
-            b.p[i] = a.p[i] + off;
-            b.m[i] = a.m[i] + off;
-            b.v[i] = a.v[i] + off;
-        }
-        b.ag = a.ag != nullptr ? a.ag + off : nullptr;
-        b.bucket = 4 | (first && off == 0 ? ZERO_BUCKET_FIRST : 0);
-        fused_step_kernel<<<grid, kBlock, 0, s>>>(sub, b, ws);
-        const int rc = finish_launch();
+        const int rc = launch(off, k);
         if (rc != ZERO_OK) return rc;
         off += k;
     } while (off < n);
     return ZERO_OK;
+}
+
+SrcArgs piece_src(const SrcArgs& src, int64_t off, int64_t k) {
+    SrcArgs sub = src;
+    sub.win = src.win + off;
+    sub.n = k;
+    return sub;
+}
+
+AdamArgs piece_args(const AdamArgs& a, int64_t off) {
+    AdamArgs b = a;
+    for (int i = 0; i < 2; ++i) {
+        b.p[i] = a.p[i] + off;
+        b.m[i] = a.m[i] + off;
+        b.v[i] = a.v[i] + off;
+    }
+    b.ag = a.ag != nullptr ? a.ag + off : nullptr;
+    return b;
+}
+
+// Launches the fused kernel over the elements of `src`, whose state and
+// all-gather pointers are those of `a`, piece by piece (for_each_piece).
+// Every launch accumulates into the workgroup slots except the first when
+// `first` (the first launch of a step).  a.window_n must be set.
+int launch_fused_range(const SrcArgs& src, const AdamArgs& a, bool first, int grid, const Partials& ws,
+                       hipStream_t s) {
+    return for_each_piece(src.n, [&](int64_t off, int64_t k) {
+        AdamArgs b = piece_args(a, off);
+        b.bucket = 4 | (first && off == 0 ? ZERO_BUCKET_FIRST : 0);
+        fused_step_kernel<<<grid, kBlock, 0, s>>>(piece_src(src, off, k), b, ws);
+        return finish_launch();
+    });
 }
 
 }  // namespace
@@ -1368,7 +1386,7 @@ int zero_reduce_owned(const zero_grad_src* src, float* grad_out, int32_t* overfl
     const int grid = grid_for(kReduce, src->n);
     (void)hipGetLastError();
     reduce_owned_kernel<false><<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
-        make_src(src), grad_out, overflow, sumsq, make_ws(workspace));
+        make_src(src), grad_out, overflow, sumsq, make_ws(workspace), 0);
     return finish_launch();
 }
 
@@ -1395,7 +1413,7 @@ int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st, const ze
     // a long window: consecutive launches accumulating the workgroup slots,
     // as the buckets of one step, then the commit
     a.window_n = n;
-    const int grid = fixed_grid();
+    const int grid = fixed_grid(kFused);
     const int rc2 = launch_fused_range(whole, a, true, grid, ws, s);
     if (rc2 != ZERO_OK) return rc2;
     a.bucket = ZERO_BUCKET_LAST | 4;
@@ -1415,14 +1433,22 @@ int zero_adam_step_clipped(const zero_grad_src* src, const zero_adam_state* st, 
     const int64_t n = src->n;
     const Partials ws = make_ws(workspace);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int grid1 = grid_for(kReduce, n);
+    const SrcArgs whole = make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr);
+    // a long window takes each pass in pieces; the first pass's pieces run
+    // on one grid and accumulate in the workgroup slots
+    const int grid1 = split_window(n) ? fixed_grid(kReduce) : grid_for(kReduce, n);
     (void)hipGetLastError();
-    reduce_owned_kernel<true><<<grid1, kBlock, 0, s>>>(make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr),
-                                                        grad_buf, nullptr, nullptr, ws);
-    int rc2 = finish_launch();
+    int rc2 = for_each_piece(n, [&](int64_t off, int64_t k) {
+        reduce_owned_kernel<true><<<grid1, kBlock, 0, s>>>(piece_src(whole, off, k), grad_buf + off, nullptr,
+                                                            nullptr, ws, off != 0);
+        return finish_launch();
+    });
     if (rc2 != ZERO_OK) return rc2;
-    clipped_update_kernel<<<grid_for(kClip, n), kBlock, 0, s>>>(grad_buf, n, a, hp->max_grad_norm, ws, grid1);
-    rc2 = finish_launch();
+    rc2 = for_each_piece(n, [&](int64_t off, int64_t k) {
+        clipped_update_kernel<<<grid_for(kClip, k), kBlock, 0, s>>>(grad_buf + off, k, piece_args(a, off),
+                                                                   hp->max_grad_norm, ws, grid1);
+        return finish_launch();
+    });
     if (rc2 != ZERO_OK) return rc2;
     commit_kernel<<<1, kBlock, 0, s>>>(a, ws, grid1, n, hp->max_grad_norm);
     return finish_launch();
@@ -1469,7 +1495,7 @@ int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st, c
     a.window_n = window_n;
     // every bucket of a step runs on the same grid: each workgroup adds its
     // partial to its own slot
-    const int grid = fixed_grid();
+    const int grid = fixed_grid(kFused);
     const Partials ws = make_ws(workspace);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
