@@ -153,7 +153,7 @@ typedef struct zero_grad_src {
 
 /* ---- workspace ----------------------------------------------------------
  * Device scratch for per-workgroup partial results, a completion counter
- * and the element count of a bucketed step.
+ * and the element count of a bucketed or split step.
  * Allocate zero_workspace_bytes() bytes of device memory (16-byte aligned),
  * zero it ONCE before first use, and never share one workspace between calls
  * that may run concurrently (different streams).  Every call leaves it ready
@@ -215,7 +215,7 @@ typedef struct zero_adam_state {
  * Dynamic loss scaling (scale_interval > 0; the practice of the
  * mixed-precision training the anthology note's "Connections" cites): the
  * gradients carry ctl->loss_scale (src->loss_scale is then ignored); after
- * each step the last workgroup multiplies the scale by scale_backoff if the
+ * each step the commit kernel multiplies the scale by scale_backoff if the
  * step overflowed (and resets good_steps), else counts the clean step and
  * multiplies the scale by scale_growth after scale_interval of them.
  *
@@ -279,6 +279,8 @@ int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st,
  *           coef = min(1, max_grad_norm / (sqrt(sumsq) + 1e-6)) and the
  *           update of zero_adam_step runs on g = g32 * coef (float64);
  *   then a one-workgroup commit; ctl->clip_coef records coef.
+ * A window of more than 2^25 elements takes each pass in consecutive
+ * launches of about 2^24 elements, as zero_adam_step does.
  * L is src->loss_scale or, with dynamic scaling, ctl->loss_scale.
  * Traffic (2*Nd + 4) + 30 bytes per element instead of 2*Nd + 26.
  *   grad_buf: device float[n], 16-byte aligned, must not overlap any other
