@@ -294,3 +294,26 @@ def test_other_validation(L):
     assert L.zero_restore_skipped(C.byref(_state(ctl=(1 << 30) + 4)), 8, 1 << 29, 0, None) == B.ZERO_EALIGN
     assert L.zero_restore_skipped(C.byref(st), 64, 1 << 24, 0, None) == B.ZERO_EALIAS   # window on master[0]
     assert L.zero_restore_skipped(C.byref(st), 64, (1 << 30) - 64, 0, None) == B.ZERO_EALIAS  # covers the ctl
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without the built library every entry point raises: there is no
+    fallback path."""
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "_LIB_PATH", os.path.join(ROOT, "_no_such_dir", "libzero_dp.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        B.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        B.plan_partitions([10, 20], 2, 8)
+
+
+def test_product_never_imports_the_oracle():
+    """The package and its C sources name no oracle module; the oracle is
+    test infrastructure."""
+    pkg = os.path.join(ROOT, "zero_partitioned_mixed_buffer_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), fn
+                assert "zero_oracle" not in text, fn
