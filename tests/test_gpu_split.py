@@ -40,16 +40,22 @@ def _sample_idx(n):
     return idx[(idx >= 0) & (idx < n)]
 
 
-def _sumsq(torch, slices):
-    g = slices.to(torch.float64).sum(0) * (1.0 / L)
+def _sumsq(torch, slices, scale=L):
+    g = slices.to(torch.float64).sum(0) * (1.0 / scale)
     return float((g * g).sum().item())
 
 
-def test_long_window_split_launches():
+@pytest.mark.parametrize("dynamic", [False, True])
+def test_long_window_split_launches(dynamic):
+    """With dynamic loss scaling (interval 2, from 4096) the slices carry
+    the control block's scale, and the scale trajectory must match the
+    oracle's exactly."""
     torch = torch_mod()
     from zero_partitioned_mixed_buffer_amd import OwnedShard
     from zero_partitioned_mixed_buffer_amd import binding as B
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    if dynamic:
+        hp.update(scale_interval=2, loss_scale=4096.0)
     master = torch.empty(N, dtype=torch.float32, device="cuda")
     gen.device_fill_params(master, 123, 0.02, N)
     idx = _sample_idx(N)
@@ -67,11 +73,12 @@ def test_long_window_split_launches():
     bucket = 1 << 20
     say(f"n={N} nd={ND}: {idx.size} sampled elements")
     for step in range(1, 4):
-        gen.device_fill_grads(dsl, 77, step, 1e-3, L, "normal", N)
+        scale = ref.scale if dynamic else L  # the scale the slices carry
+        gen.device_fill_grads(dsl, 77, step, 1e-3, scale, "normal", N)
         if step == 2:
             dsl[1, N - 10] = float("inf")  # in the last launch of the split (sampled)
         ovf, _ = ref.step(dsl[:, tidx].cpu().numpy(), L)
-        sq_want = None if ovf else _sumsq(torch, dsl)
+        sq_want = None if ovf else _sumsq(torch, dsl, scale)
         say(f"step {step}: split whole-window step, then {-(-N // bucket)} buckets")
         whole.step(dsl, L, allgather=ag_w, allgather_off=8)
         for o in range(0, N, bucket):
@@ -83,6 +90,9 @@ def test_long_window_split_launches():
         tag = f"step {step}"
         assert cw["overflow"] == cb["overflow"] == int(ovf), tag
         assert cw["t"] == cb["t"] == ref.t and cw["skipped"] == cb["skipped"], tag
+        if dynamic:
+            assert cw["loss_scale"] == cb["loss_scale"] == ref.scale, tag
+            assert cw["good_steps"] == cb["good_steps"] == ref.good_steps, tag
         for a, b in zip(whole.committed(cw), buck.committed(cb)):
             assert torch.equal(a.view(torch.int32), b.view(torch.int32)), tag
         assert torch.equal(ag_w.view(torch.int16), ag_b.view(torch.int16)), tag
@@ -95,6 +105,8 @@ def test_long_window_split_launches():
         bits = ag_w.view(torch.int16)[8 + tidx].cpu().numpy().view(np.uint16)
         assert_fp16_close(bits, ref.window().view(np.uint16), f"{tag} window")
     assert ref.flags == [0, 1, 0] and ref.t == 2
+    if dynamic:
+        assert ref.scales == [4096.0, 4096.0, 2048.0]
 
 
 def _sumsq32(torch, slices):
