@@ -317,3 +317,37 @@ def test_product_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), fn
                 assert "zero_oracle" not in text, fn
+
+
+def test_binding_checks_torch_arguments():
+    """The binding rejects torch tensors whose dtype, layout or extent does
+    not fit the call before anything reaches the library (CPU tensors stop
+    at the device check, which comes last)."""
+    torch = pytest.importorskip("torch")
+    h = torch.zeros((3, 64), dtype=torch.float16)
+    with pytest.raises(ValueError, match="dtype"):
+        B.grad_src(h.float(), 64, 0, 64, 3, 1.0)
+    with pytest.raises(ValueError, match="2-D"):
+        B.grad_src(h[:, ::2], 32, 0, 32, 3, 1.0)
+    with pytest.raises(ValueError, match="rows"):
+        B.grad_src(h, 32, 0, 32, 3, 1.0)  # rows are 64 apart, not 32
+    with pytest.raises(ValueError, match="rows"):
+        B.grad_src(h, 64, 0, 8, 4, 1.0)  # 4 slices asked, 3 held
+    with pytest.raises(ValueError, match="columns"):
+        B.grad_src(h, 64, 8, 64, 3, 1.0)  # past the end of a row
+    with pytest.raises(ValueError, match="device"):
+        B.grad_src(h, 64, 0, 64, 3, 1.0)
+    # a column view of a wider buffer is fine up to the device check: its
+    # rows keep the parent's stride
+    with pytest.raises(ValueError, match="device"):
+        B.grad_src(torch.zeros((3, 80), dtype=torch.float16)[:, 8:72], 80, 0, 64, 3, 1.0)
+    with pytest.raises(ValueError, match="outside"):
+        B.emit_fp16(0x1000, 16, torch.zeros(20, dtype=torch.float16), 8)  # an address passes through
+    with pytest.raises(ValueError, match="dtype"):
+        B.emit_fp16(0x1000, 16, torch.zeros(16, dtype=torch.float32), 0)
+    with pytest.raises(ValueError, match="contiguous"):
+        B.emit_fp16(0x1000, 16, torch.zeros(64, dtype=torch.float16)[::2], 0)
+    with pytest.raises(ValueError, match="dtype"):
+        B.adam_state([torch.zeros(8, dtype=torch.float64), 0x1000], [0x2000] * 2, [0x3000] * 2, 0x4000)
+    with pytest.raises(ValueError, match="parameter window"):
+        B.gather_params([torch.zeros(8, dtype=torch.float16)], 16, 0, 8, 0x1000)

@@ -133,6 +133,46 @@ def _ptr(x) -> Optional[int]:
     return int(x.data_ptr())
 
 
+def _is_tensor(x) -> bool:
+    return x is not None and not isinstance(x, int)
+
+
+_DTYPE_NAMES: dict = {}
+
+
+def _dtype_name(t) -> str:
+    d = t.dtype
+    name = _DTYPE_NAMES.get(d)
+    if name is None:
+        name = _DTYPE_NAMES[d] = str(d).replace("torch.", "")
+    return name
+
+
+def _check_span(t, off: int, n: int, kinds: Tuple[str, ...], what: str):
+    """For a torch tensor argument: dtype one of ``kinds``, elements laid out
+    contiguously, [off, off + n) inside the tensor, on a GPU.  Raw addresses
+    (ints) and None pass through (the library checks what it can)."""
+    if t is None or isinstance(t, int):
+        return
+    if _dtype_name(t) not in kinds:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected one of {kinds}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: tensor must be contiguous")
+    if off < 0 or n < 0 or off + n > t.numel():
+        raise ValueError(f"{what}: elements [{off}, {off + n}) outside a tensor of {t.numel()}")
+    if not t.is_cuda:
+        raise ValueError(f"{what}: must be a device tensor")
+
+
+_F16 = ("float16", "int16")
+
+
+def _check_ws(ws):
+    if ws is not None and not isinstance(ws, int) and (ws.numel() * ws.element_size() < workspace_bytes()
+                                                      or not ws.is_cuda):
+        raise ValueError(f"workspace: a device tensor of at least {workspace_bytes()} bytes")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -165,8 +205,14 @@ def memory_model(psi: float, nd: int, stage: int, k: int = 12) -> dict:
     return {name: getattr(r, name) for name, _ in MemReport._fields_}
 
 
+_ws_bytes: Optional[int] = None
+
+
 def workspace_bytes() -> int:
-    return int(lib().zero_workspace_bytes())
+    global _ws_bytes
+    if _ws_bytes is None:
+        _ws_bytes = int(lib().zero_workspace_bytes())
+    return _ws_bytes
 
 
 def ctl_init_bytes(loss_scale: float = 65536.0) -> bytes:
@@ -185,17 +231,47 @@ CTL_BYTES = C.sizeof(StepCtl)
 
 # ------------------------------------------------------------------ device calls
 def grad_src(base, slice_stride: int, elem_off: int, n: int, nd: int, loss_scale: float) -> GradSrc:
+    """Gradient source: slice k of the window is base[k, elem_off:elem_off+n].
+    A torch ``base`` must be a 2-D fp16 device tensor whose rows are
+    ``slice_stride`` elements apart and that holds the whole window."""
+    if _is_tensor(base):
+        if _dtype_name(base) not in _F16:
+            raise ValueError(f"gradient slices: dtype {base.dtype}, expected float16")
+        if base.dim() != 2 or base.stride(1) != 1:
+            raise ValueError("gradient slices: a 2-D tensor [Nd, stride] with unit element stride")
+        if base.shape[0] < nd or (nd > 1 and base.stride(0) != slice_stride):
+            raise ValueError(f"gradient slices: {base.shape[0]} rows {base.stride(0)} apart, "
+                             f"expected {nd} rows {slice_stride} apart")
+        if elem_off < 0 or n < 0 or elem_off + n > base.shape[1]:
+            raise ValueError(f"gradient slices: columns [{elem_off}, {elem_off + n}) outside {base.shape[1]}")
+        if not base.is_cuda:
+            raise ValueError("gradient slices: must be a device tensor")
     return GradSrc(_ptr(base), int(slice_stride), int(elem_off), int(n), int(nd), 0, float(loss_scale))
 
 
 def adam_state(master: Sequence, exp_avg: Sequence, exp_avg_sq: Sequence, ctl) -> AdamState:
+    """Ping-pong state; with torch tensors, each a contiguous fp32 device
+    array, and the steps then check that the window fits in all six."""
     s = AdamState()
+    arrays = [*master, *exp_avg, *exp_avg_sq]
+    for a in arrays:
+        _check_span(a, 0, 0, ("float32",), "state array")
     for i in range(2):
         s.master[i] = _ptr(master[i])
         s.exp_avg[i] = _ptr(exp_avg[i])
         s.exp_avg_sq[i] = _ptr(exp_avg_sq[i])
+    if _is_tensor(ctl) and (ctl.numel() * ctl.element_size() < CTL_BYTES or not ctl.is_cuda):
+        raise ValueError(f"control block: a device tensor of at least {CTL_BYTES} bytes")
     s.ctl = _ptr(ctl)
+    if all(_is_tensor(a) for a in arrays):
+        s._numel = min(int(a.numel()) for a in arrays)
     return s
+
+
+def _check_state(state: AdamState, n: int):
+    cap = getattr(state, "_numel", None)
+    if cap is not None and n > cap:
+        raise ValueError(f"state arrays of {cap} elements cannot hold a window of {n}")
 
 
 def adam_hp(lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
@@ -206,18 +282,29 @@ def adam_hp(lr: float, beta1: float, beta2: float, eps: float, weight_decay: flo
 
 
 def reduce_owned(src: GradSrc, grad_out, overflow, sumsq, workspace, stream=None):
+    _check_span(grad_out, 0, src.n, ("float32",), "gradient output")
+    _check_span(overflow, 0, 1, ("int32",), "overflow flag")
+    _check_span(sumsq, 0, 1, ("float64",), "sum of squares")
+    _check_ws(workspace)
     _check(lib().zero_reduce_owned(C.byref(src), _ptr(grad_out), _ptr(overflow), _ptr(sumsq),
                                    _ptr(workspace), _stream(stream)), "zero_reduce_owned")
 
 
 def adam_step(src: GradSrc, state: AdamState, hp: AdamHp, allgather, allgather_off: int, workspace,
               stream=None):
+    _check_state(state, src.n)
+    _check_span(allgather, allgather_off, src.n, _F16, "all-gather buffer")
+    _check_ws(workspace)
     _check(lib().zero_adam_step(C.byref(src), C.byref(state), C.byref(hp), _ptr(allgather),
                                 int(allgather_off), _ptr(workspace), _stream(stream)), "zero_adam_step")
 
 
 def adam_step_clipped(src: GradSrc, state: AdamState, hp: AdamHp, grad_buf, allgather, allgather_off: int,
                       workspace, stream=None):
+    _check_state(state, src.n)
+    _check_span(grad_buf, 0, src.n, ("float32",), "gradient buffer")
+    _check_span(allgather, allgather_off, src.n, _F16, "all-gather buffer")
+    _check_ws(workspace)
     _check(lib().zero_adam_step_clipped(C.byref(src), C.byref(state), C.byref(hp), _ptr(grad_buf),
                                         _ptr(allgather), int(allgather_off), _ptr(workspace), _stream(stream)),
            "zero_adam_step_clipped")
@@ -225,17 +312,24 @@ def adam_step_clipped(src: GradSrc, state: AdamState, hp: AdamHp, grad_buf, allg
 
 def adam_step_bucket(src: GradSrc, state: AdamState, hp: AdamHp, win_off: int, window_n: int, allgather,
                      allgather_off: int, phase: int, workspace, stream=None):
+    _check_state(state, window_n)
+    _check_span(allgather, allgather_off, window_n, _F16, "all-gather buffer")
+    _check_ws(workspace)
     _check(lib().zero_adam_step_bucket(C.byref(src), C.byref(state), C.byref(hp), int(win_off), int(window_n),
                                        _ptr(allgather), int(allgather_off), int(phase), _ptr(workspace),
                                        _stream(stream)), "zero_adam_step_bucket")
 
 
 def restore_skipped(state: AdamState, n: int, allgather, allgather_off: int, stream=None):
+    _check_state(state, n)
+    _check_span(allgather, allgather_off, n, _F16, "all-gather buffer")
     _check(lib().zero_restore_skipped(C.byref(state), int(n), _ptr(allgather), int(allgather_off),
                                       _stream(stream)), "zero_restore_skipped")
 
 
 def emit_fp16(master, n: int, allgather, allgather_off: int, stream=None):
+    _check_span(master, 0, n, ("float32",), "master")
+    _check_span(allgather, allgather_off, n, _F16, "all-gather buffer")
     _check(lib().zero_emit_fp16(_ptr(master), int(n), _ptr(allgather), int(allgather_off),
                                 _stream(stream)), "zero_emit_fp16")
 
@@ -243,6 +337,10 @@ def emit_fp16(master, n: int, allgather, allgather_off: int, stream=None):
 def gather_params(windows: Sequence, part: int, lo: int, hi: int, dst, stream=None):
     """Flat elements [lo, hi) of the partitioned fp16 parameters into dst;
     ``windows`` lists the Nd owners' windows (tensors, addresses or None)."""
+    if part > 0 and hi > lo:  # the windows the range touches (the library rejects a null one)
+        for w in windows[max(lo, 0) // part:min((hi - 1) // part + 1, len(windows))]:
+            _check_span(w, 0, part, _F16, "parameter window")
+    _check_span(dst, 0, max(hi - lo, 0), _F16, "layer buffer")
     arr = (C.c_void_p * max(len(windows), 1))(*[_ptr(w) for w in windows])
     _check(lib().zero_gather_params(arr, len(windows), int(part), int(lo), int(hi), _ptr(dst), _stream(stream)),
            "zero_gather_params")

@@ -43,7 +43,7 @@ class OwnedShard:
         columns [elem_off, elem_off + n) are the owned window.  With dynamic
         loss scaling the slices carry the control block's scale and
         ``loss_scale`` is ignored."""
-        nd, stride = slices.shape
+        nd, stride = slices.shape[0], slices.stride(0)
         src = B.grad_src(slices, stride, elem_off, self.n, nd, loss_scale)
         if self.clipped:
             # a skipped clipped step leaves the all-gather window untouched
@@ -61,7 +61,7 @@ class OwnedShard:
         commits the step (restoring the all-gather window if it is skipped)."""
         if self.clipped:
             raise ValueError("a bucketed step cannot clip (the norm is needed before any bucket)")
-        nd, stride = slices.shape
+        nd, stride = slices.shape[0], slices.stride(0)
         src = B.grad_src(slices, stride, elem_off, n, nd, loss_scale)
         B.adam_step_bucket(src, self.state, self.hp, win_off, self.n, allgather, allgather_off, phase,
                            self.workspace, stream)
