@@ -322,3 +322,28 @@ def test_state_canaries():
         tail = t[n:].cpu().numpy()
         assert np.all(tail == np.float32(canary)), f"array {k} written past its end"
     assert not torch.count_nonzero(ag[n:].view(torch.int16)).item()
+
+
+def test_column_view_of_wider_slice_buffer():
+    """Slices passed as a column view of a wider [Nd, W] buffer: the step
+    reads the view's rows W elements apart (the tensor's row stride), not
+    its width."""
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import OwnedShard
+    n, nd, width = 5000, 5, 5024
+    g = np.random.default_rng(29)
+    master0 = (g.standard_normal(n) * 0.02).astype(F32)
+    ref = oracle.OwnedShard(master0)
+    sh = OwnedShard(torch.from_numpy(master0).cuda())
+    wide = torch.full((nd, width), 3.0, dtype=torch.float16, device="cuda")
+    for step in (1, 2):
+        sl = gen.host_grad_slices(29, step, 0, nd, n, 0, n, 1e-3, 1024.0)
+        wide[:, 8:8 + n] = torch.from_numpy(sl).cuda()
+        ref.step(sl, 1024.0)
+        sh.step(wide[:, 8:8 + n], 1024.0)
+        torch.cuda.synchronize()
+        ctl = sh.control()
+        assert ctl["t"] == ref.t == step and ctl["overflow"] == 0
+        p, m, v = (x.cpu().numpy() for x in sh.committed(ctl))
+        for a, b, nm in ((p, ref.p, "p"), (m, ref.m, "m"), (v, ref.v, "v")):
+            assert_state_close(a, b, f"column view step {step} {nm}")
