@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--gather-layers", action="store_true",
                     help="time the Pos+g+p on-demand gather of every layer (GPT-2 shaped workloads) "
                          "instead of the step")
+    ap.add_argument("--gather-streams", type=int, default=1, choices=(1, 2),
+                    help="with --gather-layers: 2 alternates the layers between two streams (layer buffer "
+                         "k %% 2 on stream k %% 2), so one layer's gather overlaps the next one's launch")
     a = ap.parse_args()
     if a.bucket_elems < 0 or a.bucket_elems % 8 or (a.bucket_elems and a.max_grad_norm > 0):
         ap.error("--bucket-elems must be a multiple of 8, and cannot be combined with clipping")
@@ -125,14 +128,17 @@ def calibration_copy(torch, dev):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(w, n_sample, budget_s):
-    """The oracle, as it stands, on a bounded sample of the workload's window."""
+def cpu_baseline(w, n_sample, budget_s, max_grad_norm=0.0, scale_interval=0):
+    """The oracle, as it stands, on a bounded sample of the workload's window
+    (the clipped or dynamically scaled step when the timed step is; a
+    bucketed step computes what the whole-window step computes)."""
     import numpy as np
     import oracle
     from workloads import gen
     master = gen.host_params(w.seed, w.psi, 0, n_sample, w.param_sigma)
     sh = oracle.OwnedShard(master, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
-                           weight_decay=w.weight_decay)
+                           weight_decay=w.weight_decay, max_grad_norm=max_grad_norm,
+                           scale_interval=scale_interval, loss_scale=w.loss_scale)
     grads = [gen.host_grad_slices(w.seed, s, 0, w.nd, n_sample, 0, w.psi, w.grad_sigma, w.loss_scale,
                                   w.dist) for s in (1, 2)]
     steps = 0
@@ -146,8 +152,28 @@ def cpu_baseline(w, n_sample, budget_s):
     rate = n_sample * steps / el
     return {"value": rate, "unit": "elements/s", "cores": 1, "kind": "oracle",
             "sample": f"{steps} oracle steps over a {n_sample}-element window of workload {w.key} "
-                      f"(Nd={w.nd}, numpy float64, one thread), {el:.1f} s",
+                      f"(Nd={w.nd}, numpy float64, one thread"
+                      f"{', clipped' if max_grad_norm > 0 else ''}"
+                      f"{', dynamic loss scale' if scale_interval > 0 else ''}), {el:.1f} s",
             "gbs": rate * (2 * w.nd + 26) / 1e9}
+
+
+def cpu_baseline_gather(w, windows, part, ranges, budget_s):
+    """oracle.gather, as it stands, over every layer of the workload from
+    host copies of one set of the windows, repeated for about budget_s."""
+    import oracle
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        for lo, hi in ranges:
+            oracle.gather(windows, part, lo, hi)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": w.psi * passes / el, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} oracle gather passes over every layer of workload {w.key} "
+                      f"({len(ranges)} layers, Psi = {w.psi}, numpy, one thread), {el:.1f} s"}
 
 
 def bench_gather(args):
@@ -182,13 +208,15 @@ def bench_gather(args):
     biggest = max(hi - lo for lo, hi in ranges)
     bufs = [torch.empty(biggest, dtype=torch.float16, device=dev) for _ in range(2)]
     stream = torch.cuda.current_stream()
+    # layer buffer b is only ever written on streams[b], so reuse is ordered
+    streams = [stream, torch.cuda.Stream()] if args.gather_streams == 2 else [stream, stream]
     log(f"gather: {w.key}, {len(ranges)} layers (largest {biggest} elements), Nd={w.nd} windows of {part}, "
-        f"{copies} window set(s)")
+        f"{copies} window set(s), {args.gather_streams} stream(s)")
 
     def one_pass(i):
         ws = sets[i % copies]
         for k, (lo, hi) in enumerate(ranges):
-            B.gather_params(ws, part, lo, hi, bufs[k % 2], stream)
+            B.gather_params(ws, part, lo, hi, bufs[k % 2], streams[k % 2])
 
     for i in range(args.warmup):
         one_pass(i)
@@ -196,8 +224,13 @@ def bench_gather(args):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
+    streams[1].wait_event(e0)
     for i in range(args.steps):
         one_pass(args.warmup + i)
+    if streams[1] is not stream:
+        done = torch.cuda.Event()
+        done.record(streams[1])
+        stream.wait_event(done)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -206,6 +239,10 @@ def bench_gather(args):
     launches = sum(-(-(1 + (hi - 1) // part - lo // part) // 16) for lo, hi in ranges if hi > lo)
     gbs = 4 * w.psi / (ms * 1e-3) / 1e9
     log(f"gather pass: {ms * 1e3:.1f} us ({launches} launches, {pieces} window pieces), {gbs:.0f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_gather(w, [t.cpu().numpy() for t in sets[0]], part, ranges, args.cpu_seconds)
+        log(f"oracle: {cpu['value']:.3e} elements/s on 1 core")
     out = {
         "metric": "parameter elements gathered/sec (Pos+g+p on-demand layer gather), 1 MI355X",
         "value": w.psi / (ms * 1e-3),
@@ -216,13 +253,13 @@ def bench_gather(args):
         "data": "synthetic",
         "config": {"workload": f"{w.key}: every layer of {w.title}", "layers": len(ranges),
                    "largest_layer": biggest, "nd": w.nd, "window": part, "launches_per_pass": launches,
-                   "window_pieces_per_pass": pieces,
+                   "window_pieces_per_pass": pieces, "streams": args.gather_streams,
                    "window_sets_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": None,
                      "algorithmic_bytes_per_pass": 4 * w.psi, "kernel": "copy_f16_kernel",
                      "kernel_fingerprint": kernel_fingerprint()},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
@@ -395,7 +432,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         n_sample = min(S, 1 << 21) if w.nd <= 64 else min(S, 1 << 16)
-        cpu = cpu_baseline(w, n_sample, args.cpu_seconds)
+        cpu = cpu_baseline(w, n_sample, args.cpu_seconds, args.max_grad_norm, args.dynamic_scale)
         log(f"oracle: {cpu['value']:.3e} elements/s on 1 core")
 
     out = {
