@@ -347,3 +347,33 @@ def test_column_view_of_wider_slice_buffer():
         p, m, v = (x.cpu().numpy() for x in sh.committed(ctl))
         for a, b, nm in ((p, ref.p, "p"), (m, ref.m, "m"), (v, ref.v, "v")):
             assert_state_close(a, b, f"column view step {step} {nm}")
+
+
+def test_restore_skipped_second_window():
+    """zero_restore_skipped re-derives another copy of the window from the
+    committed master after a skipped step, and leaves it alone after a
+    clean one."""
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    from gpu_util import SENTINEL
+    n, nd = 20011, 3
+    g = np.random.default_rng(31)
+    master0 = (g.standard_normal(n) * 0.02).astype(F32)
+    ref = oracle.OwnedShard(master0)
+    run = GpuShardRun(master0, nd, {})
+    other = torch.full((n + 16,), SENTINEL, dtype=torch.int16, device="cuda")
+    for step in (1, 2):
+        sl = gen.host_grad_slices(31, step, 0, nd, n, 0, n, 1e-3, 1024.0)
+        if step == 2:
+            sl[1, n // 3] = np.nan
+        ovf, _ = ref.step(sl, 1024.0)
+        ctl = run.step(sl, 1024.0)[0]
+        assert ctl["overflow"] == int(ovf) == (step == 2)
+        B.restore_skipped(run.shard.state, n, other, 8)
+        torch.cuda.synchronize()
+        bits = other.cpu().numpy().view(np.uint16)
+        if step == 1:
+            assert np.all(bits == SENTINEL)  # clean step: nothing written
+        else:
+            assert_fp16_close(bits[8:8 + n], ref.window().view(np.uint16), "restored window")
+            assert np.all(bits[:8] == SENTINEL) and np.all(bits[8 + n:] == SENTINEL)
