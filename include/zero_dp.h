@@ -30,7 +30,9 @@
  *     on `stream` (a hipStream_t; NULL = the legacy default stream) and
  *     return without synchronising.  Results are valid once the stream has
  *     reached them.  On a non-OK return nothing was enqueued, except for
- *     ZERO_EHIP, which reports a failed launch (see zero_last_hip_error).
+ *     ZERO_EHIP, which reports a failed launch (see zero_last_hip_error);
+ *     launches of the same call before the failed one may have been
+ *     enqueued, and the step must then be treated as not taken.
  *   - The library allocates nothing and only borrows the caller's buffers for
  *     the duration of the enqueued work.  Its only mutable state is a
  *     per-device cache of launch sizes (filled once, thread-safe) and the
