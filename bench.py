@@ -54,6 +54,8 @@ def parse():
                     help="bucketed step: copy each bucket into one of two constant-size receive "
                          "buffers on a side stream (the simulated reduce-scatter arrival), "
                          "overlapped with the previous bucket's step")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the same steps replayed from a HIP graph (reported as config.graph_step_us)")
     ap.add_argument("--gather-layers", action="store_true",
                     help="time the Pos+g+p on-demand gather of every layer (GPT-2 shaped workloads) "
                          "instead of the step")
@@ -363,18 +365,19 @@ def main():
             if args.arrival:
                 consumed[r].record(stream)
 
-    def launch(i):
+    def launch(i, s=None):
         sh = shards[i % n_shards]
+        s = s or stream
         if bucketed:
             launch_bucketed(i)
             return
         if clipped:  # two passes; a skipped step leaves the window untouched
             B.adam_step_clipped(srcs[i % rot], sh.state, sh.hp, sh.grad_buf, ag, ag_offs[i % n_shards],
-                                sh.workspace, stream)
+                                sh.workspace, s)
             return
         # the fused kernel and the commit kernel (which also re-emits the
         # window of a skipped step)
-        B.adam_step(srcs[i % rot], sh.state, sh.hp, ag, ag_offs[i % n_shards], sh.workspace, stream)
+        B.adam_step(srcs[i % rot], sh.state, sh.hp, ag, ag_offs[i % n_shards], sh.workspace, s)
 
     for i in range(args.warmup):
         launch(i)
@@ -413,6 +416,28 @@ def main():
     if sum(c["t"] for c in ctls) != args.warmup + 3 * args.steps or any(c["skipped"] for c in ctls):
         log(f"unexpected control state after timing: {ctls}")
         sys.exit(1)
+
+    graph_us = None
+    if args.graph and not bucketed:
+        # the same K steps captured once in a HIP graph and replayed: the
+        # launches are identical, only the host-side launch cost goes
+        base = args.warmup + 3 * args.steps
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for j in range(args.steps):
+                launch(base + j, torch.cuda.current_stream())
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(3):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = g0.elapsed_time(g1) * 1e3 / (3 * args.steps)
+        log(f"the same steps from a HIP graph: {graph_us:.1f} us per step")
+        del graph
 
     calibration_copy(torch, dev)
     attain = attainable_copy(torch, dev, B)
@@ -462,6 +487,7 @@ def main():
             "dynamic_scale_interval": args.dynamic_scale,
             "bucket_elems": args.bucket_elems,
             "bucket_arrival_copies": bool(args.arrival),
+            "graph_step_us": graph_us,
         },
         "roofline": {
             "bound": "hbm",
