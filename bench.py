@@ -345,7 +345,7 @@ def main():
             + ("; arrival copies into 2 constant-size receive buffers on a side stream" if args.arrival else
                "; buckets read in place"))
 
-    def launch_bucketed(i):
+    def launch_bucketed(i, s):
         sh = shards[i % n_shards]
         gs = gsets[i % rot]
         for b, (o, k) in enumerate(buckets):
@@ -360,8 +360,7 @@ def main():
                 src = B.grad_src(recv[r], nb_elems, 0, k, w.nd, w.loss_scale)
             else:
                 src = B.grad_src(gs, S, o, k, w.nd, w.loss_scale)
-            B.adam_step_bucket(src, sh.state, sh.hp, o, S, ag, ag_offs[i % n_shards], phase, sh.workspace,
-                               stream)
+            B.adam_step_bucket(src, sh.state, sh.hp, o, S, ag, ag_offs[i % n_shards], phase, sh.workspace, s)
             if args.arrival:
                 consumed[r].record(stream)
 
@@ -369,7 +368,7 @@ def main():
         sh = shards[i % n_shards]
         s = s or stream
         if bucketed:
-            launch_bucketed(i)
+            launch_bucketed(i, s)
             return
         if clipped:  # two passes; a skipped step leaves the window untouched
             B.adam_step_clipped(srcs[i % rot], sh.state, sh.hp, sh.grad_buf, ag, ag_offs[i % n_shards],
@@ -418,7 +417,7 @@ def main():
         sys.exit(1)
 
     graph_us = None
-    if args.graph and not bucketed:
+    if args.graph and not args.arrival:
         # the same K steps captured once in a HIP graph and replayed: the
         # launches are identical, only the host-side launch cost goes
         base = args.warmup + 3 * args.steps
