@@ -377,3 +377,20 @@ def test_restore_skipped_second_window():
         else:
             assert_fp16_close(bits[8:8 + n], ref.window().view(np.uint16), "restored window")
             assert np.all(bits[:8] == SENTINEL) and np.all(bits[8 + n:] == SENTINEL)
+
+
+def test_largest_nd():
+    """Nd = 8191, the largest the library accepts (float64 holds the sum of
+    fewer than 2^13 fp16 values exactly): 511 full chunks of 16 slices and a
+    remainder of 15.  One element carries 65504 in every slice (the largest
+    finite fp16, sum 8191 * 65504), another alternating +-65504 (sum 65504);
+    the step must match the oracle and stay finite."""
+    nd, n = 8191, 1001
+
+    def mutate(step, sl):
+        sl[:, 5] = np.float16(65504.0)
+        sl[:, 6] = np.where(np.arange(nd) % 2 == 0, np.float16(65504.0), np.float16(-65504.0))
+        return sl
+
+    sh, _, _ = _run_case(n, nd, 2, 83, L=65536.0, sigma=1e-4, mutate=mutate)
+    assert sh.flags == [0, 0]
