@@ -151,7 +151,7 @@ def _sample_idx(S, n=1 << 16, extra=()):
     return idx[(idx >= 0) & (idx < S)]
 
 
-def _sampled_run(w, owner=0, inject=None, clip=0.0, bucket=0, steps=None):
+def _sampled_run(w, owner=0, inject=None, clip=0.0, bucket=0, steps=None, interval=0):
     """Steps the workload's window on the device (whole-window fused step,
     clipped step with max_grad_norm = clip, or buckets of `bucket` elements
     read in place) and the oracle on sampled elements.  With clipping the
@@ -159,11 +159,13 @@ def _sampled_run(w, owner=0, inject=None, clip=0.0, bucket=0, steps=None):
     slices."""
     torch, B, plan, S, valid = _setup(w, owner)
     from zero_partitioned_mixed_buffer_amd import OwnedShard
-    idx = _sample_idx(S)
+    idx = _sample_idx(S, extra=(inject[2],) if inject else ())
     tidx = torch.from_numpy(idx).cuda()
     master = torch.empty(S, dtype=torch.float32, device="cuda")
     gen.device_fill_params(master, w.seed + owner, w.param_sigma, valid)
     hp = dict(_hp(w), max_grad_norm=clip)
+    if interval:  # dynamic loss scaling from the workload's scale
+        hp.update(scale_interval=interval, loss_scale=w.loss_scale)
     ref = oracle.OwnedShard(master[tidx].cpu().numpy(), **hp)
     sh = OwnedShard(master, **hp)
     del master
@@ -174,17 +176,18 @@ def _sampled_run(w, owner=0, inject=None, clip=0.0, bucket=0, steps=None):
     flags = []
     for step in range(1, (steps or w.steps) + 1):
         say(f"{w.key} step {step}: filling {2 * w.nd * S / 1e9:.1f} GB of slices")
-        gen.device_fill_grads(dsl, w.seed, step, w.grad_sigma, w.loss_scale, w.dist, valid)
+        L = ref.scale if interval else w.loss_scale  # the scale the slices carry
+        gen.device_fill_grads(dsl, w.seed, step, w.grad_sigma, L, w.dist, valid)
         if inject is not None and inject[0] == step:
             dsl[inject[1], inject[2]] = float("inf")
         injected = inject is not None and inject[0] == step
-        sq32 = _sumsq32_torch(torch, dsl, w.loss_scale) if (clip and not injected) else None
+        sq32 = _sumsq32_torch(torch, dsl, L) if (clip and not injected) else None
         ovf, _ = ref.step(dsl[:, tidx].cpu().numpy(), w.loss_scale, window_sumsq=sq32)
         if ovf or injected:
             prev = [x.clone() for x in sh.committed()]
             prev_ag = ag.clone()
         else:
-            sq_want = sq32 if clip else _sumsq_torch(torch, dsl, w.loss_scale)
+            sq_want = sq32 if clip else _sumsq_torch(torch, dsl, L)
         if bucket:
             say(f"{w.key} step {step}: {-(-S // bucket)} buckets of {bucket}")
             for o in range(0, S, bucket):
@@ -198,6 +201,8 @@ def _sampled_run(w, owner=0, inject=None, clip=0.0, bucket=0, steps=None):
         ctl = sh.control()
         flags.append(ctl["overflow"])
         assert ctl["overflow"] == int(ovf) and ctl["t"] == ref.t
+        if interval:
+            assert ctl["loss_scale"] == ref.scale and ctl["good_steps"] == ref.good_steps
         if ctl["overflow"]:
             # skipped: committed state and all-gather window bit-identical
             for a, b in zip(prev, sh.committed(ctl)):
@@ -309,3 +314,14 @@ def test_c5_clipped_overflow_sampled():
     flags, ref = _sampled_run(w, inject=(2, 17, S // 2), clip=1.0, steps=3)
     assert flags == [0, 1, 0] and ref.t == 2
     assert all(c < 1.0 for c in ref.coefs if c == c)
+
+
+def test_c3_dynamic_scale_overflow_sampled():
+    """GPT-2-XL shaped list, AdamW, dynamic loss scaling (interval 2, from
+    4096), +inf at step 2 in slice 5: the scale backs off to 2048 and grows
+    back to 4096 after two clean steps; 5 steps, sampled, the window split
+    into launches."""
+    w = configs.C3
+    flags, ref = _sampled_run(w, inject=(2, 5, 12345), interval=2)
+    assert flags == [0, 1, 0, 0, 0] and ref.t == 4
+    assert ref.scales == [4096.0, 4096.0, 2048.0, 2048.0, 4096.0]
