@@ -65,6 +65,21 @@ def test_fused_step_every_nd_many_groups_per_lane(nd):
     _run_case(n, nd, steps=2, seed=300 + nd)
 
 
+# Windows for the chunked sum past 16 slices, where one wave's visit covers 4
+# (Nd < 48) or 8 (Nd >= 48) consecutive 256-element groups, so one pass of
+# the 1024 waves covers 2^20 or 2^21 elements.  Each window runs past one
+# full pass (or stops short of it), ends in a partial visit and a ragged
+# group, and the slice counts take both chunk loops (Nd a multiple of the
+# two-slice chunk, or one slice left over) on both sides of Nd = 48.
+CHUNKED_CASES = [(17, 2**20 + 3 * 256 + 5), (18, 2**20 + 3 * 256 + 5), (47, 300001), (48, 2**21 + 2053),
+                 (64, 2**21 + 2053), (99, 600003)]
+
+
+@pytest.mark.parametrize("nd,n", CHUNKED_CASES)
+def test_fused_step_chunked_visits(nd, n):
+    _run_case(n, nd, steps=2, seed=500 + nd)
+
+
 @pytest.mark.parametrize("nd", [4, 8, 64])
 def test_fused_step_adamw_many_steps(nd):
     hp = dict(HP, weight_decay=0.01)
@@ -133,16 +148,12 @@ def test_overflow_window_restored_bitwise():
     assert np.array_equal(bits1, bits2)
 
 
-@pytest.mark.parametrize("nd", list(range(1, 18)))
-def test_reduce_owned_every_nd_many_groups_per_lane(nd):
-    """The reduce pass for every slice count of its compile-time paths (two
-    groups ahead up to Nd = 8, one ahead to 16, chunked past 16), with 6 or
-    7 element groups per lane and a ragged tail: fp32 g bit-exact, flag
-    exact, sum of g^2 within 1e-12."""
+def _reduce_case(nd, n, seed):
+    """The reduce pass against the oracle: fp32 g bit-exact, flag exact,
+    sum of g^2 within 1e-12, nothing written past the window."""
     torch = torch_mod()
     from zero_partitioned_mixed_buffer_amd import binding as B
-    n = 4 * 65536 * 6 + 4 * 1000 + 3
-    sl = gen.host_grad_slices(400 + nd, 1, 0, nd, n, 0, n, 1e-3, 1024.0)
+    sl = gen.host_grad_slices(seed, 1, 0, nd, n, 0, n, 1e-3, 1024.0)
     s = oracle.reduce_owned(sl)
     gg, ovf, sq = oracle.unscale(s, 1024.0)
     stride = (n + 7) // 8 * 8
@@ -159,6 +170,20 @@ def test_reduce_owned_every_nd_many_groups_per_lane(nd):
     assert np.array_equal(got[:n].view(np.uint32), gg.astype(F32).view(np.uint32))
     assert np.all(got[n:] == 123.0)  # nothing written past the window
     assert float(ssq.item()) == pytest.approx(sq, rel=1e-12)
+
+
+@pytest.mark.parametrize("nd", list(range(1, 18)))
+def test_reduce_owned_every_nd_many_groups_per_lane(nd):
+    """The reduce pass for every slice count of its compile-time paths (two
+    groups ahead up to Nd = 8, one ahead to 16, chunked past 16), with 6 or
+    7 element groups per lane and a ragged tail."""
+    _reduce_case(nd, 4 * 65536 * 6 + 4 * 1000 + 3, 400 + nd)
+
+
+@pytest.mark.parametrize("nd,n", CHUNKED_CASES)
+def test_reduce_owned_chunked_visits(nd, n):
+    """The reduce pass on the chunked-sum windows of the fused step's test."""
+    _reduce_case(nd, n, 600 + nd)
 
 
 def test_reduce_owned_parity():

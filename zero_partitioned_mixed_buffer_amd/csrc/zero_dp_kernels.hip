@@ -100,7 +100,7 @@ __device__ __forceinline__ hvec pack_v(const float (&x)[kV]) {
 
 // Tuning knobs (compile-time; the defaults are the measured best on gfx950).
 #ifndef ZDP_UNROLL
-#define ZDP_UNROLL 16  // slice loads issued together per chunk
+#define ZDP_UNROLL 16  // Nd up to which a group's slice loads are all issued together
 #endif
 #ifndef ZDP_NT_LOAD
 #define ZDP_NT_LOAD 1  // streaming (non-temporal) loads of slices and state
@@ -144,56 +144,7 @@ __device__ __forceinline__ void stg(T* p, const T& v) {
 
 __device__ __forceinline__ hvec ldh(const uint16_t* p) { return ldg(reinterpret_cast<const hvec*>(p)); }
 
-// R slices k0 .. k0+R-1 of 8 consecutive window elements: all R loads are
-// issued before the first add, so R x 16 bytes per lane are in flight.  The
-// first chunk initialises the sums from slice 0 (s = G_0 + G_1 + ...).
-template <int R, bool kFirst>
-__device__ __forceinline__ void sum_chunk(double (&acc)[kV], const uint16_t* p, int64_t stride, int k0) {
-    hvec w[R];
-#pragma unroll
-    for (int u = 0; u < R; ++u) w[u] = ldh(p + static_cast<int64_t>(k0 + u) * stride);
-    // keep the scheduler from interleaving the adds with the loads (left to
-    // itself it serialises half of them behind full vmcnt waits)
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kFirst) {
-        init_v(acc, w[0]);
-#pragma unroll
-        for (int u = 1; u < R; ++u) add_v(acc, w[u]);
-    } else {
-#pragma unroll
-        for (int u = 0; u < R; ++u) add_v(acc, w[u]);
-    }
-}
-
-// Chunk of r < U slices (r uniform across the workgroup), dispatched to a
-// compile-time size.
-template <int R, bool kFirst>
-__device__ __forceinline__ void sum_rem(double (&acc)[kV], const uint16_t* p, int64_t stride, int k0,
-                                        int r) {
-    if constexpr (R >= 1) {
-        if (r == R) {
-            sum_chunk<R, kFirst>(acc, p, stride, k0);
-            return;
-        }
-        sum_rem<R - 1, kFirst>(acc, p, stride, k0, r);
-    }
-}
-
-// Nd-way sum of kV consecutive window elements starting at `p` (slice 0);
-// slice k is at p + k*stride.  Slices are added in index order.
-template <int U>
-__device__ __forceinline__ void sum_slices(double (&acc)[kV], const uint16_t* p, int64_t stride,
-                                            int nd) {
-    if (nd >= U) {
-        sum_chunk<U, true>(acc, p, stride, 0);
-        int k = U;
-        for (; k + U <= nd; k += U) sum_chunk<U, false>(acc, p, stride, k);
-        if (k < nd) sum_rem<U - 1, false>(acc, p, stride, k, nd - k);
-    } else {
-        sum_rem<U - 1, true>(acc, p, stride, 0, nd);
-    }
-}
-
+// Nd-way sum of one window element, slices in index order (ragged tails).
 __device__ __forceinline__ double sum_slices1(const uint16_t* p, int64_t stride, int nd) {
     double s = static_cast<double>(static_cast<float>(*reinterpret_cast<const _Float16*>(p)));
     for (int k = 1; k < nd; ++k)
@@ -401,6 +352,159 @@ __device__ void reduce_tail(int64_t j, const SrcArgs& src, float* grad_out, doub
     }
 }
 
+// Shapes of the chunked sum (Nd > kUnroll): U 256-element sub-groups per
+// wave visit, R slices per chunk, PIPE = the next chunk's loads issued
+// before this chunk's adds, XP = also across visits (when Nd is a multiple
+// of R).  Windows with Nd >= ZDP_CH_BIG_ND take the "big" shape.  Measured
+// in pairs on one box against one 256-element group per visit and chunks of
+// 16 (5.9 TB/s of slice reads at Nd = 64): the big shape is 6-11% faster
+// for Nd 48-400, the small one 2-5% for Nd 17-32.
+#ifndef ZDP_CH_BIG_ND
+#define ZDP_CH_BIG_ND 48
+#endif
+#ifndef ZDP_CHB_U
+#define ZDP_CHB_U 8
+#endif
+#ifndef ZDP_CHB_R
+#define ZDP_CHB_R 2
+#endif
+#ifndef ZDP_CHB_PIPE
+#define ZDP_CHB_PIPE 1
+#endif
+#ifndef ZDP_CHB_XP
+#define ZDP_CHB_XP 0
+#endif
+#ifndef ZDP_CHS_U
+#define ZDP_CHS_U 4
+#endif
+#ifndef ZDP_CHS_R
+#define ZDP_CHS_R 2
+#endif
+#ifndef ZDP_CHS_PIPE
+#define ZDP_CHS_PIPE 1
+#endif
+#ifndef ZDP_CHS_XP
+#define ZDP_CHS_XP 1
+#endif
+static_assert(ZDP_CHB_R >= 1 && ZDP_CHB_R <= ZDP_UNROLL && ZDP_CHS_R >= 1 && ZDP_CHS_R <= ZDP_UNROLL,
+              "the chunked path runs only for Nd > ZDP_UNROLL");
+
+// Chunked sum for Nd > kUnroll.  A wave visits U consecutive 256-element
+// sub-groups at a time (lane l holds elements 4l .. 4l+3 of each), so one
+// load instruction per slice and sub-group covers a contiguous 512 B, and a
+// chunk of R slices puts R*U of them in flight.  A scheduling barrier sits
+// between a chunk's loads and its adds: left to itself the scheduler
+// interleaves them and serialises half the loads behind full vmcnt waits.
+template <int U, int R>
+__device__ __forceinline__ void chu_load(hvec (&w)[R][U], const int64_t (&j)[U], const uint16_t* win,
+                                         int64_t stride, int k0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int u = 0; u < U; ++u) w[r][u] = ldh(win + j[u] + static_cast<int64_t>(k0 + r) * stride);
+}
+
+// Adds a chunk in slice order; the first chunk starts the sums from slice 0.
+template <int U, int R, bool kFirst>
+__device__ __forceinline__ void chu_add(double (&acc)[U][kV], const hvec (&w)[R][U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if constexpr (kFirst)
+            init_v(acc[u], w[0][u]);
+        else
+            add_v(acc[u], w[0][u]);
+#pragma unroll
+        for (int r = 1; r < R; ++r) add_v(acc[u], w[r][u]);
+    }
+}
+
+// The last chunk of r < R slices (r uniform), dispatched to a compile-time size.
+template <int U, int RR>
+__device__ __forceinline__ void chu_rem(double (&acc)[U][kV], const int64_t (&j)[U], const uint16_t* win,
+                                        int64_t stride, int k0, int r) {
+    if constexpr (RR >= 1) {
+        if (r == RR) {
+            hvec w[RR][U];
+            chu_load<U, RR>(w, j, win, stride, k0);
+            __builtin_amdgcn_sched_barrier(0);
+            chu_add<U, RR, false>(acc, w);
+            return;
+        }
+        chu_rem<U, RR - 1>(acc, j, win, stride, k0, r);
+    }
+}
+
+// Nd-way sum (Nd >= R) of the U sub-groups at element offsets j[u].
+template <int U, int R, bool PIPE>
+__device__ __forceinline__ void chu_sum(double (&acc)[U][kV], const int64_t (&j)[U], const uint16_t* win,
+                                        int64_t stride, int nd) {
+    const int nfc = nd / R;
+    hvec wa[R][U];
+    chu_load<U, R>(wa, j, win, stride, 0);
+    if constexpr (PIPE) {
+    hvec wb[R][U];
+    int c = 0;
+    for (;;) {
+        // two register sets in turn, so no set is copied while its loads are in flight
+        if (c + 1 < nfc) chu_load<U, R>(wb, j, win, stride, (c + 1) * R);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c == 0)
+            chu_add<U, R, true>(acc, wa);
+        else
+            chu_add<U, R, false>(acc, wa);
+        if (++c >= nfc) break;
+        if (c + 1 < nfc) chu_load<U, R>(wa, j, win, stride, (c + 1) * R);
+        __builtin_amdgcn_sched_barrier(0);
+        chu_add<U, R, false>(acc, wb);
+        if (++c >= nfc) break;
+    }
+    } else {
+    __builtin_amdgcn_sched_barrier(0);
+    chu_add<U, R, true>(acc, wa);
+    for (int c = 1; c < nfc; ++c) {
+        chu_load<U, R>(wa, j, win, stride, c * R);
+        __builtin_amdgcn_sched_barrier(0);
+        chu_add<U, R, false>(acc, wa);
+    }
+    }
+    chu_rem<U, R - 1>(acc, j, win, stride, nfc * R, nd - nfc * R);
+}
+
+// Element offsets of visit vi's U sub-groups for this lane; a group past
+// nfull is inactive and points at group 0 (its loads are not used).
+template <int U>
+__device__ __forceinline__ void visit_index(int64_t vi, int64_t nfull, int lane, int64_t (&j)[U], bool (&act)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t g = (vi * U + u) * 64 + lane;
+        act[u] = g < nfull;
+        j[u] = (act[u] ? g : 0) * kV;
+    }
+}
+
+// The reduce pass for Nd > kUnroll: the fused step's visits and chunked sum
+// without the state (one shape per Nd range, as there).
+template <int U, int R, bool PIPE, bool kNormOfStored>
+__device__ void rch_run(int64_t nfull, const SrcArgs& src, float* grad_out, double& sq, int& bad) {
+    const int64_t wave = logical_block() * kWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
+    const int64_t nvis = (nfull + 64 * U - 1) / (64 * U);
+    for (int64_t vi = wave; vi < nvis; vi += nwaves) {
+        int64_t j[U];
+        bool act[U];
+        visit_index<U>(vi, nfull, lane, j, act);
+        double acc[U][kV];
+        chu_sum<U, R, PIPE>(acc, j, src.win, src.stride, src.nd);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (act[u]) reduce_finish<kNormOfStored>(acc[u], src, grad_out, j[u], sq, bad);
+    }
+    // the ragged tail group nfull, by the lane that would hold it
+    if (src.n > nfull * kV && (nfull / (64 * U)) % nwaves == wave && nfull % 64 == lane)
+        reduce_tail<kNormOfStored>(nfull * kV, src, grad_out, sq, bad);
+}
+
 #ifndef ZDP_RPF2_MAXR
 #define ZDP_RPF2_MAXR 8  // Nd up to which the reduce pass loads two groups ahead
 #endif
@@ -516,16 +620,11 @@ __global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src_in, fl
                 reduce_tail<kNormOfStored>(g * kV, src, grad_out, sq, bad);
         }
     }
-    for (GroupIter it(ngroups); !done && it.gi < it.end; it.gi += it.step) {
-        const int64_t gi = it.gi;
-        const int64_t j = gi * kV;
-        if (gi < nfull) {
-            double acc[kV];
-            sum_slices<kUnroll>(acc, src.win + j, src.stride, src.nd);
-            reduce_finish<kNormOfStored>(acc, src, grad_out, j, sq, bad);
-        } else {
-            reduce_tail<kNormOfStored>(j, src, grad_out, sq, bad);
-        }
+    if (!done) {
+        if (src.nd >= ZDP_CH_BIG_ND)
+            rch_run<ZDP_CHB_U, ZDP_CHB_R, ZDP_CHB_PIPE != 0, kNormOfStored>(nfull, src, grad_out, sq, bad);
+        else
+            rch_run<ZDP_CHS_U, ZDP_CHS_R, ZDP_CHS_PIPE != 0, kNormOfStored>(nfull, src, grad_out, sq, bad);
     }
     if constexpr (kNormOfStored) {
         // the clipped step's first pass: its second pass sums the partials
@@ -768,6 +867,177 @@ __device__ __forceinline__ bool pf_dispatch(int nd, int64_t gi, int64_t end, int
     return false;
 }
 
+// The fused step element by element over [e0, e1): the ragged tail.
+__device__ void fused_elems(int64_t e0, int64_t e1, const SrcArgs& src, const FusedPtrs& f,
+                            const AdamScalars& c, double& sq, int& bad) {
+    for (int64_t e = e0; e < e1; ++e) {
+        const double s = sum_slices1(src.win + e, src.stride, src.nd);
+        bad |= !finite(s);
+        const double g = s * src.inv_scale;
+        sq += g * g;
+        float po, mo, vo;
+        adam1(c, g, f.pin[e], f.min_[e], f.vin[e], po, mo, vo);
+        f.pout[e] = po;
+        f.mout[e] = mo;
+        f.vout[e] = vo;
+        if (f.ag != nullptr) f.ag[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(po));
+    }
+}
+
+template <int U>
+__device__ __forceinline__ void visit_state(fvec (&pv)[U], fvec (&mv)[U], fvec (&vv)[U], const FusedPtrs& f,
+                                            const int64_t (&j)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        pv[u] = ldg(reinterpret_cast<const fvec*>(f.pin + j[u]));
+        mv[u] = ldg(reinterpret_cast<const fvec*>(f.min_ + j[u]));
+        vv[u] = ldg(reinterpret_cast<const fvec*>(f.vin + j[u]));
+    }
+}
+
+// Unscale, flag, sum of squares, Adam and the stores of one visit.
+template <int U>
+__device__ __forceinline__ void visit_finish(const double (&acc)[U][kV], const fvec (&pv)[U], const fvec (&mv)[U],
+                                             const fvec (&vv)[U], const int64_t (&j)[U], const bool (&act)[U],
+                                             const SrcArgs& src, const FusedPtrs& f, const AdamScalars& c,
+                                             double& sq, int& bad) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (!act[u]) continue;
+        float po[kV], mo[kV], vo[kV];
+#pragma unroll
+        for (int e = 0; e < kV; ++e) {
+            bad |= !finite(acc[u][e]);
+            const double g = acc[u][e] * src.inv_scale;
+            sq += g * g;
+            adam1(c, g, pv[u][e], mv[u][e], vv[u][e], po[e], mo[e], vo[e]);
+        }
+        fvec pw, mw, vw;
+#pragma unroll
+        for (int e = 0; e < kV; ++e) {
+            pw[e] = po[e];
+            mw[e] = mo[e];
+            vw[e] = vo[e];
+        }
+        stg(reinterpret_cast<fvec*>(f.pout + j[u]), pw);
+        stg(reinterpret_cast<fvec*>(f.mout + j[u]), mw);
+        stg(reinterpret_cast<fvec*>(f.vout + j[u]), vw);
+        if (f.ag != nullptr) stg(reinterpret_cast<hvec*>(f.ag + j[u]), pack_v(po));
+    }
+}
+
+// Visits vi = wave, wave + waves, ... (in logical workgroup order); with
+// U = 1 this is the same grid-stride order as GroupIter.
+template <int U, int R, bool PIPE>
+__device__ void ch_loop(int64_t nfull, int64_t wave, int lane, int64_t nwaves, const SrcArgs& src,
+                        const FusedPtrs& f, const AdamScalars& c, double& sq, int& bad) {
+    const int64_t nvis = (nfull + 64 * U - 1) / (64 * U);
+    for (int64_t vi = wave; vi < nvis; vi += nwaves) {
+        int64_t j[U];
+        bool act[U];
+        visit_index<U>(vi, nfull, lane, j, act);
+        fvec pv[U], mv[U], vv[U];
+        visit_state<U>(pv, mv, vv, f, j);
+        double acc[U][kV];
+        chu_sum<U, R, PIPE>(acc, j, src.win, src.stride, src.nd);
+        visit_finish<U>(acc, pv, mv, vv, j, act, src, f, c, sq, bad);
+    }
+}
+
+// The same for Nd a multiple of R, with the chunk loads one chunk ahead
+// across visits: the last chunk of a visit is added while the next visit's
+// state and first chunk are in flight, and those stay in flight through
+// this visit's update.  Register sets w0 / w1 alternate within a visit; the
+// next visit's first chunk goes to wx and moves to w0 after the update.
+template <int U, int R>
+__device__ void ch_loop_xp(int64_t nfull, int64_t wave, int lane, int64_t nwaves, const SrcArgs& src,
+                           const FusedPtrs& f, const AdamScalars& c, double& sq, int& bad) {
+    const int64_t nvis = (nfull + 64 * U - 1) / (64 * U);
+    if (wave >= nvis) return;
+    const int nfc = src.nd / R;
+    int64_t vi = wave;
+    int64_t j[U];
+    bool act[U];
+    visit_index<U>(vi, nfull, lane, j, act);
+    fvec pv[U], mv[U], vv[U];
+    visit_state<U>(pv, mv, vv, f, j);
+    hvec w0[R][U];
+    chu_load<U, R>(w0, j, src.win, src.stride, 0);
+    for (;;) {
+        const int64_t vn = vi + nwaves;
+        const bool more = vn < nvis;
+        int64_t jn[U];
+        bool actn[U];
+        visit_index<U>(more ? vn : 0, more ? nfull : 0, lane, jn, actn);
+        fvec pn[U], mn[U], vn_[U];
+        hvec w1[R][U], wx[R][U];
+        double acc[U][kV];
+        int cc = 0;
+        for (;;) {
+            if (cc + 1 < nfc) {
+                chu_load<U, R>(w1, j, src.win, src.stride, (cc + 1) * R);
+            } else if (more) {
+                visit_state<U>(pn, mn, vn_, f, jn);
+                chu_load<U, R>(wx, jn, src.win, src.stride, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (cc == 0)
+                chu_add<U, R, true>(acc, w0);
+            else
+                chu_add<U, R, false>(acc, w0);
+            if (++cc >= nfc) break;
+            if (cc + 1 < nfc) {
+                chu_load<U, R>(w0, j, src.win, src.stride, (cc + 1) * R);
+            } else if (more) {
+                visit_state<U>(pn, mn, vn_, f, jn);
+                chu_load<U, R>(wx, jn, src.win, src.stride, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            chu_add<U, R, false>(acc, w1);
+            if (++cc >= nfc) break;
+        }
+        visit_finish<U>(acc, pv, mv, vv, j, act, src, f, c, sq, bad);
+        if (!more) break;
+        // the copies below wait for the next visit's loads: keep them after the update
+        __builtin_amdgcn_sched_barrier(0);
+        vi = vn;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            j[u] = jn[u];
+            act[u] = actn[u];
+            pv[u] = pn[u];
+            mv[u] = mn[u];
+            vv[u] = vn_[u];
+#pragma unroll
+            for (int r = 0; r < R; ++r) w0[r][u] = wx[r][u];
+        }
+    }
+}
+
+// Full groups [0, nfull) and the ragged tail for Nd > kUnroll, in one shape.
+template <int U, int R, bool PIPE, bool XP>
+__device__ void ch_run(int64_t nfull, const SrcArgs& src, const FusedPtrs& f, const AdamScalars& c,
+                       double& sq, int& bad) {
+    const int64_t wave = logical_block() * kWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
+    if (XP && src.nd % R == 0)
+        ch_loop_xp<U, R>(nfull, wave, lane, nwaves, src, f, c, sq, bad);
+    else
+        ch_loop<U, R, PIPE>(nfull, wave, lane, nwaves, src, f, c, sq, bad);
+    // the ragged tail group nfull, by the lane that would hold it
+    if (src.n > nfull * kV && (nfull / (64 * U)) % nwaves == wave && nfull % 64 == lane)
+        fused_elems(nfull * kV, src.n, src, f, c, sq, bad);
+}
+
+__device__ __forceinline__ void ch_dispatch(int64_t nfull, const SrcArgs& src, const FusedPtrs& f,
+                                            const AdamScalars& c, double& sq, int& bad) {
+    if (src.nd >= ZDP_CH_BIG_ND)
+        ch_run<ZDP_CHB_U, ZDP_CHB_R, ZDP_CHB_PIPE != 0, ZDP_CHB_XP != 0>(nfull, src, f, c, sq, bad);
+    else
+        ch_run<ZDP_CHS_U, ZDP_CHS_R, ZDP_CHS_PIPE != 0, ZDP_CHS_XP != 0>(nfull, src, f, c, sq, bad);
+}
+
 __global__ void __launch_bounds__(kBlock) fused_step_kernel(SrcArgs src_in, AdamArgs a, Partials ws) {
     const SrcArgs src = resolve_scale(src_in);
     const int cur = a.ctl->cur;
@@ -795,67 +1065,12 @@ __global__ void __launch_bounds__(kBlock) fused_step_kernel(SrcArgs src_in, Adam
         if (done && ngroups > nfull) {
             // the ragged tail group, by the lane whose sequence contains it
             const int64_t g = nfull;
-            if (g >= it.gi && g < it.end && (g - it.gi) % it.step == 0) {
-                for (int64_t e = g * kV; e < src.n; ++e) {
-                    const double s = sum_slices1(src.win + e, src.stride, src.nd);
-                    bad |= !finite(s);
-                    const double gg = s * src.inv_scale;
-                    sq += gg * gg;
-                    float po, mo, vo;
-                    adam1(c, gg, pin[e], min_[e], vin[e], po, mo, vo);
-                    pout[e] = po;
-                    mout[e] = mo;
-                    vout[e] = vo;
-                    if (ag != nullptr) ag[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(po));
-                }
-            }
+            if (g >= it.gi && g < it.end && (g - it.gi) % it.step == 0) fused_elems(g * kV, src.n, src, f, c, sq, bad);
         }
     }
-    for (GroupIter it(ngroups); !done && it.gi < it.end; it.gi += it.step) {
-        const int64_t gi = it.gi;
-        const int64_t j = gi * kV;
-        if (gi < nfull) {
-            const fvec pv = ldg(reinterpret_cast<const fvec*>(pin + j));
-            const fvec mv = ldg(reinterpret_cast<const fvec*>(min_ + j));
-            const fvec vv = ldg(reinterpret_cast<const fvec*>(vin + j));
-            double acc[kV];
-            sum_slices<kUnroll>(acc, src.win + j, src.stride, src.nd);
-            float po[kV], mo[kV], vo[kV];
-#pragma unroll
-            for (int e = 0; e < kV; ++e) {
-                bad |= !finite(acc[e]);
-                const double g = acc[e] * src.inv_scale;
-                sq += g * g;
-                adam1(c, g, pv[e], mv[e], vv[e], po[e], mo[e], vo[e]);
-            }
-            fvec pw, mw, vw;
-#pragma unroll
-            for (int e = 0; e < kV; ++e) {
-                pw[e] = po[e];
-                mw[e] = mo[e];
-                vw[e] = vo[e];
-            }
-            stg(reinterpret_cast<fvec*>(pout + j), pw);
-            stg(reinterpret_cast<fvec*>(mout + j), mw);
-            stg(reinterpret_cast<fvec*>(vout + j), vw);
-            if (ag != nullptr) stg(reinterpret_cast<hvec*>(ag + j), pack_v(po));
-        } else {
-            for (int64_t e = j; e < src.n; ++e) {
-                const double s = sum_slices1(src.win + e, src.stride, src.nd);
-                bad |= !finite(s);
-                const double g = s * src.inv_scale;
-                sq += g * g;
-                float po, mo, vo;
-                adam1(c, g, pin[e], min_[e], vin[e], po, mo, vo);
-                pout[e] = po;
-                mout[e] = mo;
-                vout[e] = vo;
-                if (ag != nullptr) {
-                    const _Float16 h = static_cast<_Float16>(po);
-                    ag[e] = __builtin_bit_cast(uint16_t, h);
-                }
-            }
-        }
+    if (!done) {
+        const FusedPtrs f{pin, min_, vin, pout, mout, vout, ag};
+        ch_dispatch(nfull, src, f, c, sq, bad);
     }
     // partials for commit_kernel (a bucket after the first adds to its slot)
     const bool more = a.bucket != 0 && (a.bucket & ZERO_BUCKET_FIRST) == 0;
