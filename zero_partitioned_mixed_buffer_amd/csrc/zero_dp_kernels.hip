@@ -354,11 +354,14 @@ __device__ void reduce_tail(int64_t j, const SrcArgs& src, float* grad_out, doub
 
 // Shapes of the chunked sum (Nd > kUnroll): U 256-element sub-groups per
 // wave visit, R slices per chunk, PIPE = the next chunk's loads issued
-// before this chunk's adds, XP = also across visits (when Nd is a multiple
-// of R).  Windows with Nd >= ZDP_CH_BIG_ND take the "big" shape.  Measured
-// in pairs on one box against one 256-element group per visit and chunks of
-// 16 (5.9 TB/s of slice reads at Nd = 64): the big shape is 6-11% faster
-// for Nd 48-400, the small one 2-5% for Nd 17-32.
+// before this chunk's adds, XP = also across visits when Nd is a multiple
+// of R (1: the next visit's first chunk, 2: also its state).  Windows with
+// Nd >= ZDP_CH_BIG_ND take the "big" shape.  Measured in pairs on one box
+// against one 256-element group per visit and chunks of 16 (5.9 TB/s of
+// slice reads at Nd = 64): the big shape is 7-14% faster for Nd 48-400,
+// the small one 2-7% for Nd 17-32.  The big shape keeps only the next
+// visit's first chunk ahead of the update: its state as well does not fit
+// the registers of 8 groups per visit without spilling.
 #ifndef ZDP_CH_BIG_ND
 #define ZDP_CH_BIG_ND 48
 #endif
@@ -372,7 +375,7 @@ __device__ void reduce_tail(int64_t j, const SrcArgs& src, float* grad_out, doub
 #define ZDP_CHB_PIPE 1
 #endif
 #ifndef ZDP_CHB_XP
-#define ZDP_CHB_XP 0
+#define ZDP_CHB_XP 1
 #endif
 #ifndef ZDP_CHS_U
 #define ZDP_CHS_U 4
@@ -384,7 +387,7 @@ __device__ void reduce_tail(int64_t j, const SrcArgs& src, float* grad_out, doub
 #define ZDP_CHS_PIPE 1
 #endif
 #ifndef ZDP_CHS_XP
-#define ZDP_CHS_XP 1
+#define ZDP_CHS_XP 2
 #endif
 static_assert(ZDP_CHB_R >= 1 && ZDP_CHB_R <= ZDP_UNROLL && ZDP_CHS_R >= 1 && ZDP_CHS_R <= ZDP_UNROLL,
               "the chunked path runs only for Nd > ZDP_UNROLL");
@@ -946,10 +949,12 @@ __device__ void ch_loop(int64_t nfull, int64_t wave, int lane, int64_t nwaves, c
 
 // The same for Nd a multiple of R, with the chunk loads one chunk ahead
 // across visits: the last chunk of a visit is added while the next visit's
-// state and first chunk are in flight, and those stay in flight through
-// this visit's update.  Register sets w0 / w1 alternate within a visit; the
-// next visit's first chunk goes to wx and moves to w0 after the update.
-template <int U, int R>
+// first chunk (and with XS its state) is in flight, and those stay in
+// flight through this visit's update.  Register sets w0 / w1 alternate
+// within a visit; the next visit's first chunk goes to wx and moves to w0
+// after the update.  Without XS a visit's state loads are issued at its
+// start, behind its first chunk.
+template <int U, int R, bool XS>
 __device__ void ch_loop_xp(int64_t nfull, int64_t wave, int lane, int64_t nwaves, const SrcArgs& src,
                            const FusedPtrs& f, const AdamScalars& c, double& sq, int& bad) {
     const int64_t nvis = (nfull + 64 * U - 1) / (64 * U);
@@ -960,10 +965,11 @@ __device__ void ch_loop_xp(int64_t nfull, int64_t wave, int lane, int64_t nwaves
     bool act[U];
     visit_index<U>(vi, nfull, lane, j, act);
     fvec pv[U], mv[U], vv[U];
-    visit_state<U>(pv, mv, vv, f, j);
+    if constexpr (XS) visit_state<U>(pv, mv, vv, f, j);
     hvec w0[R][U];
     chu_load<U, R>(w0, j, src.win, src.stride, 0);
     for (;;) {
+        if constexpr (!XS) visit_state<U>(pv, mv, vv, f, j);
         const int64_t vn = vi + nwaves;
         const bool more = vn < nvis;
         int64_t jn[U];
@@ -977,7 +983,7 @@ __device__ void ch_loop_xp(int64_t nfull, int64_t wave, int lane, int64_t nwaves
             if (cc + 1 < nfc) {
                 chu_load<U, R>(w1, j, src.win, src.stride, (cc + 1) * R);
             } else if (more) {
-                visit_state<U>(pn, mn, vn_, f, jn);
+                if constexpr (XS) visit_state<U>(pn, mn, vn_, f, jn);
                 chu_load<U, R>(wx, jn, src.win, src.stride, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -989,7 +995,7 @@ __device__ void ch_loop_xp(int64_t nfull, int64_t wave, int lane, int64_t nwaves
             if (cc + 1 < nfc) {
                 chu_load<U, R>(w0, j, src.win, src.stride, (cc + 1) * R);
             } else if (more) {
-                visit_state<U>(pn, mn, vn_, f, jn);
+                if constexpr (XS) visit_state<U>(pn, mn, vn_, f, jn);
                 chu_load<U, R>(wx, jn, src.win, src.stride, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -1005,9 +1011,11 @@ __device__ void ch_loop_xp(int64_t nfull, int64_t wave, int lane, int64_t nwaves
         for (int u = 0; u < U; ++u) {
             j[u] = jn[u];
             act[u] = actn[u];
-            pv[u] = pn[u];
-            mv[u] = mn[u];
-            vv[u] = vn_[u];
+            if constexpr (XS) {
+                pv[u] = pn[u];
+                mv[u] = mn[u];
+                vv[u] = vn_[u];
+            }
 #pragma unroll
             for (int r = 0; r < R; ++r) w0[r][u] = wx[r][u];
         }
@@ -1015,14 +1023,14 @@ __device__ void ch_loop_xp(int64_t nfull, int64_t wave, int lane, int64_t nwaves
 }
 
 // Full groups [0, nfull) and the ragged tail for Nd > kUnroll, in one shape.
-template <int U, int R, bool PIPE, bool XP>
+template <int U, int R, bool PIPE, int XP>
 __device__ void ch_run(int64_t nfull, const SrcArgs& src, const FusedPtrs& f, const AdamScalars& c,
                        double& sq, int& bad) {
     const int64_t wave = logical_block() * kWaves + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
-    if (XP && src.nd % R == 0)
-        ch_loop_xp<U, R>(nfull, wave, lane, nwaves, src, f, c, sq, bad);
+    if (XP != 0 && src.nd % R == 0)
+        ch_loop_xp<U, R, XP == 2>(nfull, wave, lane, nwaves, src, f, c, sq, bad);
     else
         ch_loop<U, R, PIPE>(nfull, wave, lane, nwaves, src, f, c, sq, bad);
     // the ragged tail group nfull, by the lane that would hold it
@@ -1033,9 +1041,9 @@ __device__ void ch_run(int64_t nfull, const SrcArgs& src, const FusedPtrs& f, co
 __device__ __forceinline__ void ch_dispatch(int64_t nfull, const SrcArgs& src, const FusedPtrs& f,
                                             const AdamScalars& c, double& sq, int& bad) {
     if (src.nd >= ZDP_CH_BIG_ND)
-        ch_run<ZDP_CHB_U, ZDP_CHB_R, ZDP_CHB_PIPE != 0, ZDP_CHB_XP != 0>(nfull, src, f, c, sq, bad);
+        ch_run<ZDP_CHB_U, ZDP_CHB_R, ZDP_CHB_PIPE != 0, ZDP_CHB_XP>(nfull, src, f, c, sq, bad);
     else
-        ch_run<ZDP_CHS_U, ZDP_CHS_R, ZDP_CHS_PIPE != 0, ZDP_CHS_XP != 0>(nfull, src, f, c, sq, bad);
+        ch_run<ZDP_CHS_U, ZDP_CHS_R, ZDP_CHS_PIPE != 0, ZDP_CHS_XP>(nfull, src, f, c, sq, bad);
 }
 
 __global__ void __launch_bounds__(kBlock) fused_step_kernel(SrcArgs src_in, AdamArgs a, Partials ws) {
