@@ -13,7 +13,8 @@ synchronisations), the step's achieved HBM bandwidth against the 8 TB/s
 peak (algorithmic bytes (2*Nd + 26) per owned element over the average
 device time of the step's two kernels, from HIP events around K
 back-to-back steps on the launch stream), and the oracle's rate on a
-bounded sample of the same workload on the host cores.
+bounded sample of the same workload on one host core (and, as
+cpu_baseline.all_cores, on every core the process may use, up to 16).
 """
 from __future__ import annotations
 
@@ -84,16 +85,22 @@ def kernel_fingerprint():
 
 
 def measured_traffic(workload):
-    """HBM bytes per launch of the fused kernel from the committed rocprofv3
-    counter summary for this workload, or None if absent or stale."""
+    """HBM bytes per fused step (all of its fused launches) from the committed
+    rocprofv3 counter summaries, or None if absent or stale.  A summary of
+    one workload gives traffic_bytes_per_launch; a summary of several gives
+    traffic_bytes_per_step_<workload> for each."""
     import glob
     import re
     fp = kernel_fingerprint()
-    for path in glob.glob(os.path.join(ROOT, "profiles", f"fused_step_{workload}_*pmc*.md")):
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "fused_step_*pmc*.md"))):
         text = open(path).read()
         m_fp = re.search(r"kernel_fingerprint:\s*([0-9a-f]+)", text)
-        m_tr = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
-        if m_fp and m_tr and m_fp.group(1) == fp:
+        if not m_fp or m_fp.group(1) != fp:
+            continue
+        m_tr = re.search(rf"traffic_bytes_per_step_{workload}:\s*([0-9]+)", text)
+        if m_tr is None and os.path.basename(path).startswith(f"fused_step_{workload}_"):
+            m_tr = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+        if m_tr:
             return int(m_tr.group(1))
     return None
 
@@ -158,6 +165,50 @@ def cpu_baseline(w, n_sample, budget_s, max_grad_norm=0.0, scale_interval=0):
                       f"{', clipped' if max_grad_norm > 0 else ''}"
                       f"{', dynamic loss scale' if scale_interval > 0 else ''}), {el:.1f} s",
             "gbs": rate * (2 * w.nd + 26) / 1e9}
+
+
+def _oracle_share(job):
+    """One host core's share of the all-cores oracle figure: its own chunk of
+    the workload's parameters and gradients, stepped by the oracle for
+    about budget_s.  Returns (elements stepped, seconds)."""
+    import oracle
+    from workloads import configs, gen
+    key, k, n_sample, budget_s, max_grad_norm, scale_interval = job
+    w = configs.ALL[key]
+    lo = (k * n_sample) % max(1, w.psi - n_sample)
+    master = gen.host_params(w.seed, w.psi, lo, lo + n_sample, w.param_sigma)
+    sh = oracle.OwnedShard(master, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                           weight_decay=w.weight_decay, max_grad_norm=max_grad_norm,
+                           scale_interval=scale_interval, loss_scale=w.loss_scale)
+    grads = [gen.host_grad_slices(w.seed, s, 0, w.nd, n_sample, lo, w.psi, w.grad_sigma, w.loss_scale,
+                                  w.dist) for s in (1, 2)]
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        sh.step(grads[steps % 2], w.loss_scale)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return n_sample * steps, el
+
+
+def cpu_baseline_all_cores(w, n_sample, budget_s, max_grad_norm=0.0, scale_interval=0):
+    """The same oracle on every host core this process may use (at most 16):
+    one process per core, each stepping its own chunk of the window at the
+    same time (elements are independent).  Uses fork, and runs before this
+    process loads the HIP library, so no child is made from a process that
+    has touched the GPU."""
+    import multiprocessing as mp
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    jobs = [(w.key, k, n_sample, budget_s, max_grad_norm, scale_interval) for k in range(cores)]
+    with mp.get_context("fork").Pool(cores) as pool:
+        res = pool.map(_oracle_share, jobs, chunksize=1)
+    rate = sum(e / t for e, t in res)
+    return {"value": rate, "unit": "elements/s", "cores": cores, "kind": "oracle",
+            "sample": f"{cores} processes, each stepping its own {n_sample}-element chunk of workload {w.key} "
+                      f"for {budget_s:.0f} s (numpy float64, one thread each)",
+            "gbs": rate * (2 * w.nd + (34 if max_grad_norm > 0 else 26)) / 1e9}
 
 
 def cpu_baseline_gather(w, windows, part, ranges, budget_s):
@@ -281,6 +332,12 @@ def main():
     from zero_partitioned_mixed_buffer_amd import OwnedShard, binding as B
 
     w = configs.ALL[args.workload]
+    cpu_all = None
+    if not args.no_cpu_baseline:
+        # before the HIP library is loaded: the worker processes are forked
+        n_pool = min(w.psi // w.nd, 1 << 21) if w.nd <= 64 else min(w.psi // w.nd, 1 << 16)
+        cpu_all = cpu_baseline_all_cores(w, n_pool, args.cpu_seconds / 2, args.max_grad_norm, args.dynamic_scale)
+        log(f"oracle: {cpu_all['value']:.3e} elements/s on {cpu_all['cores']} cores")
     owner = w.owners[-1]
     plan, _ = B.plan_partitions(list(w.numels), w.nd, 256)
     S = plan["part"]
@@ -458,6 +515,7 @@ def main():
         n_sample = min(S, 1 << 21) if w.nd <= 64 else min(S, 1 << 16)
         cpu = cpu_baseline(w, n_sample, args.cpu_seconds, args.max_grad_norm, args.dynamic_scale)
         log(f"oracle: {cpu['value']:.3e} elements/s on 1 core")
+        cpu["all_cores"] = cpu_all
 
     out = {
         "metric": METRIC,
