@@ -106,7 +106,7 @@ def measured_traffic(workload):
 
 
 def attainable_copy(torch, dev, B, reps=5):
-    """Attainable streaming bandwidth on this machine: the library's own copy
+    """Attainable streaming bandwidth on this GPU: the library's own copy
     kernel (zero_gather_params over one 4 GiB window) moving 4 GiB into
     another 4 GiB buffer; GB/s of read + write."""
     n = 1 << 31  # fp16 elements
@@ -497,7 +497,7 @@ def main():
 
     calibration_copy(torch, dev)
     attain = attainable_copy(torch, dev, B)
-    log(f"attainable copy on this box: {attain['copy_gbs']:.0f} GB/s")
+    log(f"attainable copy on this GPU: {attain['copy_gbs']:.0f} GB/s")
     traffic = None if (clipped or bucketed) else measured_traffic(w.key)
 
     ms_step = wall * 1e3 / args.steps

@@ -356,7 +356,7 @@ __device__ void reduce_tail(int64_t j, const SrcArgs& src, float* grad_out, doub
 // wave visit, R slices per chunk, PIPE = the next chunk's loads issued
 // before this chunk's adds, XP = also across visits when Nd is a multiple
 // of R (1: the next visit's first chunk, 2: also its state).  Windows with
-// Nd >= ZDP_CH_BIG_ND take the "big" shape.  Measured in pairs on one box
+// Nd >= ZDP_CH_BIG_ND take the "big" shape.  Measured in pairs on one MI355X
 // against one 256-element group per visit and chunks of 16 (5.9 TB/s of
 // slice reads at Nd = 64): the big shape is 7-14% faster for Nd 48-400,
 // the small one 2-7% for Nd 17-32.  The big shape keeps only the next
