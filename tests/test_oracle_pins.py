@@ -139,6 +139,28 @@ def test_reduce_special_cases():
     assert np.array_equal(a[nz], b[nz])
 
 
+def test_reduce_zero_sign_in_any_order():
+    """The exact sum's sign of zero: -0 only when every term is -0, +0 for a
+    mixed-sign zero column and for any exact cancellation (round to nearest
+    gives +0 for x + (-x)).  All 24 orders of the four slices give the same
+    bits, so the kernels' slice order cannot matter even for zeros."""
+    from itertools import permutations
+    tiny = 2.0**-24
+    cols = np.array([
+        [-0.0, -0.0, -0.0, -0.0],         # -0
+        [0.0, -0.0, -0.0, -0.0],          # +0
+        [1.0, -1.0, -0.0, -0.0],          # +0: exact cancellation
+        [-0.0, tiny, -tiny, -0.0],        # +0
+        [65504.0, -65504.0, -0.0, -0.0],  # +0
+        [-0.0, -0.0, 1.0, -1.0],          # +0: cancellation after -0 + -0
+        [-0.0, 3.0, -1.0, -0.0],          # 2
+    ], dtype=F16).T  # [4 slices, 7 elements]
+    want = np.array([-0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 2.0])
+    for perm in permutations(range(4)):
+        got = oracle.reduce_owned(cols[list(perm)])
+        assert np.array_equal(got.view(np.uint64), want.view(np.uint64)), perm
+
+
 def test_unscale_flag_and_norm():
     g = np.random.default_rng(5)
     sl = (g.standard_normal((5, 100)) * 300).astype(F16)
