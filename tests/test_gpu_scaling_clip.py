@@ -43,8 +43,10 @@ def _run(n, nd, steps, seed, hp, bad_steps=(), sigma=1e-3, static_L=1024.0):
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
 
 
-@pytest.mark.parametrize("nd", [1, 4, 9])
+@pytest.mark.parametrize("nd", [1, 4, 9, 24, 64])
 def test_dynamic_scaling_fused(nd):
+    """The scale trajectory through skips and growth, on the prefetch path
+    (Nd <= 16) and both chunked-sum visit shapes (Nd 24 and 64)."""
     hp = dict(HP, scale_interval=2, loss_scale=4096.0)
     sh, _ = _run(20003, nd, 9, 40 + nd, hp, bad_steps=(2, 6, 7))
     assert sh.flags == [0, 1, 0, 0, 0, 1, 1, 0, 0]
