@@ -103,10 +103,13 @@ def _edge_mutate(step, sl):
     return sl
 
 
-def test_fused_step_edge_values():
+@pytest.mark.parametrize("nd", [5, 24, 64])
+def test_fused_step_edge_values(nd):
     """Signed zeros, fp16 subnormals and +-65504 at the first, last and
-    random elements; all-zero (padding-like) elements stay zero."""
-    _run_case(4099, 5, steps=4, seed=5, mutate=_edge_mutate, L=1.0)
+    random elements; all-zero (padding-like) elements stay zero.  Nd 24 and
+    64 take the chunked sum (its first chunk starts from slice 0, so an
+    all -0 column sums to -0 there too)."""
+    _run_case(4099, nd, steps=4, seed=5, mutate=_edge_mutate, L=1.0)
 
 
 @pytest.mark.parametrize("where", ["first", "middle", "last"])
