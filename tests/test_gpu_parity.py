@@ -112,12 +112,14 @@ def test_fused_step_edge_values(nd):
     _run_case(4099, nd, steps=4, seed=5, mutate=_edge_mutate, L=1.0)
 
 
+@pytest.mark.parametrize("nd", [6, 24, 64])
 @pytest.mark.parametrize("where", ["first", "middle", "last"])
 @pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan, "inf-inf"])
-def test_overflow_skip(where, bad):
+def test_overflow_skip(where, bad, nd):
     """An inf/NaN anywhere skips the step: state bit-identical, t unchanged,
-    all-gather window restored; the following steps proceed normally."""
-    n, nd = 10000 + 3, 6
+    all-gather window restored; the following steps proceed normally (on
+    the prefetch path and both chunked-sum visit shapes)."""
+    n = 10000 + 3
     pos = {"first": 0, "middle": n // 2, "last": n - 1}[where]
 
     def mutate(step, sl):
