@@ -1514,24 +1514,36 @@ int fixed_grid(KernelId id) {
 #ifndef ZDP_SPLIT_LOG2
 #define ZDP_SPLIT_LOG2 24  // elements per launch of a long window: about 2^24 (0: one launch)
 #endif
+#ifndef ZDP_SPLIT_BIG_LOG2
+#define ZDP_SPLIT_BIG_LOG2 23  // the same for Nd >= ZDP_CH_BIG_ND (the 8-group visits)
+#endif
 
 // A window longer than two launch lengths is stepped in launches of about
-// 2^24 elements.  One grid-stride launch over 10^8 elements measured 3-4%
-// slower than the same work in launches of 2^24 elements (Nd 16, 64 and
-// 400); shorter windows take one launch, where the few microseconds an
-// extra launch costs outweigh the gain.
-constexpr int64_t kSplitElems = ZDP_SPLIT_LOG2 > 0 ? (int64_t{1} << ZDP_SPLIT_LOG2) : 0;
+// 2^24 elements (2^23 from Nd = 48 up).  One grid-stride launch over 10^8
+// elements measured 3-16% slower than the same work in such launches (Nd
+// 16, 64 and 400); shorter windows take one launch, where the few
+// microseconds an extra launch costs outweigh the gain.  The 8-group visits
+// of Nd >= 48 run 1-2% faster in launches of 2^23 than of 2^24 (the
+// GPT-2-XL shard at Nd = 16 runs 1.4% slower there).
+int64_t split_elems(int32_t nd) {
+    const int l = nd >= ZDP_CH_BIG_ND ? ZDP_SPLIT_BIG_LOG2 : ZDP_SPLIT_LOG2;
+    return l > 0 ? (int64_t{1} << l) : 0;
+}
 
-bool split_window(int64_t n) { return kSplitElems > 0 && n > 2 * kSplitElems; }
+bool split_window(int64_t n, int32_t nd) {
+    const int64_t e = split_elems(nd);
+    return e > 0 && n > 2 * e;
+}
 
 // Calls launch(off, k) for consecutive pieces [off, off + k) that cover
-// [0, n): one piece, or pieces of about kSplitElems elements (multiples of
-// 1024, so every piece starts 16-byte aligned) when split_window(n).
+// [0, n): one piece, or pieces of about split_elems(nd) elements (multiples
+// of 1024, so every piece starts 16-byte aligned) when split_window(n, nd).
 template <class Launch>
-int for_each_piece(int64_t n, Launch&& launch) {
+int for_each_piece(int64_t n, int32_t nd, Launch&& launch) {
     int64_t len = n;
-    if (split_window(n)) {
-        const int64_t pieces = (n + kSplitElems - 1) / kSplitElems;
+    if (split_window(n, nd)) {
+        const int64_t e = split_elems(nd);
+        const int64_t pieces = (n + e - 1) / e;
         len = ((n + pieces - 1) / pieces + 1023) / 1024 * 1024;
     }
     int64_t off = 0;
@@ -1568,7 +1580,7 @@ AdamArgs piece_args(const AdamArgs& a, int64_t off) {
 // `first` (the first launch of a step).  a.window_n must be set.
 int launch_fused_range(const SrcArgs& src, const AdamArgs& a, bool first, int grid, const Partials& ws,
                        hipStream_t s) {
-    return for_each_piece(src.n, [&](int64_t off, int64_t k) {
+    return for_each_piece(src.n, src.nd, [&](int64_t off, int64_t k) {
         AdamArgs b = piece_args(a, off);
         b.bucket = 4 | (first && off == 0 ? ZERO_BUCKET_FIRST : 0);
         fused_step_kernel<<<grid, kBlock, 0, s>>>(piece_src(src, off, k), b, ws);
@@ -1625,7 +1637,7 @@ int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st, const ze
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const SrcArgs whole = make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr);
     (void)hipGetLastError();
-    if (!split_window(n)) {
+    if (!split_window(n, src->nd)) {
         const int grid = grid_for(kFused, n);
         fused_step_kernel<<<grid, kBlock, 0, s>>>(whole, a, ws);
         const int rc2 = finish_launch();
@@ -1659,15 +1671,16 @@ int zero_adam_step_clipped(const zero_grad_src* src, const zero_adam_state* st, 
     const SrcArgs whole = make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr);
     // a long window takes each pass in pieces; the first pass's pieces run
     // on one grid and accumulate in the workgroup slots
-    const int grid1 = split_window(n) ? fixed_grid(kReduce) : grid_for(kReduce, n);
+    const int grid1 = split_window(n, src->nd) ? fixed_grid(kReduce) : grid_for(kReduce, n);
     (void)hipGetLastError();
-    int rc2 = for_each_piece(n, [&](int64_t off, int64_t k) {
+    int rc2 = for_each_piece(n, src->nd, [&](int64_t off, int64_t k) {
         reduce_owned_kernel<true><<<grid1, kBlock, 0, s>>>(piece_src(whole, off, k), grad_buf + off, nullptr,
                                                             nullptr, ws, off != 0);
         return finish_launch();
     });
     if (rc2 != ZERO_OK) return rc2;
-    rc2 = for_each_piece(n, [&](int64_t off, int64_t k) {
+    // the update pass streams g and the state alone: pieces as for Nd < 48
+    rc2 = for_each_piece(n, 1, [&](int64_t off, int64_t k) {
         clipped_update_kernel<<<grid_for(kClip, k), kBlock, 0, s>>>(grad_buf + off, k, piece_args(a, off),
                                                                    hp->max_grad_norm, ws, grid1);
         return finish_launch();
