@@ -104,7 +104,7 @@ def _check(run, ref, got, sq, tag):
     (20011, 3, 20016, "forward"),       # one bucket (FIRST | LAST)
     (9001, 1, 512, "shuffled"),         # 18 buckets, Nd = 1
     (40000, 20, 8000, "forward"),       # Nd > 16: the chunked sum
-    (300001, 48, 65536, "shuffled"),    # Nd >= 48: 8-group visits cut by bucket edges
+    (300001, 48, 65536, "shuffled"),    # Nd >= 32: 8-group visits cut by bucket edges
     (200003, 49, 40000, "forward"),     # odd Nd: a one-slice last chunk
     (600003, 64, 131072, "reversed"),
 ])

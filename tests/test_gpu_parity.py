@@ -66,13 +66,13 @@ def test_fused_step_every_nd_many_groups_per_lane(nd):
 
 
 # Windows for the chunked sum past 16 slices, where one wave's visit covers 4
-# (Nd < 48) or 8 (Nd >= 48) consecutive 256-element groups, so one pass of
+# (Nd < 32) or 8 (Nd >= 32) consecutive 256-element groups, so one pass of
 # the 1024 waves covers 2^20 or 2^21 elements.  Each window runs past one
 # full pass (or stops short of it), ends in a partial visit and a ragged
 # group, and the slice counts take both chunk loops (Nd a multiple of the
-# two-slice chunk, or one slice left over) on both sides of Nd = 48.
-CHUNKED_CASES = [(17, 2**20 + 3 * 256 + 5), (18, 2**20 + 3 * 256 + 5), (47, 300001), (48, 2**21 + 2053),
-                 (64, 2**21 + 2053), (99, 600003)]
+# two-slice chunk, or one slice left over) on both sides of Nd = 32.
+CHUNKED_CASES = [(17, 2**20 + 3 * 256 + 5), (18, 2**20 + 3 * 256 + 5), (31, 2**20 + 3 * 256 + 5),
+                 (32, 2**21 + 2053), (47, 300001), (48, 2**21 + 2053), (64, 2**21 + 2053), (99, 600003)]
 
 
 @pytest.mark.parametrize("nd,n", CHUNKED_CASES)

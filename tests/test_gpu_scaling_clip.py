@@ -70,7 +70,7 @@ def test_clipped_many_groups_per_lane(nd):
     """Both clipped passes on a window where each lane owns 6 or 7 element
     groups (the prefetch rotations run several full cycles), ragged tail,
     clipping active, one skipped step.  Past 16 slices the reduce pass sums
-    in chunks over visits of 4 (Nd < 48) or 8 groups, with Nd = 99 leaving
+    in chunks over visits of 4 (Nd < 32) or 8 groups, with Nd = 99 leaving
     a one-slice last chunk."""
     n = 4 * 65536 * 6 + 4 * 1000 + 3
     hp = dict(HP, weight_decay=0.01, max_grad_norm=0.05)

@@ -359,11 +359,12 @@ __device__ void reduce_tail(int64_t j, const SrcArgs& src, float* grad_out, doub
 // Nd >= ZDP_CH_BIG_ND take the "big" shape.  Measured in pairs on one MI355X
 // against one 256-element group per visit and chunks of 16 (5.9 TB/s of
 // slice reads at Nd = 64): the big shape is 7-14% faster for Nd 48-400,
-// the small one 2-7% for Nd 17-32.  The big shape keeps only the next
+// the small one 2-7% for Nd 17-32.  With launches of 2^23 for the big
+// shape it also wins from Nd = 32 up (0.5-3% at Nd 32-40).  The big shape keeps only the next
 // visit's first chunk ahead of the update: its state as well does not fit
 // the registers of 8 groups per visit without spilling.
 #ifndef ZDP_CH_BIG_ND
-#define ZDP_CH_BIG_ND 48
+#define ZDP_CH_BIG_ND 32
 #endif
 #ifndef ZDP_CHB_U
 #define ZDP_CHB_U 8
@@ -1519,11 +1520,11 @@ int fixed_grid(KernelId id) {
 #endif
 
 // A window longer than two launch lengths is stepped in launches of about
-// 2^24 elements (2^23 from Nd = 48 up).  One grid-stride launch over 10^8
+// 2^24 elements (2^23 for the big visit shape, Nd >= ZDP_CH_BIG_ND).  One grid-stride launch over 10^8
 // elements measured 3-16% slower than the same work in such launches (Nd
 // 16, 64 and 400); shorter windows take one launch, where the few
 // microseconds an extra launch costs outweigh the gain.  The 8-group visits
-// of Nd >= 48 run 1-2% faster in launches of 2^23 than of 2^24 (the
+// of the big shape run 1-2% faster in launches of 2^23 than of 2^24 (the
 // GPT-2-XL shard at Nd = 16 runs 1.4% slower there).
 int64_t split_elems(int32_t nd) {
     const int l = nd >= ZDP_CH_BIG_ND ? ZDP_SPLIT_BIG_LOG2 : ZDP_SPLIT_LOG2;
@@ -1679,7 +1680,7 @@ int zero_adam_step_clipped(const zero_grad_src* src, const zero_adam_state* st, 
         return finish_launch();
     });
     if (rc2 != ZERO_OK) return rc2;
-    // the update pass streams g and the state alone: pieces as for Nd < 48
+    // the update pass streams g and the state alone: pieces as for small Nd
     rc2 = for_each_piece(n, 1, [&](int64_t off, int64_t k) {
         clipped_update_kernel<<<grid_for(kClip, k), kBlock, 0, s>>>(grad_buf + off, k, piece_args(a, off),
                                                                    hp->max_grad_norm, ws, grid1);
