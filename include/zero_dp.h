@@ -245,9 +245,10 @@ typedef struct zero_adam_hp {
  * fused pass (each workgroup leaves its partial sum of g^2 and flag in the
  * workspace) and a small commit kernel that sums them in a fixed order and
  * commits the step in ctl (see zero_adam_state), or skips it and re-emits
- * the all-gather window from the committed master.  A window of more than
- * 2^25 elements takes its fused pass in consecutive launches of about 2^24
- * elements each (measured faster than one long launch), whose partials
+ * the all-gather window from the committed master.  A long window takes its
+ * fused pass in consecutive launches (measured faster than one long
+ * launch): of about 2^24 elements when it is longer than 2^25 and Nd < 32,
+ * of about 2^23 when it is longer than 2^24 and Nd >= 32.  Their partials
  * accumulate in the workspace; the results are the same element for
  * element, and the sum of g^2 differs only in its rounding order.  A rank steps its own
  * partition alone and the new parameters then reach every rank by
@@ -281,8 +282,9 @@ int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st,
  *           coef = min(1, max_grad_norm / (sqrt(sumsq) + 1e-6)) and the
  *           update of zero_adam_step runs on g = g32 * coef (float64);
  *   then a one-workgroup commit; ctl->clip_coef records coef.
- * A window of more than 2^25 elements takes each pass in consecutive
- * launches of about 2^24 elements, as zero_adam_step does.
+ * A long window takes each pass in consecutive launches: the first pass
+ * as zero_adam_step's fused pass, the second in launches of about 2^24
+ * elements when the window is longer than 2^25.
  * L is src->loss_scale or, with dynamic scaling, ctl->loss_scale.
  * Traffic (2*Nd + 4) + 30 bytes per element instead of 2*Nd + 26.
  *   grad_buf: device float[n], 16-byte aligned, must not overlap any other
