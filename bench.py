@@ -327,17 +327,19 @@ def main():
         bench_gather(args)
         return
 
-    import torch
     from workloads import configs, gen
-    from zero_partitioned_mixed_buffer_amd import OwnedShard, binding as B
 
     w = configs.ALL[args.workload]
     cpu_all = None
     if not args.no_cpu_baseline:
-        # before the HIP library is loaded: the worker processes are forked
+        # before torch and the HIP library are loaded: the worker processes are forked, and a fork
+        # taken after a library has started threads can inherit a held lock
         n_pool = min(w.psi // w.nd, 1 << 21) if w.nd <= 64 else min(w.psi // w.nd, 1 << 16)
         cpu_all = cpu_baseline_all_cores(w, n_pool, args.cpu_seconds / 2, args.max_grad_norm, args.dynamic_scale)
         log(f"oracle: {cpu_all['value']:.3e} elements/s on {cpu_all['cores']} cores")
+
+    import torch
+    from zero_partitioned_mixed_buffer_amd import OwnedShard, binding as B
     owner = w.owners[-1]
     plan, _ = B.plan_partitions(list(w.numels), w.nd, 256)
     S = plan["part"]
