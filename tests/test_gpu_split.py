@@ -1,5 +1,6 @@
 """GPU parity of a long window, whose fused pass the library runs as several
-consecutive launches (windows of more than 2^25 elements).
+consecutive launches (windows of more than 2^25 elements, or of more than
+2^24 from 32 slices up).
 
 The same window is stepped twice on the device: by zero_adam_step (split
 into launches) and in buckets of 2^20 elements (one launch each; the
@@ -25,6 +26,11 @@ pytestmark = pytest.mark.gpu
 
 N = (1 << 25) + 5003  # a ragged tail group after the last full one
 ND = 3
+# From 32 slices up the library splits at 2^23 elements once a window is
+# longer than 2^24: this window takes three launches there and one below.
+N_BIG_ND = (1 << 24) + 5003
+BIG_ND = 48
+SPLITS = [(ND, N), (BIG_ND, N_BIG_ND)]
 L = 1024.0
 
 
@@ -45,8 +51,8 @@ def _sumsq(torch, slices, scale=L):
     return float((g * g).sum().item())
 
 
-@pytest.mark.parametrize("dynamic", [False, True])
-def test_long_window_split_launches(dynamic):
+@pytest.mark.parametrize("nd,n,dynamic", [(ND, N, False), (ND, N, True), (BIG_ND, N_BIG_ND, False)])
+def test_long_window_split_launches(nd, n, dynamic):
     """With dynamic loss scaling (interval 2, from 4096) the slices carry
     the control block's scale, and the scale trajectory must match the
     oracle's exactly."""
@@ -56,34 +62,34 @@ def test_long_window_split_launches(dynamic):
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
     if dynamic:
         hp.update(scale_interval=2, loss_scale=4096.0)
-    master = torch.empty(N, dtype=torch.float32, device="cuda")
-    gen.device_fill_params(master, 123, 0.02, N)
-    idx = _sample_idx(N)
+    master = torch.empty(n, dtype=torch.float32, device="cuda")
+    gen.device_fill_params(master, 123, 0.02, n)
+    idx = _sample_idx(n)
     tidx = torch.from_numpy(idx).cuda()
     ref = oracle.OwnedShard(master[tidx].cpu().numpy(), **hp)
     whole = OwnedShard(master, **hp)
     buck = OwnedShard(master, **hp)
     del master
-    ag_w = torch.zeros(N + 16, dtype=torch.float16, device="cuda")
-    ag_b = torch.zeros(N + 16, dtype=torch.float16, device="cuda")
+    ag_w = torch.zeros(n + 16, dtype=torch.float16, device="cuda")
+    ag_b = torch.zeros(n + 16, dtype=torch.float16, device="cuda")
     whole.emit(ag_w, 8)
     buck.emit(ag_b, 8)
-    # slice stride a multiple of 8 elements; the columns past N are zero
-    dsl = torch.empty((ND, (N + 7) // 8 * 8), dtype=torch.float16, device="cuda")
+    # slice stride a multiple of 8 elements; the columns past n are zero
+    dsl = torch.empty((nd, (n + 7) // 8 * 8), dtype=torch.float16, device="cuda")
     bucket = 1 << 20
-    say(f"n={N} nd={ND}: {idx.size} sampled elements")
+    say(f"n={n} nd={nd}: {idx.size} sampled elements")
     for step in range(1, 4):
         scale = ref.scale if dynamic else L  # the scale the slices carry
-        gen.device_fill_grads(dsl, 77, step, 1e-3, scale, "normal", N)
+        gen.device_fill_grads(dsl, 77, step, 1e-3, scale, "normal", n)
         if step == 2:
-            dsl[1, N - 10] = float("inf")  # in the last launch of the split (sampled)
+            dsl[1, n - 10] = float("inf")  # in the last launch of the split (sampled)
         ovf, _ = ref.step(dsl[:, tidx].cpu().numpy(), L)
         sq_want = None if ovf else _sumsq(torch, dsl, scale)
-        say(f"step {step}: split whole-window step, then {-(-N // bucket)} buckets")
+        say(f"step {step}: split whole-window step, then {-(-n // bucket)} buckets")
         whole.step(dsl, L, allgather=ag_w, allgather_off=8)
-        for o in range(0, N, bucket):
-            k = min(bucket, N - o)
-            phase = (B.BUCKET_FIRST if o == 0 else 0) | (B.BUCKET_LAST if o + k >= N else 0)
+        for o in range(0, n, bucket):
+            k = min(bucket, n - o)
+            phase = (B.BUCKET_FIRST if o == 0 else 0) | (B.BUCKET_LAST if o + k >= n else 0)
             buck.step_bucket(dsl, o, k, phase, L, elem_off=o, allgather=ag_b, allgather_off=8)
         torch.cuda.synchronize()
         cw, cb = whole.control(), buck.control()
@@ -114,8 +120,10 @@ def _sumsq32(torch, slices):
     return float((g * g).sum().item())
 
 
-def test_long_window_clipped_split():
-    """The clipped step on a long window, both passes split into launches:
+@pytest.mark.parametrize("nd,n", SPLITS)
+def test_long_window_clipped_split(nd, n):
+    """The clipped step on a long window, its passes split into launches
+    (the reduce pass by the slice count's rule, the update pass past 2^25):
     sampled elements (dense around every multiple of 1024) against the
     oracle given the window's norm from a float64 torch sum of the fp32
     gradients; the sum of squares and the clip coefficient within 1e-12
@@ -124,18 +132,18 @@ def test_long_window_clipped_split():
     torch = torch_mod()
     from zero_partitioned_mixed_buffer_amd import OwnedShard
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=0.5)
-    master = torch.empty(N, dtype=torch.float32, device="cuda")
-    gen.device_fill_params(master, 321, 0.02, N)
-    idx = _sample_idx(N)
+    master = torch.empty(n, dtype=torch.float32, device="cuda")
+    gen.device_fill_params(master, 321, 0.02, n)
+    idx = _sample_idx(n)
     tidx = torch.from_numpy(idx).cuda()
     ref = oracle.OwnedShard(master[tidx].cpu().numpy(), **hp)
     sh = OwnedShard(master, **hp)
     del master
-    ag = torch.zeros(N + 16, dtype=torch.float16, device="cuda")
+    ag = torch.zeros(n + 16, dtype=torch.float16, device="cuda")
     sh.emit(ag, 8)
-    dsl = torch.empty((ND, (N + 7) // 8 * 8), dtype=torch.float16, device="cuda")
+    dsl = torch.empty((nd, (n + 7) // 8 * 8), dtype=torch.float16, device="cuda")
     for step in range(1, 4):
-        gen.device_fill_grads(dsl, 78, step, 1e-3, L, "normal", N)
+        gen.device_fill_grads(dsl, 78, step, 1e-3, L, "normal", n)
         injected = step == 2
         if injected:
             dsl[2, 2] = float("-inf")  # in the first launch of the split (sampled)
