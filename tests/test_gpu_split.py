@@ -173,3 +173,81 @@ def test_long_window_clipped_split(nd, n):
         bits = ag.view(torch.int16)[8 + tidx].cpu().numpy().view(np.uint16)
         assert_fp16_close(bits, ref.window().view(np.uint16), f"{tag} window")
     assert ref.flags == [0, 1, 0] and ref.t == 2
+
+
+N_PAST_INT32 = (1 << 31) + 5003
+
+
+def _sumsq_chunked(torch, slices, n, scale):
+    tot = 0.0
+    for c in range(0, n, 1 << 27):
+        g = slices[:, c:min(n, c + (1 << 27))].to(torch.float64).sum(0) * (1.0 / scale)
+        tot += float((g * g).sum().item())
+    return tot
+
+
+def test_window_past_int32_elements():
+    """A window of 2^31 + 5003 elements (Nd = 1; about 125 GB of device
+    memory for two shards), so element indices and offsets pass the int32
+    range.  Two steps, the second skipped by an inf in the last element
+    group: the commit then re-emits the whole window from the committed
+    master in one launch.  The split fused step and a bucketed twin
+    (buckets of 2^26 elements, so its boundaries differ from the split's)
+    agree bit for bit over the whole window; sampled elements (around every
+    multiple of 2^28, around 2^31 and the tail) match the oracle."""
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import OwnedShard
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    torch.cuda.empty_cache()
+    n, nd = N_PAST_INT32, 1
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    master = torch.empty(n, dtype=torch.float32, device="cuda")
+    gen.device_fill_params(master, 124, 0.02, n)
+    g = np.random.default_rng(9)
+    near = (np.arange(0, n, 1 << 28, dtype=np.int64)[:, None] + np.arange(-8, 8, dtype=np.int64)).ravel()
+    idx = np.unique(np.concatenate([near, (1 << 31) + np.arange(-16, 16, dtype=np.int64),
+                                    g.integers(0, n, 1 << 14, dtype=np.int64), np.arange(n - 16, n, dtype=np.int64)]))
+    idx = idx[(idx >= 0) & (idx < n)]
+    tidx = torch.from_numpy(idx).cuda()
+    ref = oracle.OwnedShard(master[tidx].cpu().numpy(), **hp)
+    whole = OwnedShard(master, **hp)
+    buck = OwnedShard(master, **hp)
+    del master
+    ag_w = torch.zeros(n + 16, dtype=torch.float16, device="cuda")
+    ag_b = torch.zeros(n + 16, dtype=torch.float16, device="cuda")
+    whole.emit(ag_w, 8)
+    buck.emit(ag_b, 8)
+    dsl = torch.empty((nd, (n + 7) // 8 * 8), dtype=torch.float16, device="cuda")
+    bucket = 1 << 26
+    say(f"n={n} nd={nd}: {idx.size} sampled elements")
+    for step in range(1, 3):
+        gen.device_fill_grads(dsl, 79, step, 1e-3, L, "normal", n)
+        if step == 2:
+            dsl[0, n - 10] = float("inf")
+        ovf, _ = ref.step(dsl[:, tidx].cpu().numpy(), L)
+        sq_want = None if ovf else _sumsq_chunked(torch, dsl, n, L)
+        say(f"step {step}: split whole-window step, then {-(-n // bucket)} buckets")
+        whole.step(dsl, L, allgather=ag_w, allgather_off=8)
+        for o in range(0, n, bucket):
+            k = min(bucket, n - o)
+            phase = (B.BUCKET_FIRST if o == 0 else 0) | (B.BUCKET_LAST if o + k >= n else 0)
+            buck.step_bucket(dsl, o, k, phase, L, elem_off=o, allgather=ag_b, allgather_off=8)
+        torch.cuda.synchronize()
+        cw, cb = whole.control(), buck.control()
+        tag = f"step {step}"
+        assert cw["overflow"] == cb["overflow"] == int(ovf), tag
+        assert cw["t"] == cb["t"] == ref.t and cw["skipped"] == cb["skipped"], tag
+        for a, b in zip(whole.committed(cw), buck.committed(cb)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), tag
+        assert torch.equal(ag_w.view(torch.int16), ag_b.view(torch.int16)), tag
+        if not ovf:
+            assert cw["sumsq"] == pytest.approx(sq_want, rel=1e-12), tag
+            assert cb["sumsq"] == pytest.approx(sq_want, rel=1e-12), tag
+        p, m, v = (x[tidx].cpu().numpy() for x in whole.committed(cw))
+        for got, want, nm in ((p, ref.p, "p"), (m, ref.m, "m"), (v, ref.v, "v")):
+            assert_state_close(got, want, f"{tag} {nm}")
+        bits = ag_w.view(torch.int16)[8 + tidx].cpu().numpy().view(np.uint16)
+        assert_fp16_close(bits, ref.window().view(np.uint16), f"{tag} window")
+    assert ref.flags == [0, 1] and ref.t == 1
+    del whole, buck, ag_w, ag_b, dsl
+    torch.cuda.empty_cache()
