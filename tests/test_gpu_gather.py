@@ -101,6 +101,39 @@ def test_gather_unused_windows_may_be_null():
         B.gather_params(sparse, part, 0, 10, out)  # window 0 is needed
 
 
+class _DeviceSlices:
+    """A device window that the oracle reads by slices: each slice is copied
+    to the host on demand, so windows of several GB need not be."""
+
+    def __init__(self, t):
+        self.t = t
+        self.dtype = np.float16
+
+    def __getitem__(self, sl):
+        return self.t[sl].cpu().numpy()
+
+
+def test_gather_past_int32_offsets():
+    """Two windows of 2^31 + 4096 elements: ranges whose offsets, in the
+    flat buffer and inside a window, pass the int32 range (a window edge
+    at 2^31 + 4096, the end of the flat buffer near 2^32, a 64M-element
+    range across the edge), on both copy paths."""
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    torch.cuda.empty_cache()
+    nd, part = 2, (1 << 31) + 4096
+    ws = _windows(torch, nd, part, 31)
+    wh = [_DeviceSlices(w) for w in ws]
+    cases = [(part - 1000, part + 3000), (2 * part - 5003, 2 * part), ((1 << 31) - 8, (1 << 31) + 8200),
+             (part - (1 << 25), part + (1 << 25))]
+    for lo, hi in cases:
+        for dst_off in (0, 8, 3):
+            say(f"[{lo}, {hi}) dst+{dst_off}")
+            _gather_check(torch, B, ws, wh, part, lo, hi, dst_off, f"[{lo}, {hi}) dst+{dst_off}")
+    del ws, wh
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("key", ["c2", "c3"])
 def test_gather_every_layer_full(key):
     """Every layer of the GPT-2 shaped list, gathered from the Nd windows of
