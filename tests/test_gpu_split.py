@@ -40,7 +40,8 @@ def say(msg):
 
 def _sample_idx(n):
     g = np.random.default_rng(5)
-    near = (np.arange(0, n, 1024, dtype=np.int64)[:, None] + np.arange(-4, 4, dtype=np.int64)).ravel()
+    every = 1024 if n <= (1 << 26) else (1 << 20)  # the oracle's share stays at seconds
+    near = (np.arange(0, n, every, dtype=np.int64)[:, None] + np.arange(-4, 4, dtype=np.int64)).ravel()
     idx = np.unique(np.concatenate([near, g.integers(0, n, 1 << 15, dtype=np.int64),
                                     np.arange(n - 16, n, dtype=np.int64)]))
     return idx[(idx >= 0) & (idx < n)]
@@ -116,21 +117,27 @@ def test_long_window_split_launches(nd, n, dynamic):
 
 
 def _sumsq32(torch, slices):
-    g = (slices.to(torch.float64).sum(0) * (1.0 / L)).to(torch.float32).to(torch.float64)
-    return float((g * g).sum().item())
+    tot = 0.0
+    for c in range(0, slices.shape[1], 1 << 27):
+        g = (slices[:, c:c + (1 << 27)].to(torch.float64).sum(0) * (1.0 / L)).to(torch.float32).to(torch.float64)
+        tot += float((g * g).sum().item())
+    return tot
 
 
-@pytest.mark.parametrize("nd,n", SPLITS)
+@pytest.mark.parametrize("nd,n", SPLITS + [(1, (1 << 31) + 5003)])
 def test_long_window_clipped_split(nd, n):
     """The clipped step on a long window, its passes split into launches
-    (the reduce pass by the slice count's rule, the update pass past 2^25):
-    sampled elements (dense around every multiple of 1024) against the
+    (the reduce pass by the slice count's rule, the update pass past 2^25),
+    also on a window of 2^31 + 5003 elements, past the int32 range:
+    sampled elements (dense around every multiple of 1024, or of 2^20 on
+    windows longer than 2^26) against the
     oracle given the window's norm from a float64 torch sum of the fp32
     gradients; the sum of squares and the clip coefficient within 1e-12
     (a piece missing from the norm would move both); a skipped step leaves
     state and window bit-identical."""
     torch = torch_mod()
     from zero_partitioned_mixed_buffer_amd import OwnedShard
+    torch.cuda.empty_cache()
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=0.5)
     master = torch.empty(n, dtype=torch.float32, device="cuda")
     gen.device_fill_params(master, 321, 0.02, n)
@@ -146,7 +153,7 @@ def test_long_window_clipped_split(nd, n):
         gen.device_fill_grads(dsl, 78, step, 1e-3, L, "normal", n)
         injected = step == 2
         if injected:
-            dsl[2, 2] = float("-inf")  # in the first launch of the split (sampled)
+            dsl[min(2, nd - 1), 2] = float("-inf")  # in the first launch of the split (sampled)
         sq32 = None if injected else _sumsq32(torch, dsl)
         ovf, _ = ref.step(dsl[:, tidx].cpu().numpy(), L, window_sumsq=sq32)
         assert ovf == injected
