@@ -262,7 +262,8 @@ def test_determinism_two_runs():
 
 def test_fused_step_nd400_small_window():
     """Nd = 400 (the largest configuration's slice count) on a small ragged
-    window: 25 chunks of 16 slices per group."""
+    window: 200 chunks of 2 slices per element group, in visits of 8 groups
+    (two full visits and a 3-element tail)."""
     _run_case(4099, 400, steps=2, seed=400, L=2048.0, sigma=1e-4, dist="student_t3")
 
 
@@ -411,8 +412,8 @@ def test_restore_skipped_second_window():
 
 def test_largest_nd():
     """Nd = 8191, the largest the library accepts (float64 holds the sum of
-    fewer than 2^13 fp16 values exactly): 511 full chunks of 16 slices and a
-    remainder of 15.  One element carries 65504 in every slice (the largest
+    fewer than 2^13 fp16 values exactly): 4095 chunks of 2 slices and a
+    remainder of 1.  One element carries 65504 in every slice (the largest
     finite fp16, sum 8191 * 65504), another alternating +-65504 (sum 65504);
     the step must match the oracle and stay finite."""
     nd, n = 8191, 1001
