@@ -60,9 +60,9 @@ def parse():
     ap.add_argument("--gather-layers", action="store_true",
                     help="time the Pos+g+p on-demand gather of every layer (GPT-2 shaped workloads) "
                          "instead of the step")
-    ap.add_argument("--gather-streams", type=int, default=1, choices=(1, 2),
-                    help="with --gather-layers: 2 alternates the layers between two streams (layer buffer "
-                         "k %% 2 on stream k %% 2), so one layer's gather overlaps the next one's launch")
+    ap.add_argument("--gather-streams", type=int, default=1, choices=(1, 2, 3, 4),
+                    help="with --gather-layers: N > 1 rotates the layers over N streams (layer buffer "
+                         "k %% N on stream k %% N), so one layer's gather overlaps the next ones' launches")
     a = ap.parse_args()
     if a.bucket_elems < 0 or a.bucket_elems % 8 or (a.bucket_elems and a.max_grad_norm > 0):
         ap.error("--bucket-elems must be a multiple of 8, and cannot be combined with clipping")
@@ -232,8 +232,9 @@ def cpu_baseline_gather(w, windows, part, ranges, budget_s):
 def bench_gather(args):
     """Pos+g+p: gather every layer of a GPT-2 shaped list (one forward's
     worth of on-demand gathers, Psi elements) from the Nd owners' windows
-    into two constant-size layer buffers used alternately (a layer buffer is
-    released by reusing it two layers later)."""
+    into constant-size layer buffers used in turn, one per stream and at
+    least two (a layer buffer is released by reusing it that many layers
+    later)."""
     import torch
     from workloads import configs, gen
     from zero_partitioned_mixed_buffer_amd import binding as B
@@ -259,17 +260,21 @@ def bench_gather(args):
             del t
         sets.append(ws)
     biggest = max(hi - lo for lo, hi in ranges)
-    bufs = [torch.empty(biggest, dtype=torch.float16, device=dev) for _ in range(2)]
+    nbuf = max(2, args.gather_streams)
+    bufs = [torch.empty(biggest, dtype=torch.float16, device=dev) for _ in range(nbuf)]
     stream = torch.cuda.current_stream()
     # layer buffer b is only ever written on streams[b], so reuse is ordered
-    streams = [stream, torch.cuda.Stream()] if args.gather_streams == 2 else [stream, stream]
+    if args.gather_streams > 1:
+        streams = [stream] + [torch.cuda.Stream() for _ in range(nbuf - 1)]  # default priority
+    else:
+        streams = [stream] * nbuf
     log(f"gather: {w.key}, {len(ranges)} layers (largest {biggest} elements), Nd={w.nd} windows of {part}, "
         f"{copies} window set(s), {args.gather_streams} stream(s)")
 
     def one_pass(i):
         ws = sets[i % copies]
         for k, (lo, hi) in enumerate(ranges):
-            B.gather_params(ws, part, lo, hi, bufs[k % 2], streams[k % 2])
+            B.gather_params(ws, part, lo, hi, bufs[k % nbuf], streams[k % nbuf])
 
     for i in range(args.warmup):
         one_pass(i)
@@ -277,12 +282,14 @@ def bench_gather(args):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
-    streams[1].wait_event(e0)
+    side = [st for st in streams[1:] if st is not stream]
+    for st in side:
+        st.wait_event(e0)
     for i in range(args.steps):
         one_pass(args.warmup + i)
-    if streams[1] is not stream:
+    for st in side:
         done = torch.cuda.Event()
-        done.record(streams[1])
+        done.record(st)
         stream.wait_event(done)
     e1.record(stream)
     torch.cuda.synchronize()
