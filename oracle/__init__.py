@@ -17,5 +17,6 @@ from .zero_oracle import (  # noqa: F401
     scaler_update,
     clip_coefficient,
     clipped_gradient,
+    reduced_fp32,
     gather,
 )

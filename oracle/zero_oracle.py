@@ -27,8 +27,11 @@ accumulation precision, the overflow policy) the plainest reading is taken:
             2^16 in magnitude, so the float64 sum is exact for Nd < 8192 and
             any order gives the same bits (up to the sign of a zero sum, which
             the left-to-right order fixes).
-* unscale:  g = s * (1/L);  overflow = any(!isfinite(s)) over the window;
-            sumsq = sum of g*g, summed exactly and rounded once (math.fsum).
+* unscale:  g = s * (1/L);  overflow = any(!isfinite(g)) over the window
+            (every non-finite s gives a non-finite g, and so does a scale
+            whose reciprocal overflows, such as a dynamic scale backed off
+            to 0); sumsq = sum of g*g, summed exactly and rounded once
+            (math.fsum).
 * Adam:     bias-corrected Adam with eps added after the square root of the
             corrected second moment, AdamW-style decoupled weight decay
             p * (1 - lr*wd).  All arithmetic in float64, one IEEE operation at
@@ -43,10 +46,12 @@ accumulation precision, the overflow policy) the plainest reading is taken:
 * scaler:   dynamic loss scaling (mixed-precision practice): an overflowing
             step multiplies the scale by the backoff factor and resets the
             clean-step count; every `interval` consecutive clean steps
-            multiply it by the growth factor.  The gradients of a step carry
-            the scale in force when the step starts.
+            multiply it by the growth factor (the old scale stays if the
+            grown one is not finite) and reset the count.  The gradients of
+            a step carry the scale in force when the step starts.
 * clip:     global-norm clipping needs the norm before the update, so the
-            reduced gradient is materialised as fp32 (g32 = fp32(s * (1/L))),
+            reduced gradient is materialised as fp32 (g32 = fp32(s * (1/L)),
+            overflow = any(!isfinite(g32))),
             its norm is sqrt(sum g32^2) (exact sum, rounded once), and the
             update uses g32 * min(1, max_norm / (norm + 1e-6)) in float64.
 * emit:     allgather[off + j] = fp16 round-to-nearest-even of the fp32 master.
@@ -175,18 +180,30 @@ def reduce_owned(slices: np.ndarray) -> np.ndarray:
     return s
 
 
+def _inverse(loss_scale: float) -> float:
+    """1/L in float64; a scale of 0 (a dynamic scale backed off that far)
+    or one whose reciprocal overflows gives inf."""
+    if not (loss_scale >= 0 and math.isfinite(loss_scale)):
+        raise ValueError("loss scale must be non-negative and finite")
+    with np.errstate(divide="ignore", over="ignore"):
+        return float(np.float64(1.0) / np.float64(loss_scale))
+
+
 def unscale(s: np.ndarray, loss_scale: float):
-    """Returns (g, overflow, sumsq).  Overflow is any non-finite reduced value
-    (mixed-precision practice cited by the anthology note, "Connections":
-    Micikevicius et al.).  sumsq is meaningful only without overflow."""
-    if not (loss_scale > 0 and math.isfinite(loss_scale)):
-        raise ValueError("loss scale must be positive and finite")
-    inv = 1.0 / float(loss_scale)
-    overflow = bool(np.any(~np.isfinite(s)))
-    g = s * inv
+    """Returns (g, overflow, sumsq).  Overflow is any non-finite unscaled
+    gradient (mixed-precision practice cited by the anthology note,
+    "Connections": Micikevicius et al.): every non-finite reduced value gives
+    one, and so does a scale whose reciprocal is not finite.  sumsq is
+    meaningful only without overflow."""
+    inv = _inverse(loss_scale)
+    with np.errstate(invalid="ignore", over="ignore"):
+        g = s * inv
+    overflow = bool(np.any(~np.isfinite(g)))
     if overflow:
         return g, True, float("nan")
-    return g, False, math.fsum((g * g).tolist())
+    with np.errstate(over="ignore"):
+        gg = g * g
+    return g, False, math.fsum(gg.tolist())
 
 
 # --------------------------------------------------------------------------
@@ -265,12 +282,15 @@ def gather(windows: Sequence[np.ndarray], part: int, lo: int, hi: int) -> np.nda
 
 def scaler_update(scale: float, good: int, overflow: bool, growth: float, backoff: float,
                   interval: int):
-    """Next (scale, good_steps) after a step with the given overflow flag."""
+    """Next (scale, good_steps) after a step with the given overflow flag.
+    A growth that would make the scale non-finite keeps the old scale (the
+    count still resets); a backoff is applied as it falls, down to 0."""
     if overflow:
         return scale * backoff, 0
     good += 1
     if good == interval:
-        return scale * growth, 0
+        grown = scale * growth
+        return (grown if math.isfinite(grown) else scale), 0
     return scale, good
 
 
@@ -284,22 +304,33 @@ def clip_coefficient(sumsq: float, max_norm: float) -> float:
     return c if c < 1.0 else 1.0
 
 
+def reduced_fp32(s: np.ndarray, loss_scale: float):
+    """First pass of the clipping path over reduced values s: returns (g32,
+    overflow, sumsq) with g32 = fp32(s * (1/L)) (as an fp32 gradient buffer
+    holds it), overflow = any non-finite g32, and sumsq = sum g32^2 summed
+    exactly and rounded once (NaN on overflow)."""
+    inv = _inverse(loss_scale)
+    with np.errstate(invalid="ignore", over="ignore"):
+        g32 = (s * inv).astype(F32)
+    if bool(np.any(~np.isfinite(g32))):
+        return g32, True, float("nan")
+    g64 = g32.astype(F64)
+    return g32, False, math.fsum((g64 * g64).tolist())
+
+
 def clipped_gradient(s: np.ndarray, loss_scale: float, max_norm: float, window_sumsq: float = None):
     """Two-pass gradient of the clipping path: returns (g, overflow, sumsq,
     coef) with g the float64 gradient the update uses.  The norm is the
     whole window's: when `s` holds only a sample of the window's elements,
     `window_sumsq` supplies the window's sum of g32^2 (computed elsewhere
     from the same inputs)."""
-    inv = 1.0 / float(loss_scale)
-    overflow = bool(np.any(~np.isfinite(s)))
-    with np.errstate(invalid="ignore", over="ignore"):
-        g32 = (s * inv).astype(F32)
+    g32, overflow, sumsq = reduced_fp32(s, loss_scale)
     if overflow:
         return None, True, float("nan"), float("nan")
-    g64 = g32.astype(F64)
-    sumsq = math.fsum((g64 * g64).tolist()) if window_sumsq is None else float(window_sumsq)
+    if window_sumsq is not None:
+        sumsq = float(window_sumsq)
     coef = clip_coefficient(sumsq, max_norm)
-    return g64 * coef, False, sumsq, coef
+    return g32.astype(F64) * coef, False, sumsq, coef
 
 
 class OwnedShard:
@@ -333,20 +364,54 @@ class OwnedShard:
         return emit(self.p.astype(F32))
 
     def step(self, slices: np.ndarray, loss_scale: float = None, window_sumsq: float = None):
-        """One step.  With dynamic scaling (scale_interval > 0) the slices
-        carry self.scale and `loss_scale` is ignored.  `window_sumsq`: see
-        clipped_gradient (a shard that holds a sample of a window)."""
+        """One step over the whole window: ``slices`` [Nd, S].  With dynamic
+        scaling (scale_interval > 0) the slices carry self.scale and
+        `loss_scale` is ignored.  `window_sumsq`: see clipped_gradient (a
+        shard that holds a sample of a window)."""
+        slices = np.asarray(slices)
+        return self.step_chunks([(0, slices.shape[1], slices)], loss_scale, window_sumsq)
+
+    def step_chunks(self, chunks, loss_scale: float = None, window_sumsq: float = None, pmap=map):
+        """The same step with the window's slices given in column chunks:
+        ``chunks`` yields (lo, hi, slices[:, lo:hi]) tiling [0, S) in order,
+        so that a window too large for one [Nd, S] host array can be
+        stepped.  Elements are independent; the only window-wide results
+        are the flag (set if any chunk's is) and the sum of g^2: each
+        chunk's exact sum, added with math.fsum (one chunk gives the exact
+        sum of the window).  ``pmap`` maps the per-chunk work over the
+        chunks: the built-in map, or a thread pool's (chunks share
+        nothing).  Returns (skipped, sumsq)."""
         dynamic = self.scale_interval > 0
         L = self.scale if dynamic else float(loss_scale)
+        clip = self.max_grad_norm > 0
         self.scales.append(L)
-        s = reduce_owned(slices)
-        if s.shape[0] != self.p.shape[0]:
+
+        def reduce_chunk(chunk):
+            lo, hi, sl = chunk
+            s = reduce_owned(sl)
+            if s.shape[0] != hi - lo:
+                raise ValueError("chunk width mismatch")
+            g, ovf, sq = reduced_fp32(s, L) if clip else unscale(s, L)
+            return lo, hi, g, ovf, sq
+
+        parts = list(pmap(reduce_chunk, chunks))
+        pos = 0
+        for lo, hi, _, _, _ in parts:
+            if lo != pos:
+                raise ValueError("chunks must tile the window in order")
+            pos = hi
+        if pos != self.p.shape[0]:
             raise ValueError("window size mismatch")
-        if self.max_grad_norm > 0:
-            g, overflow, sq, coef = clipped_gradient(s, L, self.max_grad_norm, window_sumsq)
-        else:
-            g, overflow, sq = unscale(s, L)
-            coef = 1.0
+        overflow = any(ovf for _, _, _, ovf, _ in parts)
+        sq = float("nan") if overflow else math.fsum(x for _, _, _, _, x in parts)
+        coef = 1.0
+        if clip:
+            if overflow:
+                coef = float("nan")
+            else:
+                if window_sumsq is not None:
+                    sq = float(window_sumsq)
+                coef = clip_coefficient(sq, self.max_grad_norm)
         self.flags.append(int(overflow))
         self.sumsq.append(sq)
         self.coefs.append(coef)
@@ -359,7 +424,17 @@ class OwnedShard:
         sc = step_scalars(self.hp["lr"], self.hp["beta1"], self.hp["beta2"],
                           self.hp["eps"], self.hp["weight_decay"],
                           self.b1_pow, self.b2_pow)
-        self.p, self.m, self.v = adam_update(self.p, self.m, self.v, g, sc)
+        p1, m1, v1 = (np.empty_like(x) for x in (self.p, self.m, self.v))
+
+        def update_chunk(part):
+            lo, hi, g = part[0], part[1], part[2]
+            if clip:
+                g = g.astype(F64) * coef
+            p1[lo:hi], m1[lo:hi], v1[lo:hi] = adam_update(self.p[lo:hi], self.m[lo:hi], self.v[lo:hi], g, sc)
+
+        for _ in pmap(update_chunk, parts):
+            pass
+        self.p, self.m, self.v = p1, m1, v1
         self.t += 1
         self.b1_pow = sc["b1t"]
         self.b2_pow = sc["b2t"]

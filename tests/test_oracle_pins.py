@@ -63,6 +63,77 @@ def test_memory_stage_structure():
     assert oracle.memory_model(psi, 8, 2)["comm_elems_ring"] == 2 * psi * 7 / 8
 
 
+def _ring_reduce_scatter(bufs, sent):
+    """Ring reduce-scatter of Nd equal-length vectors (one per rank), run
+    step by step: in step k rank r sends its partial of chunk (r - k) mod Nd
+    to rank r + 1, which adds it to its own.  After Nd - 1 steps rank r holds
+    the full sum of chunk (r + 1) mod Nd.  sent[r] counts the elements rank
+    r put on the wire."""
+    nd = len(bufs)
+    n = bufs[0].size // nd
+    acc = [b.astype(F64).copy() for b in bufs]
+    for k in range(nd - 1):
+        msgs = []
+        for r in range(nd):
+            c = (r - k) % nd
+            msgs.append((r, c, acc[r][c * n:(c + 1) * n].copy()))
+        for r, c, m in msgs:
+            dst = (r + 1) % nd
+            acc[dst][c * n:(c + 1) * n] += m
+            sent[r] += m.size
+    return {(r + 1) % nd: acc[r][((r + 1) % nd) * n:((r + 1) % nd + 1) * n] for r in range(nd)}
+
+
+def _ring_all_gather(owned, nd, n, sent):
+    """Ring all-gather: rank r starts with its chunk r; in step k it sends
+    chunk (r - k) mod Nd to rank r + 1.  Returns every rank's full vector."""
+    full = [np.full(nd * n, np.nan) for _ in range(nd)]
+    for r in range(nd):
+        full[r][r * n:(r + 1) * n] = owned[r]
+    for k in range(nd - 1):
+        msgs = [(r, (r - k) % nd) for r in range(nd)]
+        data = [full[r][c * n:(c + 1) * n].copy() for r, c in msgs]
+        for (r, c), m in zip(msgs, data):
+            full[(r + 1) % nd][c * n:(c + 1) * n] = m
+            sent[r] += m.size
+    return full
+
+
+@pytest.mark.parametrize("nd", [1, 2, 3, 8, 13])
+def test_ring_volume_by_simulation(nd):
+    """The ring variant of the communication volume, counted rather than
+    computed: a ring reduce-scatter and ring all-gathers are run on data
+    (their results are checked), the elements each rank sends are tallied,
+    and the tally per stage (Pos / Pos+g: one reduce-scatter + one
+    all-gather; Pos+g+p: two parameter all-gathers + one reduce-scatter) is
+    compared with comm_elems_ring.  A factor such as Nd/(Nd-1) or
+    2(Nd-1)/Nd per collective would fail here."""
+    g = np.random.default_rng(nd)
+    n = 5
+    psi = nd * n
+    grads = [g.integers(-50, 50, psi).astype(F64) for _ in range(nd)]
+    sent_rs = np.zeros(nd, dtype=np.int64)
+    owned = _ring_reduce_scatter(grads, sent_rs)
+    total = np.sum(grads, axis=0)
+    for r in range(nd):
+        assert np.array_equal(owned[r], total[r * n:(r + 1) * n])
+    params = g.standard_normal(psi)
+    sent_ag = np.zeros(nd, dtype=np.int64)
+    full = _ring_all_gather([params[r * n:(r + 1) * n] for r in range(nd)], nd, n, sent_ag)
+    for r in range(nd):
+        assert np.array_equal(full[r], params)
+    # every rank sends the same amount in each collective
+    assert len(set(sent_rs)) == 1 and len(set(sent_ag)) == 1
+    per_stage = {0: sent_rs[0] + sent_ag[0], 1: sent_rs[0] + sent_ag[0], 2: sent_rs[0] + sent_ag[0],
+                 3: sent_rs[0] + 2 * sent_ag[0]}
+    for stage, want in per_stage.items():
+        r = oracle.memory_model(psi, nd, stage)
+        assert r["comm_elems_ring"] == pytest.approx(float(want), rel=1e-15, abs=1e-9)
+        # and the nominal volume is the ring's without the (Nd-1)/Nd factor
+        assert r["comm_elems"] == pytest.approx(float(want) * nd / max(nd - 1, 1) if nd > 1 else
+                                                r["comm_elems"], rel=1e-15)
+
+
 # ----------------------------------------------------------------- planner
 @pytest.mark.parametrize("align", [8, 256])
 def test_plan_bruteforce(align):
@@ -466,6 +537,62 @@ def test_scaler_matches_torch_amp_update():
             assert scale == float(ts.item()) and good == int(tt.item())
 
 
+def test_scaler_limits_match_torch():
+    """Near the limits: a growth that overflows keeps the scale and still
+    resets the count, and a backoff falls to 0 without a floor, as torch's
+    update does at its own (float32) limits; the oracle's scale is float64."""
+    torch = pytest.importorskip("torch")
+    ts = torch.tensor([2.0 ** 127], dtype=torch.float32)
+    tt = torch.tensor([2], dtype=torch.int32)
+    torch._amp_update_scale_(ts, tt, torch.tensor([0.0]), 2.0, 0.5, 3)
+    assert float(ts.item()) == 2.0 ** 127 and int(tt.item()) == 0
+    assert oracle.scaler_update(2.0 ** 1023, 2, False, 2.0, 0.5, 3) == (2.0 ** 1023, 0)
+    assert oracle.scaler_update(2.0 ** 1022, 2, False, 2.0, 0.5, 3) == (2.0 ** 1023, 0)
+    ts = torch.tensor([2.0 ** -149], dtype=torch.float32)
+    torch._amp_update_scale_(ts, tt, torch.tensor([1.0]), 2.0, 0.5, 3)
+    assert float(ts.item()) == 0.0 and int(tt.item()) == 0
+    assert oracle.scaler_update(2.0 ** -1074, 5, True, 2.0, 0.5, 3) == (0.0, 0)
+    assert oracle.scaler_update(0.0, 0, True, 2.0, 0.5, 3) == (0.0, 0)
+
+
+def test_flag_on_unscaled_gradient():
+    """The overflow flag is raised by any non-finite unscaled gradient: a
+    finite sum with a scale whose reciprocal overflows (2^-1074: 1/L = inf;
+    0 after a long backoff) gives g = +-inf, or NaN for a zero sum, and the
+    step is flagged; with a normal scale the flag is exactly the non-finite
+    sums.  A flag on the sums alone would pass these steps and commit NaN."""
+    s = np.array([0.0, 1.5, -3.0], dtype=F64)
+    for L in (2.0 ** -1074, 0.0):
+        g, ovf, _ = oracle.unscale(s, L)
+        assert ovf and np.isnan(g[0]) and np.isposinf(g[1]) and np.isneginf(g[2])
+        assert not np.any(~np.isfinite(s))  # the sums themselves are finite
+        _, ovf32, _, _ = oracle.clipped_gradient(s, L, 1.0)
+        assert ovf32
+    g, ovf, _ = oracle.unscale(s, 2.0 ** -1000)  # 1/L = 2^1000: finite
+    assert not ovf and g[1] == 1.5 * 2.0 ** 1000
+    g, ovf, _ = oracle.unscale(np.array([np.inf, 1.0]), 1024.0)
+    assert ovf
+    # fp32 overflow of a finite float64 gradient flags the clipped step only
+    big = np.array([1.0, 2.0 ** 100], dtype=F64)
+    assert not oracle.unscale(big, 2.0 ** -60)[1]
+    assert oracle.clipped_gradient(big, 2.0 ** -60, 1.0)[1]
+
+
+def test_dynamic_scale_backed_off_to_zero_skips():
+    """A dynamic scale that backs off to 0 skips every later step and never
+    writes the state: t stays 0, the state is bit-identical."""
+    g = np.random.default_rng(40)
+    p0 = g.standard_normal(64).astype(F32) * 0.02
+    sh = oracle.OwnedShard(p0, scale_interval=2, loss_scale=2.0 ** -1074)
+    sl = (g.standard_normal((3, 64)) * 10).astype(F16)
+    for _ in range(4):
+        ovf, _ = sh.step(sl)
+        assert ovf
+    assert sh.t == 0 and sh.scales == [2.0 ** -1074, 0.0, 0.0, 0.0] and sh.scale == 0.0
+    assert np.array_equal(sh.p.view(np.uint32), p0.view(np.uint32))
+    assert not np.any(sh.m) and not np.any(sh.v)
+
+
 def test_clip_matches_torch_clip_grad_norm():
     torch = pytest.importorskip("torch")
     g = np.random.default_rng(32)
@@ -653,3 +780,38 @@ def test_clipped_sample_with_window_norm_matches_full_window():
     alone = oracle.OwnedShard(master[idx], max_grad_norm=0.05)
     alone.step(sl[:, idx], 1024.0)
     assert alone.coefs[-1] != full.coefs[-1]
+
+
+@pytest.mark.parametrize("clip", [0.0, 0.05])
+def test_step_chunks_matches_whole_window(clip):
+    """The chunked step (column chunks of uneven width, mapped over a thread
+    pool) gives the whole-window step's state bit for bit, the same flags,
+    scale trajectory and step count, and the same sum of g^2 up to the
+    rounding of adding the chunks' exact sums (and through the clip
+    coefficient, within one fp32 rounding of the state)."""
+    from concurrent.futures import ThreadPoolExecutor
+    g = np.random.default_rng(90)
+    n, nd = 10007, 5
+    p0 = (g.standard_normal(n) * 0.02).astype(F32)
+    hp = dict(weight_decay=0.01, max_grad_norm=clip, scale_interval=2, loss_scale=1024.0)
+    a, b = oracle.OwnedShard(p0, **hp), oracle.OwnedShard(p0, **hp)
+    edges = [0, 1, 8, 4096, 4100, 9000, n]
+    with ThreadPoolExecutor(4) as ex:
+        for step in range(1, 6):
+            sl = (g.standard_normal((nd, n)) * 1e-3 * a.scale).astype(F16)
+            if step == 3:
+                sl[2, 4099] = np.inf
+            ra = a.step(sl)
+            chunks = [(lo, hi, sl[:, lo:hi]) for lo, hi in zip(edges, edges[1:])]
+            rb = b.step_chunks(chunks, pmap=ex.map)
+            assert ra[0] == rb[0]
+            if not ra[0]:
+                assert rb[1] == pytest.approx(ra[1], rel=1e-15)
+            assert a.t == b.t and a.flags == b.flags and a.scales == b.scales
+            tol = 0.0 if clip == 0 else 1.2e-7
+            for x, y in ((a.p, b.p), (a.m, b.m), (a.v, b.v)):
+                d = np.abs(x.astype(F64) - y.astype(F64))
+                assert np.all(d <= tol * np.abs(x.astype(F64)))
+    assert a.flags == [0, 0, 1, 0, 0]
+    with pytest.raises(ValueError):
+        b.step_chunks([(0, 8, sl[:, :8]), (9, n, sl[:, 9:])])
