@@ -150,7 +150,7 @@ typedef struct zero_grad_src {
     int64_t n;              /* window length S >= 0 (any value; a tail of n % 8 is handled) */
     int32_t nd;             /* number of slices, 1 <= nd < 8192 (the float64 sum is exact below 2^13 terms) */
     int32_t reserved;       /* must be 0 */
-    double loss_scale;      /* L > 0 and finite; g = s * (1/L) */
+    double loss_scale;      /* L > 0, L and 1/L finite; g = s * (1/L) */
 } zero_grad_src;
 
 /* ---- workspace ----------------------------------------------------------
@@ -165,7 +165,7 @@ int64_t zero_workspace_bytes(void);
 
 /* ---- reduce (decomposed path) ---------------------------------------
  * s_j = G_0[j] + ... + G_{Nd-1}[j] (exact, float64), g_j = s_j * (1/L),
- * *overflow = 1 if any s_j is inf/NaN else 0, *sumsq = sum_j g_j^2 (float64,
+ * *overflow = 1 if any fp32(g_j) is inf/NaN (so any inf/NaN s_j) else 0, *sumsq = sum_j g_j^2 (float64,
  * deterministic order).  Pos+g: a gradient partition is summed on its
  * owning rank alone (upskillscore "How it works").
  *   grad_out: device float[n], 16-byte aligned, receives fp32(g); may be NULL.
@@ -219,7 +219,11 @@ typedef struct zero_adam_state {
  * gradients carry ctl->loss_scale (src->loss_scale is then ignored); after
  * each step the commit kernel multiplies the scale by scale_backoff if the
  * step overflowed (and resets good_steps), else counts the clean step and
- * multiplies the scale by scale_growth after scale_interval of them.
+ * multiplies the scale by scale_growth after scale_interval of them (and
+ * resets good_steps), keeping the old scale if the grown one is not finite
+ * (as torch's amp scaler does).  A scale backed off to 0 (or to a value
+ * whose reciprocal overflows) makes every g non-finite, so every later step
+ * is skipped and the state is never written with inf/NaN.
  *
  * Global-norm clipping (max_grad_norm > 0) is applied only by
  * zero_adam_step_clipped, which needs the norm before the update. */

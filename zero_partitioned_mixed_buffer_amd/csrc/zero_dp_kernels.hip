@@ -8,11 +8,17 @@
 // all-gather):
 //
 //   s_j  = G_0[j] + G_1[j] + ... + G_{Nd-1}[j]       exact in float64
-//   g_j  = s_j * (1/L);  flag |= !isfinite(s_j);  sumsq += g_j^2
+//   g_j  = s_j * (1/L);  flag |= !isfinite(g_j);  sumsq += g_j^2
 //   m'   = b1*m + (1-b1)*g          v' = b2*v + (1-b2)*(g*g)
 //   d    = sqrt(v') * (1/sqrt(1-b2^t)) + eps          q = m'/d
 //   p'   = p*(1-lr*wd) - (lr/(1-b1^t))*q
 //   fp32 stores of p', m', v';  allgather[off+j] = fp16(fp32(p'))
+//
+// The flag tests g, not s: a non-finite s always gives a non-finite g, and
+// so does a loss scale whose reciprocal overflows (a dynamic scale backed
+// off to 0 or to a subnormal), which then skips the step instead of
+// committing inf/NaN state.  Where g is stored as fp32 (the reduce pass),
+// the fp32 value is tested, which also catches an fp32 overflow.
 //
 // Every floating-point operation above is one IEEE float64 operation with
 // round-to-nearest-even; contraction into fused multiply-adds is disabled
@@ -324,9 +330,9 @@ __device__ __forceinline__ void reduce_finish(const double (&acc)[kV], const Src
     float gf[kV];
 #pragma unroll
     for (int e = 0; e < kV; ++e) {
-        bad |= !finite(acc[e]);
         const double g = acc[e] * src.inv_scale;
         gf[e] = static_cast<float>(g);
+        bad |= !finite(static_cast<double>(gf[e]));
         const double gn = kNormOfStored ? static_cast<double>(gf[e]) : g;
         sq += gn * gn;
     }
@@ -343,9 +349,9 @@ template <bool kNormOfStored>
 __device__ void reduce_tail(int64_t j, const SrcArgs& src, float* grad_out, double& sq, int& bad) {
     for (int64_t e = j; e < src.n; ++e) {
         const double s = sum_slices1(src.win + e, src.stride, src.nd);
-        bad |= !finite(s);
         const double g = s * src.inv_scale;
         const float g32 = static_cast<float>(g);
+        bad |= !finite(static_cast<double>(g32));
         const double gn = kNormOfStored ? static_cast<double>(g32) : g;
         sq += gn * gn;
         if (grad_out != nullptr) grad_out[e] = g32;
@@ -705,7 +711,9 @@ __device__ __forceinline__ void commit_step(const AdamArgs& a, int cur, double b
         } else {
             int g = w->good_steps + 1;
             if (g == a.interval) {
-                w->loss_scale = w->loss_scale * a.growth;
+                // as torch's amp scaler: a growth that overflows keeps the scale
+                const double grown = w->loss_scale * a.growth;
+                if (__builtin_isfinite(grown)) w->loss_scale = grown;
                 g = 0;
             }
             w->good_steps = g;
@@ -758,8 +766,8 @@ __device__ __forceinline__ void pf_finish(const hvec (&w)[R], const fvec& pv, co
     float po[kV], mo[kV], vo[kV];
 #pragma unroll
     for (int e = 0; e < kV; ++e) {
-        bad |= !finite(acc[e]);
         const double g = acc[e] * src.inv_scale;
+        bad |= !finite(g);
         sq += g * g;
         adam1(c, g, pv[e], mv[e], vv[e], po[e], mo[e], vo[e]);
     }
@@ -876,8 +884,8 @@ __device__ void fused_elems(int64_t e0, int64_t e1, const SrcArgs& src, const Fu
                             const AdamScalars& c, double& sq, int& bad) {
     for (int64_t e = e0; e < e1; ++e) {
         const double s = sum_slices1(src.win + e, src.stride, src.nd);
-        bad |= !finite(s);
         const double g = s * src.inv_scale;
+        bad |= !finite(g);
         sq += g * g;
         float po, mo, vo;
         adam1(c, g, f.pin[e], f.min_[e], f.vin[e], po, mo, vo);
@@ -911,8 +919,8 @@ __device__ __forceinline__ void visit_finish(const double (&acc)[U][kV], const f
         float po[kV], mo[kV], vo[kV];
 #pragma unroll
         for (int e = 0; e < kV; ++e) {
-            bad |= !finite(acc[u][e]);
             const double g = acc[u][e] * src.inv_scale;
+            bad |= !finite(g);
             sq += g * g;
             adam1(c, g, pv[u][e], mv[u][e], vv[u][e], po[e], mo[e], vo[e]);
         }
@@ -1393,7 +1401,9 @@ int check_src(const zero_grad_src* src, Range* span) {
         src->reserved != 0)
         return ZERO_EINVAL;
     if (src->base == nullptr && src->n != 0) return ZERO_EINVAL;
-    if (!(src->loss_scale > 0.0) || !__builtin_isfinite(src->loss_scale)) return ZERO_EINVAL;
+    if (!(src->loss_scale > 0.0) || !__builtin_isfinite(src->loss_scale) ||
+        !__builtin_isfinite(1.0 / src->loss_scale))
+        return ZERO_EINVAL;
     if (src->nd > 1 && src->slice_stride < 0) return ZERO_EINVAL;
     if (!aligned16(src->base) || src->elem_off % 8 != 0) return ZERO_EALIGN;
     if (src->nd > 1 && src->slice_stride % 8 != 0) return ZERO_EALIGN;
