@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the ZeRO-DP owned-partition step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5]
 
 A step is one pass of the whole hot path over one batch of gradients:
 zero_adam_step, i.e. the fused reduce + unscale/flag/sum-of-squares + Adam +
@@ -15,6 +15,11 @@ device time of the step's two kernels, from HIP events around K
 back-to-back steps on the launch stream), and the oracle's rate on a
 bounded sample of the same workload on one host core (and, as
 cpu_baseline.all_cores, on every core the process may use, up to 16).
+The reported workload is the 60B-parameter shard at Nd = 400 (S =
+150,000,128 owned elements, 120 GB of slices), the largest that fits one
+GPU; with the plain fused step the other four workloads are timed too and
+reported under config.other_workloads, and a skipped step (an inf
+gradient, the window re-emitted) is timed apart under config.skipped_step.
 """
 from __future__ import annotations
 
@@ -40,7 +45,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", help="c1..c5 (c2 is the reported workload)")
+    ap.add_argument("--workload", default="c5",
+                    help="c1..c5; c5 (the 60B-parameter shard at Nd = 400, the largest workload that fits "
+                         "one GPU) is the reported one")
+    ap.add_argument("--others", default="c1,c2,c3,c4",
+                    help="plain fused step only: also time these workloads (fewer steps) and report them "
+                         "under config.other_workloads ('' = none)")
     ap.add_argument("--rotate", type=int, default=0,
                     help="gradient sets cycled through (0 = enough to exceed 1 GB of slices)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
@@ -200,13 +210,16 @@ def cpu_baseline_all_cores(w, n_sample, budget_s, max_grad_norm=0.0, scale_inter
     process loads the HIP library, so no child is made from a process that
     has touched the GPU."""
     import multiprocessing as mp
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(16, affinity))
     jobs = [(w.key, k, n_sample, budget_s, max_grad_norm, scale_interval) for k in range(cores)]
     with mp.get_context("fork").Pool(cores) as pool:
         res = pool.map(_oracle_share, jobs, chunksize=1)
     rate = sum(e / t for e, t in res)
     return {"value": rate, "unit": "elements/s", "cores": cores, "kind": "oracle",
-            "sample": f"{cores} processes, each stepping its own {n_sample}-element chunk of workload {w.key} "
+            "affinity_cores": affinity, "core_cap": 16,
+            "sample": f"{cores} processes (one per core this process may use, {affinity}, capped at 16), "
+                      f"each stepping its own {n_sample}-element chunk of workload {w.key} "
                       f"for {budget_s:.0f} s (numpy float64, one thread each)",
             "gbs": rate * (2 * w.nd + (34 if max_grad_norm > 0 else 26)) / 1e9}
 
@@ -324,28 +337,55 @@ def bench_gather(args):
     print(json.dumps(out), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: the step of one rank runs on one MI355X and no "
-              f"collective is part of this path (asked for --gpus {args.gpus})", file=sys.stderr)
-        sys.exit(2)
-    if args.gather_layers:
-        bench_gather(args)
-        return
+def host_cpu():
+    """The host CPU's model name (as lscpu prints it, from /proc/cpuinfo),
+    the cores this process may run on, and the cores the host has."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "affinity_cores": len(os.sched_getaffinity(0)), "host_cores": os.cpu_count()}
 
-    from workloads import configs, gen
 
-    w = configs.ALL[args.workload]
-    cpu_all = None
-    if not args.no_cpu_baseline:
-        # before torch and the HIP library are loaded: the worker processes are forked, and a fork
-        # taken after a library has started threads can inherit a held lock
-        n_pool = min(w.psi // w.nd, 1 << 21) if w.nd <= 64 else min(w.psi // w.nd, 1 << 16)
-        cpu_all = cpu_baseline_all_cores(w, n_pool, args.cpu_seconds / 2, args.max_grad_norm, args.dynamic_scale)
-        log(f"oracle: {cpu_all['value']:.3e} elements/s on {cpu_all['cores']} cores")
+STAGES = ("DP", "Pos", "Pos+g", "Pos+g+p")
 
+
+def memory_model_report(B, w):
+    """The library's memory and communication model (zero_memory_model) for
+    the workload's Psi and Nd: per-device model-state GB (1e9 bytes) of each
+    stage, the reduction against plain data parallelism, and the per-rank
+    communication volume in elements (nominal and over a ring)."""
+    rows = []
+    for st in range(4):
+        r = B.memory_model(w.psi, w.nd, st)
+        rows.append({"stage": STAGES[st],
+                     "params_gb": r["params_bytes"] / 1e9, "grads_gb": r["grads_bytes"] / 1e9,
+                     "optim_gb": r["optim_bytes"] / 1e9, "total_gb": r["total_bytes"] / 1e9,
+                     "total_gb_1dp": round(r["total_bytes"] / 1e9, 1),
+                     "reduction_vs_dp": r["reduction_vs_dp"],
+                     "comm_elems": r["comm_elems"], "comm_elems_ring": r["comm_elems_ring"]})
+    return {"psi": w.psi, "nd": w.nd, "k_bytes_per_param": 12, "stages": rows}
+
+
+def log_memory_model(mm):
+    log(f"memory model, Psi = {mm['psi']:.4g}, Nd = {mm['nd']}: " + " / ".join(
+        f"{r['stage']} {r['total_gb_1dp']:.1f} GB ({r['reduction_vs_dp']:.2f}x)" for r in mm["stages"]))
+    log("communication per rank and step: " + " / ".join(
+        f"{r['stage']} {r['comm_elems']:.4g} elements" for r in mm["stages"]))
+
+
+def measure_step(args, w, steps, warmup, graph=False, skip_timing=False):
+    """Allocates the workload's inputs and state on the GPU, times `steps`
+    whole steps after `warmup` untimed ones, frees everything, and returns
+    the measurements.  Nothing but the step's own launches runs on the
+    stream in the timed regions."""
     import torch
+    from workloads import gen
     from zero_partitioned_mixed_buffer_amd import OwnedShard, binding as B
     owner = w.owners[-1]
     plan, _ = B.plan_partitions(list(w.numels), w.nd, 256)
@@ -444,14 +484,14 @@ def main():
         # window of a skipped step)
         B.adam_step(srcs[i % rot], sh.state, sh.hp, ag, ag_offs[i % n_shards], sh.workspace, s)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
 
     # Timed region: K whole steps back to back, nothing else on the stream.
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        launch(args.warmup + i)
+    for i in range(steps):
+        launch(warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -460,70 +500,167 @@ def main():
     # cache release and a dispatch gap to every launch).
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for i in range(args.steps):
-        launch(args.warmup + args.steps + i)
+    for i in range(steps):
+        launch(warmup + steps + i)
     e1.record(stream)
     torch.cuda.synchronize()
-    kern_avg = e0.elapsed_time(e1) / args.steps
+    kern_avg = e0.elapsed_time(e1) / steps
     # Distribution: the same launches, each between its own pair of events
     # (the records add a little to every launch, so the mean above is the
     # figure reported; these are its spread).
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i in range(args.steps):
+           for _ in range(steps)]
+    for i in range(steps):
         evs[i][0].record(stream)
-        launch(args.warmup + 2 * args.steps + i)
+        launch(warmup + 2 * steps + i)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-    pct = lambda q: per[min(len(per) - 1, int(round(q * (len(per) - 1))))]
+    pct = lambda q: per[min(len(per) - 1, int(round(q * (len(per) - 1))))]  # noqa: E731
     ctls = [sh.control() for sh in shards]
-    if sum(c["t"] for c in ctls) != args.warmup + 3 * args.steps or any(c["skipped"] for c in ctls):
+    if sum(c["t"] for c in ctls) != warmup + 3 * steps or any(c["skipped"] for c in ctls):
         log(f"unexpected control state after timing: {ctls}")
         sys.exit(1)
 
     graph_us = None
-    if args.graph and not args.arrival:
+    if graph and not args.arrival:
         # the same K steps captured once in a HIP graph and replayed: the
         # launches are identical, only the host-side launch cost goes
-        base = args.warmup + 3 * args.steps
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for j in range(args.steps):
+        base = warmup + 3 * steps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(steps):
                 launch(base + j, torch.cuda.current_stream())
         for _ in range(2):
-            graph.replay()
+            g.replay()
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record(stream)
         for _ in range(3):
-            graph.replay()
+            g.replay()
         g1.record(stream)
         torch.cuda.synchronize()
-        graph_us = g0.elapsed_time(g1) * 1e3 / (3 * args.steps)
+        graph_us = g0.elapsed_time(g1) * 1e3 / (3 * steps)
         log(f"the same steps from a HIP graph: {graph_us:.1f} us per step")
-        del graph
+        del g
 
-    calibration_copy(torch, dev)
-    attain = attainable_copy(torch, dev, B)
-    log(f"attainable copy on this GPU: {attain['copy_gbs']:.0f} GB/s")
-    traffic = None if (clipped or bucketed) else measured_traffic(w.key)
+    skip = None
+    if skip_timing and not (clipped or bucketed or args.dynamic_scale):
+        # A step with an inf gradient (slice min(17, Nd-1), window element
+        # S/2): the fused pass runs as on any step, then the commit kernel
+        # skips it and re-emits the window from the committed master
+        # (6 more bytes per element).  Timed apart from the clean steps.
+        k, j = min(17, w.nd - 1), S // 2
+        sh = shards[0]
+        gs = gsets[0]
+        keep = gs[k, j].clone()
+        gs[k, j] = float("inf")
+        t_before = sh.control()["t"]
+        reps = 3
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(reps):
+            B.adam_step(srcs[0], sh.state, sh.hp, ag, ag_offs[0], sh.workspace, stream)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        c = sh.control()
+        gs[k, j] = keep
+        if c["t"] != t_before or c["skipped"] != reps or c["overflow"] != 1:
+            log(f"the injected step was not skipped: {c}")
+            sys.exit(1)
+        skip_us = s0.elapsed_time(s1) * 1e3 / reps
+        skip = {"step_us": skip_us, "extra_bytes_per_elem": 6,
+                "injected": f"+inf at slice {k}, window element {j}",
+                "extra_us_vs_clean": skip_us - kern_avg * 1e3}
+        log(f"skipped step (inf at slice {k}, element {j}): {skip_us:.1f} us "
+            f"({skip_us - kern_avg * 1e3:+.1f} us against a clean step; the re-emit moves 6 B per element)")
 
-    ms_step = wall * 1e3 / args.steps
     # algorithmic bytes per owned element: fused 2*Nd + 26; clipped
     # (2*Nd + 4) for the reduce pass + 30 for the update pass
     bytes_elem = 2 * w.nd + (34 if clipped else 26)
     achieved = bytes_elem * S / (kern_avg * 1e-3) / 1e9
     what = (f"bucketed step ({len(buckets)} launches + commit)" if bucketed else
             "clipped step (reduce + update + commit kernels)" if clipped else "fused step (fused + commit kernels)")
-    log(f"{what}: avg {kern_avg * 1e3:.1f} us over {args.steps} back-to-back steps; "
-        f"step {ms_step * 1e3:.1f} us; {achieved:.0f} GB/s")
+    ms_step = wall * 1e3 / steps
+    log(f"{w.key} {what}: avg {kern_avg * 1e3:.1f} us over {steps} back-to-back steps; "
+        f"step {ms_step * 1e3:.1f} us; {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.3f} of peak)")
+    res = {
+        "w": w, "S": S, "owner": owner, "rot": rot, "n_shards": n_shards, "full": full,
+        "ms_step": ms_step, "kern_avg_ms": kern_avg, "pcts_us": [pct(0.1), pct(0.5), pct(0.9)],
+        "bytes_elem": bytes_elem, "achieved_gbs": achieved, "graph_us": graph_us, "skip": skip,
+        "what": what, "n_buckets": len(buckets) if bucketed else 0,
+    }
+    del gsets, srcs, shards, ag
+    if bucketed:
+        del recv
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the step of one rank runs on one MI355X and no "
+              f"collective is part of this path (asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    if args.gather_layers:
+        bench_gather(args)
+        return
+
+    from workloads import configs
+
+    w = configs.ALL[args.workload]
+    cpu_all = None
+    if not args.no_cpu_baseline:
+        # before torch and the HIP library are loaded: the worker processes are forked, and a fork
+        # taken after a library has started threads can inherit a held lock
+        n_pool = min(w.psi // w.nd, 1 << 21) if w.nd <= 64 else min(w.psi // w.nd, 1 << 16)
+        cpu_all = cpu_baseline_all_cores(w, n_pool, args.cpu_seconds / 2, args.max_grad_norm, args.dynamic_scale)
+        log(f"oracle: {cpu_all['value']:.3e} elements/s on {cpu_all['cores']} cores")
+
+    import torch
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    dev = torch.device("cuda", 0)
+
+    clipped = args.max_grad_norm > 0
+    bucketed = args.bucket_elems > 0
+    plain = not (clipped or bucketed or args.dynamic_scale or args.arrival)
+    mm = memory_model_report(B, w)
+    log_memory_model(mm)
+
+    res = measure_step(args, w, args.steps, args.warmup, graph=args.graph, skip_timing=plain)
+    S = res["S"]
+
+    others = {}
+    if plain and args.others:
+        # the other workloads' whole steps, each in its own allocation (the
+        # headline's buffers are freed first), reported beside the headline
+        for key in [k for k in args.others.split(",") if k and k != w.key]:
+            wo = configs.ALL[key]
+            r = measure_step(args, wo, max(5, args.steps // 2), min(args.warmup, 3))
+            others[key] = {"workload": f"{wo.key}: {wo.title}", "owned_elems": r["S"], "nd": wo.nd,
+                           "bytes_per_elem": r["bytes_elem"], "step_us_events": r["kern_avg_ms"] * 1e3,
+                           "step_us_host": r["ms_step"] * 1e3, "hbm_gbs": r["achieved_gbs"],
+                           "frac_of_peak": r["achieved_gbs"] / PEAK_HBM_GBS,
+                           "elements_per_s": r["S"] / (r["ms_step"] * 1e-3)}
+
+    calibration_copy(torch, dev)
+    attain = attainable_copy(torch, dev, B)
+    log(f"attainable copy on this GPU: {attain['copy_gbs']:.0f} GB/s")
+    traffic = None if (clipped or bucketed) else measured_traffic(w.key)
+
+    kern_avg = res["kern_avg_ms"]
+    ms_step = res["ms_step"]
+    bytes_elem = res["bytes_elem"]
+    achieved = res["achieved_gbs"]
 
     cpu = None
     if not args.no_cpu_baseline:
         n_sample = min(S, 1 << 21) if w.nd <= 64 else min(S, 1 << 16)
         cpu = cpu_baseline(w, n_sample, args.cpu_seconds, args.max_grad_norm, args.dynamic_scale)
         log(f"oracle: {cpu['value']:.3e} elements/s on 1 core")
+        cpu["host"] = host_cpu()
         cpu["all_cores"] = cpu_all
 
     out = {
@@ -542,18 +679,21 @@ def main():
         "config": {
             "workload": f"{w.key}: {w.title}",
             "nd": w.nd,
-            "owner": owner,
+            "owner": res["owner"],
             "owned_elems": S,
             "bytes_per_elem": bytes_elem,
-            "grad_sets_rotated": rot,
-            "shards_rotated": n_shards,
-            "allgather": "full flat buffer" if full else "one window per shard",
+            "grad_sets_rotated": res["rot"],
+            "shards_rotated": res["n_shards"],
+            "allgather": "full flat buffer" if res["full"] else "one window per shard",
             "step_hbm_gbs": bytes_elem * S / (ms_step * 1e-3) / 1e9,
             "max_grad_norm": args.max_grad_norm,
             "dynamic_scale_interval": args.dynamic_scale,
             "bucket_elems": args.bucket_elems,
             "bucket_arrival_copies": bool(args.arrival),
-            "graph_step_us": graph_us,
+            "graph_step_us": res["graph_us"],
+            "skipped_step": res["skip"],
+            "memory_model": mm,
+            "other_workloads": others or None,
         },
         "roofline": {
             "bound": "hbm",
@@ -567,10 +707,10 @@ def main():
             "traffic_bytes_per_launch": traffic,
             "algorithmic_bytes_per_launch": bytes_elem * S,
             "kernel": ("reduce_owned_kernel + clipped_update_kernel + commit_kernel" if clipped else
-                       f"fused_step_kernel x {len(buckets)} buckets + commit_kernel" if bucketed else
+                       f"fused_step_kernel x {res['n_buckets']} buckets + commit_kernel" if bucketed else
                        "fused_step_kernel + commit_kernel"),
             "kernel_avg_us": kern_avg * 1e3,
-            "kernel_us_p10_p50_p90_per_launch_events": [pct(0.1), pct(0.5), pct(0.9)],
+            "kernel_us_p10_p50_p90_per_launch_events": res["pcts_us"],
             "attainable": attain,
             "frac_of_attainable": achieved / attain["copy_gbs"],
             "kernel_fingerprint": kernel_fingerprint(),

@@ -70,3 +70,26 @@ def test_all_cores_oracle_baseline_runs():
     assert r["kind"] == "oracle" and r["unit"] == "elements/s"
     assert 1 <= r["cores"] <= 16
     assert r["value"] > 0 and r["gbs"] > 0
+
+
+def test_memory_model_report_c4_prints_the_pages_table(capsys):
+    """The bench line's config.memory_model at the 7.5B-parameter, Nd = 64
+    workload: 120.0 / 31.4 / 16.6 / 1.9 GB, 2Psi = 1.5e10 and 3Psi =
+    2.25e10 elements, from the library's zero_memory_model."""
+    from workloads import configs
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    mm = bench.memory_model_report(B, configs.C4)
+    assert mm["psi"] == 7_500_000_000 and mm["nd"] == 64
+    assert [r["stage"] for r in mm["stages"]] == ["DP", "Pos", "Pos+g", "Pos+g+p"]
+    assert [r["total_gb_1dp"] for r in mm["stages"]] == [120.0, 31.4, 16.6, 1.9]
+    assert [r["comm_elems"] for r in mm["stages"]] == [1.5e10, 1.5e10, 1.5e10, 2.25e10]
+    assert mm["stages"][3]["reduction_vs_dp"] == 64.0
+    bench.log_memory_model(mm)
+    err = capsys.readouterr().err
+    assert "DP 120.0 GB" in err and "Pos 31.4 GB" in err and "Pos+g 16.6 GB" in err and "Pos+g+p 1.9 GB" in err
+    assert "2.25e+10 elements" in err and "1.5e+10 elements" in err
+
+
+def test_host_cpu_reports_model_and_affinity():
+    h = bench.host_cpu()
+    assert h["affinity_cores"] >= 1 and h["host_cores"] >= h["affinity_cores"]

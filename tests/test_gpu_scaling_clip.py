@@ -102,3 +102,39 @@ def test_clipped_skip_leaves_window_and_state():
     for a, b in ((p1, p2), (m1, m2), (v1, v2)):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     assert np.array_equal(bits1, bits2)
+
+
+@pytest.mark.parametrize("nd", [3, 24])
+def test_dynamic_scale_limits(nd):
+    """Dynamic scaling at the ends of float64: a growth from 2^1023 would
+    overflow, so the scale stays (the count resets); a backoff from
+    2^-1073 reaches 2^-1074 and then 0, and with 1/L = inf every g is
+    non-finite, so those steps are skipped and the state is never written.
+    The slices are drawn at a fixed scale; only the control block's scale
+    is extreme."""
+    n = 20003
+    g = np.random.default_rng(80 + nd)
+    master0 = (g.standard_normal(n) * 0.02).astype(F32)
+    for start, bad_steps, want_scales, want_flags in (
+            (2.0 ** 1022, (3,), [2.0 ** 1022, 2.0 ** 1023, 2.0 ** 1023, 2.0 ** 1022],
+             [0, 0, 1, 0]),
+            (2.0 ** -1073, (), [2.0 ** -1073, 2.0 ** -1074, 0.0, 0.0], [1, 1, 1, 1])):
+        hp = dict(HP, scale_interval=1, loss_scale=start)
+        sh = oracle.OwnedShard(master0, **hp)
+        run = GpuShardRun(master0, nd, hp)
+        for step in range(1, 5):
+            sl = gen.host_grad_slices(80 + nd, step, 0, nd, n, 0, n, 1e-3, 1024.0)
+            if step in bad_steps:
+                sl[1, 17] = np.inf
+            ovf, sq = sh.step(sl)
+            ctl, p, m, v, bits = run.step(sl, 1.0)
+            tag = f"nd={nd} start={start} step={step}"
+            assert ctl["overflow"] == int(ovf) and ctl["t"] == sh.t, tag
+            assert ctl["loss_scale"] == sh.scale and ctl["good_steps"] == sh.good_steps, tag
+            for got, want, nm in ((p, sh.p, "p"), (m, sh.m, "m"), (v, sh.v, "v")):
+                assert_state_close(got, want, f"{tag} {nm}")
+            assert_fp16_close(run.window(bits), sh.window().view(np.uint16), f"{tag} window")
+            assert run.guards_intact(bits), tag
+        assert sh.scales == want_scales and sh.flags == want_flags
+        if want_flags == [1, 1, 1, 1]:
+            assert np.array_equal(p.view(np.uint32), master0.view(np.uint32)) and not np.any(m)

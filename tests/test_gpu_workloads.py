@@ -1,17 +1,26 @@
 """Parity of the HIP path at the workloads' full sizes, in the launch
-configuration the benchmark times (the library picks the grid from n).
+configuration the benchmark times (the library picks the grid and the
+launch pieces from n).
 
 The seeded inputs are drawn on the device by torch's generator and copied
 to the host for the oracle; nothing the oracle sees comes from the HIP path.
-C1 and C2 are compared element by element over the whole window (and, for
-C1/C2, the whole all-gather buffer); C3-C5 are compared on a sampled set of
-elements whose oracle state is carried by the oracle itself from the
-generated initial parameters (elements are independent), plus properties
-that hold at any size: flags and step counts, sum of g^2 against a float64
-torch reduction of the same slices, bit-identical state and window across
-a skipped step.
+The fused step of every workload (C1-C5) is compared element by element
+over the whole window after every step: C1 and C2 (with, for C1/C2, the
+whole all-gather buffer) against the oracle stepping the whole window at
+once, C3-C5 against the oracle stepping the window in column chunks over a
+thread pool (elements are independent; sum g^2 is the chunks' exact sums
+added with fsum).  The clipped, bucketed and dynamically scaled variants at
+the GPT-2-XL and Nd = 400 sizes compare a sampled set of elements, whose
+oracle state the oracle carries from the generated initial parameters, plus
+what holds at any size: flags and step counts, sum of g^2 against a
+float64 torch reduction of the same slices, bit-identical state and window
+across a skipped step.
 """
+import collections
+import os
 import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -143,6 +152,98 @@ def test_c2_gpt2_small_full():
     assert np.all(bits[w.psi:] == 0)
 
 
+def _bounded_map(ex, depth):
+    """A map over a thread pool that keeps at most ``depth`` items in
+    flight, yielding results in order (so the chunk producer, which copies
+    slices to the host, never runs far ahead of the workers)."""
+    def pmap(fn, items):
+        pending = collections.deque()
+        for it in items:
+            pending.append(ex.submit(fn, it))
+            if len(pending) >= depth:
+                yield pending.popleft().result()
+        while pending:
+            yield pending.popleft().result()
+    return pmap
+
+
+def _host_chunks(slices, n):
+    """Column chunks (lo, hi, host fp16 [Nd, hi - lo]) of the window [0, n)
+    of a device slice buffer, each about 512 MB or 2^22 columns."""
+    nd = slices.shape[0]
+    width = max(1 << 16, min(1 << 22, 1 << (29 - max(1, (2 * nd - 1).bit_length()))))
+    for lo in range(0, n, width):
+        hi = min(n, lo + width)
+        yield lo, hi, slices[:, lo:hi].contiguous().cpu().numpy()
+
+
+def _full_run(w, owner=0, inject=None, clip=0.0, steps=None, interval=0, bucket=0):
+    """Steps the workload's whole window on the device and in the oracle
+    (chunked over the window, its chunks mapped over a thread pool) and
+    compares every element after every step: fp32 master / m / v within
+    1e-5 relative, the fp16 window within 1 ulp, the flag, t and the loss
+    scale exactly, sum g^2 (and the clip coefficient) against the oracle's
+    within 1e-12.  ``bucket`` > 0 ingests the window in buckets of that
+    many elements, read in place."""
+    torch, B, plan, S, valid = _setup(w, owner)
+    from zero_partitioned_mixed_buffer_amd import OwnedShard
+    master = torch.empty(S, dtype=torch.float32, device="cuda")
+    gen.device_fill_params(master, w.seed + owner, w.param_sigma, valid)
+    hp = dict(_hp(w), max_grad_norm=clip)
+    if interval:  # dynamic loss scaling from the workload's scale
+        hp.update(scale_interval=interval, loss_scale=w.loss_scale)
+    ref = oracle.OwnedShard(master.cpu().numpy(), **hp)
+    sh = OwnedShard(master, **hp)
+    del master
+    guard = 8
+    ag = torch.full((guard + S + guard,), 0x7E5A, dtype=torch.int16, device="cuda").view(torch.float16)
+    sh.emit(ag, guard)
+    dsl = torch.empty((w.nd, S), dtype=torch.float16, device="cuda")
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    flags = []
+    with ThreadPoolExecutor(threads) as ex:
+        pmap = _bounded_map(ex, 2 * threads)
+        for step in range(1, (steps or w.steps) + 1):
+            say(f"{w.key} full window step {step}: S={S} Nd={w.nd}, filling {2 * w.nd * S / 1e9:.1f} GB")
+            L = ref.scale if interval else w.loss_scale  # the scale the slices carry
+            gen.device_fill_grads(dsl, w.seed, step, w.grad_sigma, L, w.dist, valid)
+            if inject is not None and inject[0] == step:
+                dsl[inject[1], inject[2]] = float("inf")
+            if bucket:
+                for o in range(0, S, bucket):
+                    k = min(bucket, S - o)
+                    phase = (B.BUCKET_FIRST if o == 0 else 0) | (B.BUCKET_LAST if o + k >= S else 0)
+                    sh.step_bucket(dsl, o, k, phase, w.loss_scale, elem_off=o, allgather=ag,
+                                   allgather_off=guard)
+            else:
+                sh.step(dsl, w.loss_scale, allgather=ag, allgather_off=guard)
+            torch.cuda.synchronize()
+            ctl = sh.control()
+            t0 = time.perf_counter()
+            ovf, sq = ref.step_chunks(_host_chunks(dsl, S), w.loss_scale, pmap=pmap)
+            say(f"{w.key} step {step}: oracle over the window in {time.perf_counter() - t0:.1f} s "
+                f"({threads} threads), flag {int(ovf)}")
+            flags.append(ctl["overflow"])
+            assert ctl["overflow"] == int(ovf) and ctl["t"] == ref.t
+            if interval:
+                assert ctl["loss_scale"] == ref.scale and ctl["good_steps"] == ref.good_steps
+            if not ovf:
+                assert ctl["sumsq"] == pytest.approx(sq, rel=1e-12)
+                if clip:
+                    assert ctl["clip_coef"] == pytest.approx(ref.coefs[-1], rel=1e-12)
+            p, m, v = (x.cpu().numpy() for x in sh.committed(ctl))
+            for got, want, nm in ((p, ref.p, "p"), (m, ref.m, "m"), (v, ref.v, "v")):
+                assert_state_close(got, want, f"{w.key} step {step} {nm}")
+            del p, m, v
+            bits = ag.view(torch.int16).cpu().numpy().view(np.uint16)
+            assert_fp16_close(bits[guard:guard + S], ref.window().view(np.uint16), f"{w.key} step {step} window")
+            assert np.all(bits[:guard] == 0x7E5A) and np.all(bits[guard + S:] == 0x7E5A)
+            del bits
+    del dsl
+    torch.cuda.empty_cache()
+    return flags, ref
+
+
 def _sample_idx(S, n=1 << 16, extra=()):
     g = np.random.default_rng(S % 1000003)
     fixed = np.array([0, 1, 2, 3, S - 4, S - 3, S - 2, S - 1, S // 2 - 1, S // 2, S // 2 + 1, *extra],
@@ -223,27 +324,30 @@ def _sampled_run(w, owner=0, inject=None, clip=0.0, bucket=0, steps=None, interv
     return flags, ref
 
 
-def test_c3_gpt2_xl_adamw_sampled():
+def test_c3_gpt2_xl_adamw_full():
     """GPT-2-XL shaped list (1,557,611,200 params), Nd = 16, AdamW wd = 0.01,
-    rank 0, 5 steps."""
-    flags, ref = _sampled_run(configs.C3)
+    rank 0, 5 steps; every element of the window after every step."""
+    flags, ref = _full_run(configs.C3)
     assert flags == [0] * 5 and ref.t == 5
 
 
-def test_c4_7p5b_sampled():
-    """Psi = 7.5e9 flat, Nd = 64, rank 0, 3 steps; the memory model gives the
-    printed 120 / 31.4 / 16.6 / 1.9 GB and 2Psi / 3Psi."""
+def test_c4_7p5b_full():
+    """Psi = 7.5e9 flat, Nd = 64, rank 0, 3 steps, every element of the
+    window after every step; the memory model gives the printed
+    120 / 31.4 / 16.6 / 1.9 GB and 2Psi / 3Psi."""
     from zero_partitioned_mixed_buffer_amd import binding as B
     mm = [B.memory_model(7.5e9, 64, s) for s in range(4)]
     assert [round(r["total_bytes"] / 1e9, 1) for r in mm] == [120.0, 31.4, 16.6, 1.9]
     assert mm[2]["comm_elems"] == 1.5e10 and mm[3]["comm_elems"] == 2.25e10
-    flags, ref = _sampled_run(configs.C4)
+    flags, ref = _full_run(configs.C4)
     assert flags == [0] * 3 and ref.t == 3
 
 
-def test_c5_60b_nd400_overflow_skip_sampled():
+def test_c5_60b_nd400_overflow_skip_full():
     """Psi = 6e10 flat, Nd = 400 Student-t(3) slices, +inf in slice 17 at
-    step 2 (window element S/2): flags [0, 1, 0, 0], three committed steps."""
+    step 2 (window element S/2): flags [0, 1, 0, 0], three committed steps;
+    every element of the 150,000,128-element window after every step,
+    including the skipped one (state and window unchanged)."""
     w = configs.C5
     torch = torch_mod()
     free, _ = torch.cuda.mem_get_info()
@@ -252,7 +356,7 @@ def test_c5_60b_nd400_overflow_skip_sampled():
     from zero_partitioned_mixed_buffer_amd import binding as B
     S = B.plan_partitions(list(w.numels), w.nd, 256)[0]["part"]
     assert S == 150000128
-    flags, ref = _sampled_run(w, inject=(2, 17, S // 2))
+    flags, ref = _full_run(w, inject=(2, 17, S // 2))
     assert flags == [0, 1, 0, 0] and ref.t == 3
 
 
