@@ -50,14 +50,15 @@
 extern "C" {
 #endif
 
-#define ZERO_DP_ABI_VERSION 4
+#define ZERO_DP_ABI_VERSION 5
 
 /* ---- status codes --------------------------------------------------- */
 #define ZERO_OK          0
 #define ZERO_EINVAL     -1  /* null pointer, nd < 1, n < 0, bad stage/align, bad hyperparameter */
 #define ZERO_EALIGN     -2  /* a vector operand is not 16-byte aligned, or an offset/stride is not a multiple of 8 elements */
 #define ZERO_EOVERFLOW  -3  /* an int64 size or offset computation would overflow */
-#define ZERO_ECAPACITY  -4  /* the caller's fragment array is too small; *n_frags holds the needed count */
+#define ZERO_ECAPACITY  -4  /* the caller's fragment array is too small (*n_frags holds the needed count),
+                              or the library's fixed scratch is too small for the device */
 #define ZERO_EALIAS     -5  /* an output buffer overlaps an input it must not overlap */
 #define ZERO_EHIP       -6  /* a HIP launch or runtime call failed; see zero_last_hip_error() */
 
@@ -275,6 +276,27 @@ int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st,
                    void* workspace, void* stream);
 /* (hp->max_grad_norm must be 0 here; dynamic loss scaling is applied when
  * hp->scale_interval > 0.) */
+
+/* ---- fused step without a workspace argument ---------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The step
+ * of zero_adam_step, with its workspace replaced by a device array the
+ * library holds, zero_workspace_bytes() bytes (98,560) per GPU, kept until
+ * the process ends; the call itself allocates nothing.  The first call on
+ * a device looks up that device's copy (hipGetSymbolAddress).  Every call
+ * on one GPU shares that GPU's copy and leaves the last call's partials in
+ * it: calls that may overlap on one GPU (several streams, or host threads
+ * without ordering) race and must not be made; calls in one stream's
+ * order are fine.  Nothing needs clearing between calls (each step's
+ * first launch writes every slot its commit reads).  The array holds the
+ * partials of up to 8192 workgroups, more than a step launches on any
+ * device (one per CU: 256 on MI355X); a device that would need more gets
+ * ZERO_ECAPACITY.  The window length is not limited by it.  Arguments,
+ * results and the other errors are those of zero_adam_step.
+ */
+int zero_adam_step_noalloc(const zero_grad_src* src, const zero_adam_state* st,
+                           const zero_adam_hp* hp, uint16_t* allgather, int64_t allgather_off,
+                           void* stream);
 
 /* ---- clipped step (two passes) ----------------------------------------
  * Global-norm clipping needs the norm of the whole gradient before any

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(L):
     for name in declared:
         assert hasattr(L, name), name
     assert declared == set(B.EXPORTED)
-    assert L.zero_abi_version() == B.ABI_VERSION == 4
+    assert L.zero_abi_version() == B.ABI_VERSION == 5
 
 
 def test_strerror(L):

@@ -26,9 +26,9 @@ EXPORTED = (
     "zero_strerror", "zero_last_hip_error", "zero_abi_version", "zero_plan_partitions",
     "zero_memory_model", "zero_workspace_bytes", "zero_reduce_owned", "zero_ctl_init",
     "zero_adam_step", "zero_adam_step_clipped", "zero_adam_step_bucket", "zero_restore_skipped",
-    "zero_emit_fp16", "zero_gather_params",
+    "zero_emit_fp16", "zero_gather_params", "zero_adam_step_noalloc",
 )
-ABI_VERSION = 4
+ABI_VERSION = 5
 BUCKET_FIRST = 1
 BUCKET_LAST = 2
 
@@ -102,6 +102,8 @@ def lib():
     L.zero_ctl_init.restype = None
     L.zero_adam_step.argtypes = [C.POINTER(GradSrc), C.POINTER(AdamState), C.POINTER(AdamHp), P,
                                  C.c_int64, P, P]
+    L.zero_adam_step_noalloc.argtypes = [C.POINTER(GradSrc), C.POINTER(AdamState), C.POINTER(AdamHp), P,
+                                         C.c_int64, P]
     L.zero_adam_step_clipped.argtypes = [C.POINTER(GradSrc), C.POINTER(AdamState), C.POINTER(AdamHp), P, P,
                                          C.c_int64, P, P]
     L.zero_adam_step_bucket.argtypes = [C.POINTER(GradSrc), C.POINTER(AdamState), C.POINTER(AdamHp), C.c_int64,
@@ -110,6 +112,7 @@ def lib():
     L.zero_emit_fp16.argtypes = [P, C.c_int64, P, C.c_int64, P]
     L.zero_gather_params.argtypes = [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int64, C.c_int64, P, P]
     for name in ("zero_plan_partitions", "zero_memory_model", "zero_reduce_owned", "zero_adam_step",
+                 "zero_adam_step_noalloc",
                  "zero_adam_step_clipped", "zero_adam_step_bucket", "zero_restore_skipped", "zero_emit_fp16",
                  "zero_gather_params"):
         getattr(L, name).restype = C.c_int
@@ -297,6 +300,14 @@ def adam_step(src: GradSrc, state: AdamState, hp: AdamHp, allgather, allgather_o
     _check_ws(workspace)
     _check(lib().zero_adam_step(C.byref(src), C.byref(state), C.byref(hp), _ptr(allgather),
                                 int(allgather_off), _ptr(workspace), _stream(stream)), "zero_adam_step")
+
+
+def adam_step_noalloc(src: GradSrc, state: AdamState, hp: AdamHp, allgather, allgather_off: int, stream=None):
+    """zero_adam_step on the library's own per-GPU scratch (no workspace)."""
+    _check_state(state, src.n)
+    _check_span(allgather, allgather_off, src.n, _F16, "all-gather buffer")
+    _check(lib().zero_adam_step_noalloc(C.byref(src), C.byref(state), C.byref(hp), _ptr(allgather),
+                                        int(allgather_off), _stream(stream)), "zero_adam_step_noalloc")
 
 
 def adam_step_clipped(src: GradSrc, state: AdamState, hp: AdamHp, grad_buf, allgather, allgather_off: int,

@@ -53,11 +53,20 @@
 
 #include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/zero_dp.h"
 #include "zero_dp_internal.h"
 
 #pragma clang fp contract(off)
+
+// Device scratch of zero_adam_step_noalloc: the layout of a caller's
+// workspace (one partial and one flag per workgroup, for up to
+// zdp::kMaxBlocks workgroups, and the element count of a split window),
+// one copy per GPU for the life of the process.  Host code never uses this
+// name as an address: the device address comes from hipGetSymbolAddress,
+// once per device with that device current (scratch_addr below).
+static __device__ __align__(256) unsigned char scratch[zdp::kWsBytes];
 
 namespace {
 
@@ -1599,11 +1608,55 @@ int launch_fused_range(const SrcArgs& src, const AdamArgs& a, bool first, int gr
     });
 }
 
+// ---------------------------------------------- allocation-free step
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+// The current device's scratch address (looked up on its first use).
+int scratch_addr(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        zdp::set_last_hip_error(e != hipSuccess ? static_cast<int>(e) : static_cast<int>(hipErrorInvalidDevice));
+        return ZERO_EHIP;
+    }
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || p == nullptr) {
+                zdp::set_last_hip_error(e != hipSuccess ? static_cast<int>(e) : static_cast<int>(hipErrorUnknown));
+                return ZERO_EHIP;
+            }
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return ZERO_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int64_t zero_workspace_bytes(void) { return zdp::kWsBytes; }
+
+int zero_adam_step_noalloc(const zero_grad_src* src, const zero_adam_state* st, const zero_adam_hp* hp,
+                           uint16_t* allgather, int64_t allgather_off, void* stream) {
+    // every launch of a step uses one slot per workgroup; the scratch holds
+    // kMaxBlocks of them (a grid never has more: resident_blocks caps it)
+    if (fixed_grid(kFused) > zdp::kMaxBlocks || resident_blocks(kCommit) > zdp::kMaxBlocks)
+        return ZERO_ECAPACITY;
+    void* ws = nullptr;
+    const int rc = scratch_addr(&ws);
+    if (rc != ZERO_OK) return rc;
+    // the step of zero_adam_step on this device's scratch: its first launch
+    // writes every slot and the count the commit reads, so nothing needs
+    // clearing between calls
+    return zero_adam_step(src, st, hp, allgather, allgather_off, ws, stream);
+}
 
 int zero_reduce_owned(const zero_grad_src* src, float* grad_out, int32_t* overflow, double* sumsq,
                       void* workspace, void* stream) {
