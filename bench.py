@@ -138,6 +138,29 @@ def attainable_copy(torch, dev, B, reps=5):
             "note": "4 GiB read + 4 GiB written per copy, mean of 5 back-to-back copies"}
 
 
+def attainable_triad(torch, dev, B, reps=5):
+    """STREAM's triad a = b + q*c through the library's calibration kernel
+    over 2^30 fp32 elements per array (4 GiB each): GB/s of 8 bytes read
+    and 4 written per element."""
+    n = 1 << 30
+    b = torch.ones(n, dtype=torch.float32, device=dev)
+    c = torch.ones(n, dtype=torch.float32, device=dev)
+    a = torch.empty(n, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    B.calib_triad(a, b, c, 3.0, n, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        B.calib_triad(a, b, c, 3.0, n, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"triad_gbs": 12 * n / (ms * 1e-3) / 1e9, "triad_bytes": 12 * n,
+            "triad_kernel": "triad_kernel (3 x 4 GiB fp32, mean of 5 back-to-back launches)"}
+
+
 def calibration_copy(torch, dev):
     """A plain device copy of known size (256 MiB -> 256 MiB) for scaling the
     FETCH_SIZE / WRITE_SIZE counters of a profiled run; not timed."""
@@ -575,6 +598,35 @@ def measure_step(args, w, steps, warmup, graph=False, skip_timing=False):
         log(f"skipped step (inf at slice {k}, element {j}): {skip_us:.1f} us "
             f"({skip_us - kern_avg * 1e3:+.1f} us against a clean step; the re-emit moves 6 B per element)")
 
+    mix = None
+    if not (clipped or bucketed):
+        # The same buffers through the calibration kernel that moves exactly
+        # this step's streams (Nd fp16 slices and 3 fp32 state arrays read,
+        # 3 fp32 arrays and the fp16 window written) in the same launch
+        # shape with no arithmetic: the rate this memory schedule attains
+        # on this GPU.  It writes the non-current state set and the windows,
+        # which the next step overwrites anyway.
+        ctls = [sh.control() for sh in shards]  # cur after the graph and skip runs
+
+        def mix_launch(i):
+            r = i % n_shards
+            sh, cur = shards[r], ctls[r]["cur"]
+            ins = [sh.master[cur], sh.exp_avg[cur], sh.exp_avg_sq[cur]]
+            outs = [sh.master[cur ^ 1], sh.exp_avg[cur ^ 1], sh.exp_avg_sq[cur ^ 1]]
+            B.calib_stream_mix(srcs[i % rot], ins, outs, ag[ag_offs[r]:ag_offs[r] + S], stream)
+
+        for i in range(max(1, min(warmup, 3))):
+            mix_launch(i)
+        torch.cuda.synchronize()
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record(stream)
+        for i in range(steps):
+            mix_launch(i)
+        m1.record(stream)
+        torch.cuda.synchronize()
+        mix_us = m0.elapsed_time(m1) * 1e3 / steps
+        mix = {"us": mix_us, "gbs": (2 * w.nd + 26) * S / (mix_us * 1e-6) / 1e9}
+
     # algorithmic bytes per owned element: fused 2*Nd + 26; clipped
     # (2*Nd + 4) for the reduce pass + 30 for the update pass
     bytes_elem = 2 * w.nd + (34 if clipped else 26)
@@ -584,11 +636,14 @@ def measure_step(args, w, steps, warmup, graph=False, skip_timing=False):
     ms_step = wall * 1e3 / steps
     log(f"{w.key} {what}: avg {kern_avg * 1e3:.1f} us over {steps} back-to-back steps; "
         f"step {ms_step * 1e3:.1f} us; {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.3f} of peak)")
+    if mix is not None:
+        log(f"{w.key} the same streams with no arithmetic (stream-mix kernel): {mix['us']:.1f} us, "
+            f"{mix['gbs']:.0f} GB/s; the step runs at {achieved / mix['gbs']:.3f} of it")
     res = {
         "w": w, "S": S, "owner": owner, "rot": rot, "n_shards": n_shards, "full": full,
         "ms_step": ms_step, "kern_avg_ms": kern_avg, "pcts_us": [pct(0.1), pct(0.5), pct(0.9)],
         "bytes_elem": bytes_elem, "achieved_gbs": achieved, "graph_us": graph_us, "skip": skip,
-        "what": what, "n_buckets": len(buckets) if bucketed else 0,
+        "what": what, "n_buckets": len(buckets) if bucketed else 0, "mix": mix,
     }
     del gsets, srcs, shards, ag
     if bucketed:
@@ -643,11 +698,18 @@ def main():
                            "bytes_per_elem": r["bytes_elem"], "step_us_events": r["kern_avg_ms"] * 1e3,
                            "step_us_host": r["ms_step"] * 1e3, "hbm_gbs": r["achieved_gbs"],
                            "frac_of_peak": r["achieved_gbs"] / PEAK_HBM_GBS,
-                           "elements_per_s": r["S"] / (r["ms_step"] * 1e-3)}
+                           "elements_per_s": r["S"] / (r["ms_step"] * 1e-3),
+                           "mix_gbs": r["mix"]["gbs"] if r["mix"] else None,
+                           "frac_of_mix": r["achieved_gbs"] / r["mix"]["gbs"] if r["mix"] else None}
 
     calibration_copy(torch, dev)
     attain = attainable_copy(torch, dev, B)
-    log(f"attainable copy on this GPU: {attain['copy_gbs']:.0f} GB/s")
+    attain.update(attainable_triad(torch, dev, B))
+    if res["mix"] is not None:
+        attain["mix_gbs"] = res["mix"]["gbs"]
+        attain["mix_kernel"] = "stream_mix_kernel (this workload's streams, the step's launch shape, no arithmetic)"
+    log(f"attainable on this GPU: copy {attain['copy_gbs']:.0f} GB/s, triad {attain['triad_gbs']:.0f} GB/s"
+        + (f", this step's stream mix {attain['mix_gbs']:.0f} GB/s" if "mix_gbs" in attain else ""))
     traffic = None if (clipped or bucketed) else measured_traffic(w.key)
 
     kern_avg = res["kern_avg_ms"]
@@ -713,6 +775,7 @@ def main():
             "kernel_us_p10_p50_p90_per_launch_events": res["pcts_us"],
             "attainable": attain,
             "frac_of_attainable": achieved / attain["copy_gbs"],
+            "frac_of_mix": achieved / attain["mix_gbs"] if "mix_gbs" in attain else None,
             "kernel_fingerprint": kernel_fingerprint(),
         },
         "cpu_baseline": cpu,

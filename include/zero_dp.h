@@ -413,6 +413,27 @@ int zero_gather_params(const uint16_t* const* windows, int32_t nd, int64_t part,
 int zero_emit_fp16(const float* master, int64_t n, uint16_t* allgather,
                    int64_t allgather_off, void* stream);
 
+/* ---- bandwidth calibration (for benchmarks; not part of the step) ------
+ * What HBM attains on the running GPU, beside the step: STREAM's triad
+ * a[i] = b[i] + q*c[i] (fp32; 8 bytes read and 4 written per element), and
+ * a kernel that moves exactly the fused step's streams with no arithmetic
+ * (per element: the Nd fp16 slice reads of src, reads of in[0..2] (fp32),
+ * writes of out[0..2] (fp32) and out16 (fp16); 2*Nd + 26 bytes) in the
+ * fused step's launch shape, visit order and launch pieces.  It writes
+ * out[0] = in[0], out[1] = in[1], out[2] = in[2] with the XOR of the
+ * element's slices folded into its bits, and out16 = the top 16 bits of
+ * in[0] (values with no meaning: only the traffic matters).
+ *   triad: a, b, c device float[n], 16-byte aligned; a overlaps neither b
+ *   nor c.  mix: src as for the step (src->loss_scale is not used but must
+ *   be valid); in, out: host arrays of 3 device pointers to n floats each,
+ *   16-byte aligned; out16 device uint16[n], 16-byte aligned; no output
+ *   overlaps another output or any input.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EALIAS, ZERO_EHIP.
+ */
+int zero_calib_triad(float* a, const float* b, const float* c, float q, int64_t n, void* stream);
+int zero_calib_stream_mix(const zero_grad_src* src, const float* const* in, float* const* out,
+                          uint16_t* out16, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

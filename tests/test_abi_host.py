@@ -296,6 +296,33 @@ def test_other_validation(L):
     assert L.zero_restore_skipped(C.byref(st), 64, (1 << 30) - 64, 0, None) == B.ZERO_EALIAS  # covers the ctl
 
 
+@no_gpu
+def test_calibration_validation(L):
+    assert L.zero_calib_triad(1 << 24, 1 << 25, 1 << 26, 1.0, -1, None) == B.ZERO_EINVAL
+    assert L.zero_calib_triad(None, 1 << 25, 1 << 26, 1.0, 8, None) == B.ZERO_EINVAL
+    assert L.zero_calib_triad(1 << 24, 1 << 25, 1 << 26, 1.0, 0, None) == B.ZERO_OK  # empty
+    assert L.zero_calib_triad((1 << 24) + 4, 1 << 25, 1 << 26, 1.0, 8, None) == B.ZERO_EALIGN
+    assert L.zero_calib_triad(1 << 24, (1 << 24) + 16, 1 << 26, 1.0, 8, None) == B.ZERO_EALIAS
+    assert L.zero_calib_triad(1 << 24, 1 << 25, 1 << 62, 1.0, 2 ** 61, None) == B.ZERO_EOVERFLOW
+    src = B.grad_src(A, 64, 0, 64, 4, 1024.0)
+    ins = (C.c_void_p * 3)(1 << 24, 1 << 25, 1 << 26)
+    outs = (C.c_void_p * 3)(1 << 27, 1 << 28, 1 << 29)
+    mix = L.zero_calib_stream_mix
+    assert mix(C.byref(B.grad_src(A, 64, 0, 64, 0, 1024.0)), ins, outs, 1 << 30, None) == B.ZERO_EINVAL
+    assert mix(C.byref(src), None, outs, 1 << 30, None) == B.ZERO_EINVAL
+    assert mix(C.byref(src), ins, outs, None, None) == B.ZERO_EINVAL
+    assert mix(C.byref(src), ins, (C.c_void_p * 3)(1 << 27, None, 1 << 29), 1 << 30, None) == B.ZERO_EINVAL
+    assert mix(C.byref(src), ins, (C.c_void_p * 3)((1 << 27) + 8, 1 << 28, 1 << 29), 1 << 30, None) == \
+        B.ZERO_EALIGN
+    assert mix(C.byref(src), ins, outs, (1 << 30) + 2, None) == B.ZERO_EALIGN
+    assert mix(C.byref(src), ins, (C.c_void_p * 3)(1 << 24, 1 << 28, 1 << 29), 1 << 30, None) == \
+        B.ZERO_EALIAS  # an output on an input
+    assert mix(C.byref(src), ins, outs, A + 32, None) == B.ZERO_EALIAS  # fp16 output in the slices
+    assert mix(C.byref(src), ins, (C.c_void_p * 3)(1 << 27, (1 << 27) + 128, 1 << 29), 1 << 30, None) == \
+        B.ZERO_EALIAS  # two outputs overlap
+    assert mix(C.byref(B.grad_src(A, 64, 0, 0, 4, 1024.0)), ins, outs, 1 << 30, None) == B.ZERO_OK  # empty
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     """Without the built library every entry point raises: there is no
     fallback path."""

@@ -11,7 +11,10 @@ import ctypes as C
 import os
 from typing import List, Optional, Sequence, Tuple
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzero_dp.so")
+# the in-tree build; ZERO_DP_LIBRARY names another build of the same ABI
+# (the host-only sanitizer build that the host-side tests load)
+_LIB_PATH = os.environ.get("ZERO_DP_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                              "libzero_dp.so")
 _lib = None
 
 ZERO_OK = 0
@@ -26,7 +29,8 @@ EXPORTED = (
     "zero_strerror", "zero_last_hip_error", "zero_abi_version", "zero_plan_partitions",
     "zero_memory_model", "zero_workspace_bytes", "zero_reduce_owned", "zero_ctl_init",
     "zero_adam_step", "zero_adam_step_clipped", "zero_adam_step_bucket", "zero_restore_skipped",
-    "zero_emit_fp16", "zero_gather_params", "zero_adam_step_noalloc",
+    "zero_emit_fp16", "zero_gather_params", "zero_adam_step_noalloc", "zero_calib_triad",
+    "zero_calib_stream_mix",
 )
 ABI_VERSION = 5
 BUCKET_FIRST = 1
@@ -111,8 +115,10 @@ def lib():
     L.zero_restore_skipped.argtypes = [C.POINTER(AdamState), C.c_int64, P, C.c_int64, P]
     L.zero_emit_fp16.argtypes = [P, C.c_int64, P, C.c_int64, P]
     L.zero_gather_params.argtypes = [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int64, C.c_int64, P, P]
+    L.zero_calib_triad.argtypes = [P, P, P, C.c_float, C.c_int64, P]
+    L.zero_calib_stream_mix.argtypes = [C.POINTER(GradSrc), C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), P, P]
     for name in ("zero_plan_partitions", "zero_memory_model", "zero_reduce_owned", "zero_adam_step",
-                 "zero_adam_step_noalloc",
+                 "zero_adam_step_noalloc", "zero_calib_triad", "zero_calib_stream_mix",
                  "zero_adam_step_clipped", "zero_adam_step_bucket", "zero_restore_skipped", "zero_emit_fp16",
                  "zero_gather_params"):
         getattr(L, name).restype = C.c_int
@@ -355,3 +361,24 @@ def gather_params(windows: Sequence, part: int, lo: int, hi: int, dst, stream=No
     arr = (C.c_void_p * max(len(windows), 1))(*[_ptr(w) for w in windows])
     _check(lib().zero_gather_params(arr, len(windows), int(part), int(lo), int(hi), _ptr(dst), _stream(stream)),
            "zero_gather_params")
+
+
+# ------------------------------------------------------------------ calibration
+def calib_triad(a, b, c, q: float, n: int, stream=None):
+    """a[i] = b[i] + q * c[i] over n fp32 elements (STREAM's triad)."""
+    for t, what in ((a, "a"), (b, "b"), (c, "c")):
+        _check_span(t, 0, n, ("float32",), f"triad {what}")
+    _check(lib().zero_calib_triad(_ptr(a), _ptr(b), _ptr(c), float(q), int(n), _stream(stream)),
+           "zero_calib_triad")
+
+
+def calib_stream_mix(src: GradSrc, ins: Sequence, outs: Sequence, out16, stream=None):
+    """The fused step's streams with no arithmetic: src's slices and ins[0..2]
+    read, outs[0..2] and out16 written, src.n elements each."""
+    for t in (*ins, *outs):
+        _check_span(t, 0, src.n, ("float32",), "stream-mix array")
+    _check_span(out16, 0, src.n, _F16, "stream-mix fp16 output")
+    pin = (C.c_void_p * 3)(*[_ptr(t) for t in ins])
+    pout = (C.c_void_p * 3)(*[_ptr(t) for t in outs])
+    _check(lib().zero_calib_stream_mix(C.byref(src), pin, pout, _ptr(out16), _stream(stream)),
+           "zero_calib_stream_mix")

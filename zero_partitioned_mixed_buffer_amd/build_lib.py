@@ -2,10 +2,12 @@
 
     python -m zero_partitioned_mixed_buffer_amd.build_lib [--asm]
 
-The host translation unit (planner, memory model) and the HIP translation
-unit (kernels, asynchronous entry points) are compiled separately and
-linked into one shared library next to this file.  ``--asm`` also writes
-the gfx950 assembly of the kernels to _build/ for inspection.
+The host translation units (planner, memory model, argument validation and
+the C entry points) are compiled with g++, the HIP translation unit
+(kernels and their launchers) with hipcc, and both are linked into one
+shared library next to this file.  ``--asm`` also writes the gfx950
+assembly of the kernels to _build/ for inspection.  (hostcheck_build.py
+builds the host units alone under the sanitizers.)
 """
 from __future__ import annotations
 
@@ -20,6 +22,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzero_dp.so")
+HOST_SOURCES = ("zero_dp_host.cpp", "zero_dp_calls.cpp")
+# the step's kernels and launchers; the benchmark's calibration kernels
+DEVICE_SOURCES = ("zero_dp_kernels.hip", "zero_dp_calib.hip")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -52,18 +57,22 @@ def _run(cmd, verbose):
 def build(verbose: bool = False, asm: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
-    host_o = os.path.join(BUILD, "zero_dp_host.o")
-    dev_o = os.path.join(BUILD, "zero_dp_kernels.o")
-    _run(["g++", *HOST_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, "zero_dp_host.cpp"), "-o", host_o],
-         verbose)
-    _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, "zero_dp_kernels.hip"), "-o", dev_o],
-         verbose)
+    objs = []
+    for src in HOST_SOURCES:
+        o = os.path.join(BUILD, src.replace(".cpp", ".o"))
+        _run(["g++", *HOST_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", o], verbose)
+        objs.append(o)
+    dev_objs = []
+    for src in DEVICE_SOURCES:
+        o = os.path.join(BUILD, src.replace(".hip", ".o"))
+        _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", o], verbose)
+        dev_objs.append(o)
     if asm:
         _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "--cuda-device-only", "-S",
               os.path.join(CSRC, "zero_dp_kernels.hip"), "-o", os.path.join(BUILD, "zero_dp_kernels.s")],
              verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", host_o, dev_o, "-o", tmp,
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, *dev_objs, "-o", tmp,
           "-Wl,-rpath,/opt/rocm/lib"], verbose)
     os.replace(tmp, LIB)
     return LIB

@@ -1,8 +1,16 @@
 // Internal declarations shared by the host and device translation units of
 // the ZeRO-DP owned-partition library.  Not part of the public ABI.
+//
+// The host translation unit zero_dp_calls.cpp validates every argument of
+// the asynchronous C entry points and fills the kernel argument structs
+// below; the device translation units (zero_dp_kernels.hip: the step;
+// zero_dp_calib.hip: bandwidth calibration) hold the kernels and the
+// launchers declared here, which choose grids and enqueue the launches.
 #pragma once
 
 #include <cstdint>
+
+#include "../../include/zero_dp.h"
 
 namespace zdp {
 
@@ -27,5 +35,78 @@ constexpr int64_t kWsBytes = kWsPartFlag + 4 * kMaxBlocks;
 void set_last_hip_error(int e);
 bool mul_overflows(int64_t a, int64_t b, int64_t* out);
 bool add_overflows(int64_t a, int64_t b, int64_t* out);
+
+// ------------------------------------------------------- kernel arguments
+// Workgroup partials in the workspace.
+struct Partials {
+    uint32_t* ticket;
+    double* sq;
+    int32_t* flag;
+};
+
+// The gradient source of one launch.
+struct SrcArgs {
+    const uint16_t* win;       // base + elem_off: slice 0 of the window
+    int64_t stride;
+    int64_t n;
+    int32_t nd;
+    double inv_scale;          // 1/L of a static loss scale
+    const zero_step_ctl* dyn;  // non-null: L = dyn->loss_scale (dynamic loss scaling)
+};
+
+// The Adam state, hyperparameters and outputs of a step.
+struct AdamArgs {
+    float* p[2];
+    float* m[2];
+    float* v[2];
+    zero_step_ctl* ctl;
+    double lr, b1, b2, eps, wd;
+    uint16_t* ag;  // all-gather window start, or null
+    double growth, backoff;  // dynamic loss scaling factors
+    int32_t interval;        // > 0: dynamic loss scaling
+    // bucketed step: this launch covers one bucket of the window; the
+    // per-workgroup partials accumulate in their slots across the step's
+    // launches and the elements covered in run_count
+    int32_t bucket;          // 0: whole-window step; else ZERO_BUCKET_FIRST/LAST bits | 4
+    int64_t window_n;        // elements the step's buckets must cover
+    int64_t* run_count;
+};
+
+// ------------------------------------------------------------- launchers
+// Every argument has been validated by the caller.  Each returns ZERO_OK
+// or ZERO_EHIP (with the HIP error recorded by set_last_hip_error).  A
+// build without a device translation unit links versions that return
+// ZERO_EHIP for every launch.
+
+// The decomposed reduce (zero_reduce_owned).
+int launch_reduce(const SrcArgs& src, float* grad_out, int32_t* overflow, double* sumsq, const Partials& ws,
+                  void* stream);
+// The fused pass(es) over the whole window, then the commit (zero_adam_step).
+int launch_step(const SrcArgs& src, const AdamArgs& a, const Partials& ws, void* stream);
+// The clipped step's two passes and its commit (zero_adam_step_clipped).
+int launch_step_clipped(const SrcArgs& src, const AdamArgs& a, float* grad_buf, double max_norm,
+                        const Partials& ws, void* stream);
+// One bucket (`a` holds the bucket's state and window pointers, `whole`
+// the window's, for the commit after the last bucket).
+int launch_bucket(const SrcArgs& src, const AdamArgs& a, const AdamArgs& whole, int32_t phase,
+                  const Partials& ws, void* stream);
+// Flat elements [lo, hi) of the windows into dst (zero_gather_params).
+int launch_gather(const uint16_t* const* windows, int64_t part, int64_t lo, int64_t hi, uint16_t* dst,
+                  void* stream);
+// The window re-emit of a skipped step, decided on the device.
+int launch_restore(const float* p0, const float* p1, const zero_step_ctl* ctl, uint16_t* ag, int64_t n,
+                   void* stream);
+// allgather window = fp16(master).
+int launch_emit(const float* master, uint16_t* ag, int64_t n, void* stream);
+// The current device's address of the library-held scratch that
+// zero_adam_step_noalloc uses as its workspace (kWsBytes bytes), or
+// ZERO_ECAPACITY if a step on this device would need more workgroup slots.
+int scratch_workspace(void** ws);
+
+// Bandwidth calibration (zero_dp_calib.hip): STREAM's triad, and the fused
+// step's streams with no arithmetic in its launch shape.
+int launch_calib_triad(float* a, const float* b, const float* c, float q, int64_t n, void* stream);
+int launch_calib_mix(const SrcArgs& src, const float* const* in, float* const* out, uint16_t* out16,
+                     void* stream);
 
 }  // namespace zdp

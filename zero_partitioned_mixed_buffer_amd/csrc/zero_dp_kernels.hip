@@ -70,8 +70,11 @@ static __device__ __align__(256) unsigned char scratch[zdp::kWsBytes];
 
 namespace {
 
+using zdp::AdamArgs;
 using zdp::kBlock;
 using zdp::kWaves;
+using zdp::Partials;
+using zdp::SrcArgs;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -223,11 +226,6 @@ struct GroupIter {
     }
 };
 
-struct Partials {
-    uint32_t* ticket;
-    double* sq;
-    int32_t* flag;
-};
 
 // Publishes this workgroup's partial and returns true in every thread of
 // the workgroup that finishes last; that workgroup then holds the totals
@@ -310,14 +308,6 @@ __device__ __forceinline__ void sum_partials(const Partials& ws, int nparts, dou
 }
 
 // ---------------------------------------------------------------- kernels
-struct SrcArgs {
-    const uint16_t* win;       // base + elem_off: slice 0 of the window
-    int64_t stride;
-    int64_t n;
-    int32_t nd;
-    double inv_scale;          // 1/L of a static loss scale
-    const zero_step_ctl* dyn;  // non-null: L = dyn->loss_scale (dynamic loss scaling)
-};
 
 // The kernel's view of the source with 1/L resolved (the same IEEE division
 // as the host's 1.0 / L in every workgroup).
@@ -660,22 +650,6 @@ struct AdamScalars {
     double b1, b2, omb1, omb2, ss, isb, dcy, eps;
 };
 
-struct AdamArgs {
-    float* p[2];
-    float* m[2];
-    float* v[2];
-    zero_step_ctl* ctl;
-    double lr, b1, b2, eps, wd;
-    uint16_t* ag;  // all-gather window start, or null
-    double growth, backoff;  // dynamic loss scaling factors
-    int32_t interval;        // > 0: dynamic loss scaling
-    // bucketed step: this launch covers one bucket of the window; the
-    // per-workgroup partials accumulate in their slots across the step's
-    // launches and the elements covered in run_count
-    int32_t bucket;          // 0: whole-window step; else ZERO_BUCKET_FIRST/LAST bits | 4
-    int64_t window_n;        // elements the step's buckets must cover
-    int64_t* run_count;
-};
 
 // Scalars of the step being taken, t = committed + 1 (identical in every
 // lane and workgroup: the same IEEE operations on the same inputs).
@@ -1325,7 +1299,7 @@ __global__ void __launch_bounds__(kBlock) copy_f16_kernel(CopyPieces t, uint16_t
     for (int i = 0; i < t.np; ++i) copy_piece(t.src[i], dst + t.off[i], t.len[i]);
 }
 
-// ---------------------------------------------------------------- host glue
+// ---------------------------------------------------------------- launchers
 constexpr int kMaxDevices = 64;
 enum KernelId { kReduce = 0, kFused = 1, kEmit = 2, kRestore = 3, kClip = 4, kCopy = 5, kCommit = 6, kKernels = 7 };
 std::atomic<int> g_grid_cache[kKernels][kMaxDevices];  // 0 = not computed yet
@@ -1388,139 +1362,12 @@ int copy_grid(int64_t n) {
     return static_cast<int>(g < 1 ? 1 : g);
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-struct Range {
-    uintptr_t lo, hi;  // [lo, hi)
-};
-bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
-
 int finish_launch() {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         zdp::set_last_hip_error(static_cast<int>(e));
         return ZERO_EHIP;
     }
-    return ZERO_OK;
-}
-
-// Validates a gradient source and returns the byte span its slices cover.
-int check_src(const zero_grad_src* src, Range* span) {
-    if (src == nullptr || src->nd < 1 || src->nd >= 8192 || src->n < 0 || src->elem_off < 0 ||
-        src->reserved != 0)
-        return ZERO_EINVAL;
-    if (src->base == nullptr && src->n != 0) return ZERO_EINVAL;
-    if (!(src->loss_scale > 0.0) || !__builtin_isfinite(src->loss_scale) ||
-        !__builtin_isfinite(1.0 / src->loss_scale))
-        return ZERO_EINVAL;
-    if (src->nd > 1 && src->slice_stride < 0) return ZERO_EINVAL;
-    if (!aligned16(src->base) || src->elem_off % 8 != 0) return ZERO_EALIGN;
-    if (src->nd > 1 && src->slice_stride % 8 != 0) return ZERO_EALIGN;
-    int64_t last = 0, end = 0, bytes = 0;
-    const int64_t stride = src->nd > 1 ? src->slice_stride : 0;
-    if (zdp::mul_overflows(static_cast<int64_t>(src->nd - 1), stride, &last) ||
-        zdp::add_overflows(last, src->elem_off, &last) || zdp::add_overflows(last, src->n, &end) ||
-        zdp::mul_overflows(end, 2, &bytes))
-        return ZERO_EOVERFLOW;
-    span->lo = reinterpret_cast<uintptr_t>(src->base + src->elem_off);
-    span->hi = reinterpret_cast<uintptr_t>(src->base) + static_cast<uintptr_t>(bytes);
-    return ZERO_OK;
-}
-
-SrcArgs make_src(const zero_grad_src* src, const zero_step_ctl* dyn = nullptr) {
-    SrcArgs s;
-    s.win = src->base + src->elem_off;
-    s.stride = src->nd > 1 ? src->slice_stride : 0;
-    s.n = src->n;
-    s.nd = src->nd;
-    s.inv_scale = 1.0 / src->loss_scale;
-    s.dyn = dyn;
-    return s;
-}
-
-Partials make_ws(void* workspace) {
-    char* w = static_cast<char*>(workspace);
-    Partials p;
-    p.ticket = reinterpret_cast<uint32_t*>(w + zdp::kWsTicket);
-    p.sq = reinterpret_cast<double*>(w + zdp::kWsPartSq);
-    p.flag = reinterpret_cast<int32_t*>(w + zdp::kWsPartFlag);
-    return p;
-}
-
-Range bytes_of(const void* p, int64_t n, int64_t elem) {
-    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-    return Range{lo, lo + static_cast<uintptr_t>(n) * static_cast<uintptr_t>(elem)};
-}
-
-// Validates the arguments of a step (fused or clipped) and fills the kernel
-// arguments.  `grad_buf` (the clipped path's fp32 gradient) may be null.
-int check_step(const zero_grad_src* src, const zero_adam_state* st, const zero_adam_hp* hp,
-               uint16_t* allgather, int64_t allgather_off, void* workspace, float* grad_buf,
-               AdamArgs* a, uint16_t** ag_out) {
-    Range span{};
-    int rc = check_src(src, &span);
-    if (rc != ZERO_OK) return rc;
-    if (st == nullptr || hp == nullptr || st->ctl == nullptr || workspace == nullptr) return ZERO_EINVAL;
-    if (!(hp->lr >= 0.0) || !__builtin_isfinite(hp->lr) || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
-        !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps > 0.0) || !__builtin_isfinite(hp->eps) ||
-        !(hp->weight_decay >= 0.0) || !__builtin_isfinite(hp->weight_decay) ||
-        !(hp->max_grad_norm >= 0.0) || !__builtin_isfinite(hp->max_grad_norm) || hp->reserved != 0 ||
-        hp->scale_interval < 0)
-        return ZERO_EINVAL;
-    if (hp->scale_interval > 0 &&
-        (!(hp->scale_growth > 0.0) || !__builtin_isfinite(hp->scale_growth) || !(hp->scale_backoff > 0.0) ||
-         !__builtin_isfinite(hp->scale_backoff)))
-        return ZERO_EINVAL;
-    const int64_t n = src->n;
-    int64_t b4 = 0;
-    if (zdp::mul_overflows(n, 4, &b4)) return ZERO_EOVERFLOW;
-    float* arrs[7] = {st->master[0],     st->master[1],     st->exp_avg[0], st->exp_avg[1],
-                      st->exp_avg_sq[0], st->exp_avg_sq[1], grad_buf};
-    Range r[11];
-    int nr = 0;
-    for (int i = 0; i < 7; ++i) {
-        if (i == 6 && grad_buf == nullptr) continue;
-        if (arrs[i] == nullptr && n != 0) return ZERO_EINVAL;
-        if (!aligned16(arrs[i])) return ZERO_EALIGN;
-        r[nr++] = bytes_of(arrs[i], n, 4);
-    }
-    if (!aligned16(workspace)) return ZERO_EALIGN;
-    uint16_t* ag = nullptr;
-    if (allgather != nullptr) {
-        if (allgather_off < 0) return ZERO_EINVAL;
-        int64_t e = 0;
-        if (zdp::add_overflows(allgather_off, n, &e) || zdp::mul_overflows(e, 2, &e)) return ZERO_EOVERFLOW;
-        ag = allgather + allgather_off;
-        if (!aligned16(ag)) return ZERO_EALIGN;
-        r[nr++] = bytes_of(ag, n, 2);
-    }
-    r[nr++] = span;
-    // the control block and the workspace must not overlap any data either
-    if ((reinterpret_cast<uintptr_t>(st->ctl) & 7u) != 0) return ZERO_EALIGN;
-    r[nr++] = bytes_of(st->ctl, 1, static_cast<int64_t>(sizeof(zero_step_ctl)));
-    r[nr++] = bytes_of(workspace, 1, zdp::kWsBytes);
-    for (int i = 0; i < nr; ++i)
-        for (int k = i + 1; k < nr; ++k)
-            if (overlap(r[i], r[k])) return ZERO_EALIAS;
-    for (int i = 0; i < 2; ++i) {
-        a->p[i] = st->master[i];
-        a->m[i] = st->exp_avg[i];
-        a->v[i] = st->exp_avg_sq[i];
-    }
-    a->ctl = st->ctl;
-    a->lr = hp->lr;
-    a->b1 = hp->beta1;
-    a->b2 = hp->beta2;
-    a->eps = hp->eps;
-    a->wd = hp->weight_decay;
-    a->ag = ag;
-    a->growth = hp->scale_growth;
-    a->backoff = hp->scale_backoff;
-    a->interval = hp->scale_interval;
-    a->bucket = 0;
-    a->window_n = n;
-    a->run_count = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + zdp::kWsRunCount);
-    *ag_out = ag;
     return ZERO_OK;
 }
 
@@ -1639,73 +1486,27 @@ int scratch_addr(void** out) {
 
 }  // namespace
 
-extern "C" {
+namespace zdp {
 
-int64_t zero_workspace_bytes(void) { return zdp::kWsBytes; }
-
-int zero_adam_step_noalloc(const zero_grad_src* src, const zero_adam_state* st, const zero_adam_hp* hp,
-                           uint16_t* allgather, int64_t allgather_off, void* stream) {
-    // every launch of a step uses one slot per workgroup; the scratch holds
-    // kMaxBlocks of them (a grid never has more: resident_blocks caps it)
-    if (fixed_grid(kFused) > zdp::kMaxBlocks || resident_blocks(kCommit) > zdp::kMaxBlocks)
-        return ZERO_ECAPACITY;
-    void* ws = nullptr;
-    const int rc = scratch_addr(&ws);
-    if (rc != ZERO_OK) return rc;
-    // the step of zero_adam_step on this device's scratch: its first launch
-    // writes every slot and the count the commit reads, so nothing needs
-    // clearing between calls
-    return zero_adam_step(src, st, hp, allgather, allgather_off, ws, stream);
-}
-
-int zero_reduce_owned(const zero_grad_src* src, float* grad_out, int32_t* overflow, double* sumsq,
-                      void* workspace, void* stream) {
-    Range span{};
-    int rc = check_src(src, &span);
-    if (rc != ZERO_OK) return rc;
-    if (overflow == nullptr || sumsq == nullptr || workspace == nullptr) return ZERO_EINVAL;
-    if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(overflow) & 3u) != 0 ||
-        (reinterpret_cast<uintptr_t>(sumsq) & 7u) != 0)
-        return ZERO_EALIGN;
-    Range r[5];
-    int nr = 0;
-    r[nr++] = span;
-    r[nr++] = bytes_of(overflow, 1, 4);
-    r[nr++] = bytes_of(sumsq, 1, 8);
-    r[nr++] = bytes_of(workspace, 1, zdp::kWsBytes);
-    if (grad_out != nullptr) {
-        if (!aligned16(grad_out)) return ZERO_EALIGN;
-        int64_t b = 0;
-        if (zdp::mul_overflows(src->n, 4, &b)) return ZERO_EOVERFLOW;
-        r[nr++] = bytes_of(grad_out, src->n, 4);
-    }
-    for (int i = 0; i < nr; ++i)
-        for (int k = i + 1; k < nr; ++k)
-            if (overlap(r[i], r[k])) return ZERO_EALIAS;
-    const int grid = grid_for(kReduce, src->n);
+int launch_reduce(const SrcArgs& src, float* grad_out, int32_t* overflow, double* sumsq, const Partials& ws,
+                  void* stream) {
+    const int grid = grid_for(kReduce, src.n);
     (void)hipGetLastError();
-    reduce_owned_kernel<false><<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
-        make_src(src), grad_out, overflow, sumsq, make_ws(workspace), 0);
+    reduce_owned_kernel<false><<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(src, grad_out, overflow,
+                                                                                      sumsq, ws, 0);
     return finish_launch();
 }
 
-int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st, const zero_adam_hp* hp,
-                   uint16_t* allgather, int64_t allgather_off, void* workspace, void* stream) {
-    AdamArgs a;
-    uint16_t* ag = nullptr;
-    const int rc = check_step(src, st, hp, allgather, allgather_off, workspace, nullptr, &a, &ag);
-    if (rc != ZERO_OK) return rc;
-    if (hp->max_grad_norm != 0.0) return ZERO_EINVAL;  // clipping needs the two-pass entry point
-    const int64_t n = src->n;
-    const Partials ws = make_ws(workspace);
+int launch_step(const SrcArgs& whole, const AdamArgs& a_in, const Partials& ws, void* stream) {
+    AdamArgs a = a_in;
+    const int64_t n = whole.n;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const SrcArgs whole = make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr);
     (void)hipGetLastError();
-    if (!split_window(n, src->nd)) {
+    if (!split_window(n, whole.nd)) {
         const int grid = grid_for(kFused, n);
         fused_step_kernel<<<grid, kBlock, 0, s>>>(whole, a, ws);
-        const int rc2 = finish_launch();
-        if (rc2 != ZERO_OK) return rc2;
+        const int rc = finish_launch();
+        if (rc != ZERO_OK) return rc;
         commit_kernel<<<grid_for(kCommit, n), kBlock, 0, s>>>(a, ws, grid, n, 0.0);
         return finish_launch();
     }
@@ -1713,129 +1514,54 @@ int zero_adam_step(const zero_grad_src* src, const zero_adam_state* st, const ze
     // as the buckets of one step, then the commit
     a.window_n = n;
     const int grid = fixed_grid(kFused);
-    const int rc2 = launch_fused_range(whole, a, true, grid, ws, s);
-    if (rc2 != ZERO_OK) return rc2;
+    const int rc = launch_fused_range(whole, a, true, grid, ws, s);
+    if (rc != ZERO_OK) return rc;
     a.bucket = ZERO_BUCKET_LAST | 4;
     commit_kernel<<<grid_for(kCommit, n), kBlock, 0, s>>>(a, ws, grid, n, 0.0);
     return finish_launch();
 }
 
-int zero_adam_step_clipped(const zero_grad_src* src, const zero_adam_state* st, const zero_adam_hp* hp,
-                           float* grad_buf, uint16_t* allgather, int64_t allgather_off, void* workspace,
-                           void* stream) {
-    AdamArgs a;
-    uint16_t* ag = nullptr;
-    if (grad_buf == nullptr && src != nullptr && src->n != 0) return ZERO_EINVAL;
-    const int rc = check_step(src, st, hp, allgather, allgather_off, workspace, grad_buf, &a, &ag);
-    if (rc != ZERO_OK) return rc;
-    if (!(hp->max_grad_norm > 0.0) || !__builtin_isfinite(hp->max_grad_norm)) return ZERO_EINVAL;
-    const int64_t n = src->n;
-    const Partials ws = make_ws(workspace);
+int launch_step_clipped(const SrcArgs& whole, const AdamArgs& a, float* grad_buf, double max_norm,
+                        const Partials& ws, void* stream) {
+    const int64_t n = whole.n;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const SrcArgs whole = make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr);
     // a long window takes each pass in pieces; the first pass's pieces run
     // on one grid and accumulate in the workgroup slots
-    const int grid1 = split_window(n, src->nd) ? fixed_grid(kReduce) : grid_for(kReduce, n);
+    const int grid1 = split_window(n, whole.nd) ? fixed_grid(kReduce) : grid_for(kReduce, n);
     (void)hipGetLastError();
-    int rc2 = for_each_piece(n, src->nd, [&](int64_t off, int64_t k) {
+    int rc = for_each_piece(n, whole.nd, [&](int64_t off, int64_t k) {
         reduce_owned_kernel<true><<<grid1, kBlock, 0, s>>>(piece_src(whole, off, k), grad_buf + off, nullptr,
                                                             nullptr, ws, off != 0);
         return finish_launch();
     });
-    if (rc2 != ZERO_OK) return rc2;
+    if (rc != ZERO_OK) return rc;
     // the update pass streams g and the state alone: pieces as for small Nd
-    rc2 = for_each_piece(n, 1, [&](int64_t off, int64_t k) {
+    rc = for_each_piece(n, 1, [&](int64_t off, int64_t k) {
         clipped_update_kernel<<<grid_for(kClip, k), kBlock, 0, s>>>(grad_buf + off, k, piece_args(a, off),
-                                                                   hp->max_grad_norm, ws, grid1);
+                                                                   max_norm, ws, grid1);
         return finish_launch();
     });
-    if (rc2 != ZERO_OK) return rc2;
-    commit_kernel<<<1, kBlock, 0, s>>>(a, ws, grid1, n, hp->max_grad_norm);
+    if (rc != ZERO_OK) return rc;
+    commit_kernel<<<1, kBlock, 0, s>>>(a, ws, grid1, n, max_norm);
     return finish_launch();
 }
 
-int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st, const zero_adam_hp* hp,
-                          int64_t win_off, int64_t window_n, uint16_t* allgather, int64_t allgather_off,
-                          int32_t phase, void* workspace, void* stream) {
-    if (src == nullptr || st == nullptr || hp == nullptr) return ZERO_EINVAL;
-    if ((phase & ~(ZERO_BUCKET_FIRST | ZERO_BUCKET_LAST)) != 0 || win_off < 0 || window_n < 0 || src->n < 0)
-        return ZERO_EINVAL;
-    int64_t end = 0, b = 0;
-    if (zdp::add_overflows(win_off, src->n, &end) || zdp::mul_overflows(window_n, 4, &b)) return ZERO_EOVERFLOW;
-    if (end > window_n) return ZERO_EINVAL;
-    if (win_off % 8 != 0) return ZERO_EALIGN;
-    // the bucket's view of the state and of the all-gather window
-    zero_adam_state sub = *st;
-    for (int i = 0; i < 2; ++i) {
-        if (st->master[i] == nullptr || st->exp_avg[i] == nullptr || st->exp_avg_sq[i] == nullptr) {
-            if (window_n != 0) return ZERO_EINVAL;
-            continue;
-        }
-        sub.master[i] = st->master[i] + win_off;
-        sub.exp_avg[i] = st->exp_avg[i] + win_off;
-        sub.exp_avg_sq[i] = st->exp_avg_sq[i] + win_off;
-    }
-    int64_t ag_off = 0;
-    if (allgather != nullptr && (allgather_off < 0 || zdp::add_overflows(allgather_off, win_off, &ag_off)))
-        return allgather_off < 0 ? ZERO_EINVAL : ZERO_EOVERFLOW;
-    AdamArgs a;
-    uint16_t* ag = nullptr;
-    const int rc = check_step(src, &sub, hp, allgather, ag_off, workspace, nullptr, &a, &ag);
-    if (rc != ZERO_OK) return rc;
-    if (hp->max_grad_norm != 0.0) return ZERO_EINVAL;  // clipping needs the norm before any bucket
-    // the whole window's all-gather range, for the re-emit of a skipped step
-    uint16_t* ag_window = nullptr;
-    if (allgather != nullptr) {
-        int64_t e = 0;
-        if (zdp::add_overflows(allgather_off, window_n, &e) || zdp::mul_overflows(e, 2, &e)) return ZERO_EOVERFLOW;
-        ag_window = allgather + allgather_off;
-        if (!aligned16(ag_window)) return ZERO_EALIGN;
-    }
-    a.bucket = phase | 4;  // the commit below checks the buckets' coverage
-    a.window_n = window_n;
+int launch_bucket(const SrcArgs& src, const AdamArgs& a, const AdamArgs& whole, int32_t phase,
+                  const Partials& ws, void* stream) {
     // every bucket of a step runs on the same grid: each workgroup adds its
     // partial to its own slot
     const int grid = fixed_grid(kFused);
-    const Partials ws = make_ws(workspace);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    const int rc2 = launch_fused_range(make_src(src, hp->scale_interval > 0 ? st->ctl : nullptr), a,
-                                       (phase & ZERO_BUCKET_FIRST) != 0, grid, ws, s);
-    if (rc2 != ZERO_OK || (phase & ZERO_BUCKET_LAST) == 0) return rc2;
+    const int rc = launch_fused_range(src, a, (phase & ZERO_BUCKET_FIRST) != 0, grid, ws, s);
+    if (rc != ZERO_OK || (phase & ZERO_BUCKET_LAST) == 0) return rc;
     // the commit, over the whole window
-    AdamArgs c = a;
-    for (int i = 0; i < 2; ++i) {
-        c.p[i] = st->master[i];
-        c.m[i] = st->exp_avg[i];
-        c.v[i] = st->exp_avg_sq[i];
-    }
-    c.ag = ag_window;
-    commit_kernel<<<grid_for(kCommit, window_n), kBlock, 0, s>>>(c, ws, grid, window_n, 0.0);
+    commit_kernel<<<grid_for(kCommit, whole.window_n), kBlock, 0, s>>>(whole, ws, grid, whole.window_n, 0.0);
     return finish_launch();
 }
 
-int zero_gather_params(const uint16_t* const* windows, int32_t nd, int64_t part, int64_t lo, int64_t hi,
-                       uint16_t* dst, void* stream) {
-    if (windows == nullptr || nd < 1 || part < 1 || lo < 0 || hi < lo) return ZERO_EINVAL;
-    int64_t total = 0, bytes = 0;
-    if (zdp::mul_overflows(static_cast<int64_t>(nd), part, &total)) return ZERO_EOVERFLOW;
-    if (hi > total) return ZERO_EINVAL;
-    const int64_t n = hi - lo;
-    if (n == 0) return ZERO_OK;  // nothing to gather
-    if (dst == nullptr) return ZERO_EINVAL;
-    if (zdp::mul_overflows(n, 2, &bytes)) return ZERO_EOVERFLOW;
-    if ((reinterpret_cast<uintptr_t>(dst) & 1u) != 0) return ZERO_EALIGN;
-    const Range out = bytes_of(dst, n, 2);
-    // every piece is validated before anything is launched
-    for (int64_t f = lo; f < hi;) {
-        const int64_t r = f / part;
-        const int64_t take = ((r + 1) * part < hi ? (r + 1) * part : hi) - f;
-        const uint16_t* w = windows[r];
-        if (w == nullptr) return ZERO_EINVAL;
-        if ((reinterpret_cast<uintptr_t>(w) & 1u) != 0) return ZERO_EALIGN;
-        if (overlap(bytes_of(w + (f - r * part), take, 2), out)) return ZERO_EALIAS;
-        f += take;
-    }
+int launch_gather(const uint16_t* const* windows, int64_t part, int64_t lo, int64_t hi, uint16_t* dst,
+                  void* stream) {
     // the pieces, kMaxPieces per launch (one launch for any layer that
     // touches at most kMaxPieces windows)
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1859,47 +1585,26 @@ int zero_gather_params(const uint16_t* const* windows, int32_t nd, int64_t part,
     return ZERO_OK;
 }
 
-int zero_restore_skipped(const zero_adam_state* st, int64_t n, uint16_t* allgather,
-                         int64_t allgather_off, void* stream) {
-    if (st == nullptr || st->ctl == nullptr || n < 0 || allgather_off < 0) return ZERO_EINVAL;
-    if (n != 0 && (allgather == nullptr || st->master[0] == nullptr || st->master[1] == nullptr))
-        return ZERO_EINVAL;
-    int64_t e = 0;
-    if (zdp::mul_overflows(n, 4, &e) || zdp::add_overflows(allgather_off, n, &e) ||
-        zdp::mul_overflows(e, 2, &e))
-        return ZERO_EOVERFLOW;
-    if (n == 0) return ZERO_OK;  // nothing to restore
-    uint16_t* ag = allgather + allgather_off;
-    if (!aligned16(ag) || !aligned16(st->master[0]) || !aligned16(st->master[1]) ||
-        (reinterpret_cast<uintptr_t>(st->ctl) & 7u) != 0)
-        return ZERO_EALIGN;
-    const Range w = bytes_of(ag, n, 2);
-    if (overlap(w, bytes_of(st->master[0], n, 4)) || overlap(w, bytes_of(st->master[1], n, 4)) ||
-        overlap(w, bytes_of(st->ctl, 1, static_cast<int64_t>(sizeof(zero_step_ctl)))))
-        return ZERO_EALIAS;
+int launch_restore(const float* p0, const float* p1, const zero_step_ctl* ctl, uint16_t* ag, int64_t n,
+                   void* stream) {
     const int grid = grid_for(kRestore, n);
     (void)hipGetLastError();
-    restore_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(
-        st->master[0], st->master[1], st->ctl, ag, n);
+    restore_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(p0, p1, ctl, ag, n);
     return finish_launch();
 }
 
-int zero_emit_fp16(const float* master, int64_t n, uint16_t* allgather, int64_t allgather_off,
-                   void* stream) {
-    if (n < 0 || allgather_off < 0) return ZERO_EINVAL;
-    if (n == 0) return ZERO_OK;  // nothing to write
-    if (master == nullptr || allgather == nullptr) return ZERO_EINVAL;
-    int64_t e = 0;
-    if (zdp::mul_overflows(n, 4, &e) || zdp::add_overflows(allgather_off, n, &e) ||
-        zdp::mul_overflows(e, 2, &e))
-        return ZERO_EOVERFLOW;
-    uint16_t* ag = allgather + allgather_off;
-    if (!aligned16(ag) || !aligned16(master)) return ZERO_EALIGN;
-    if (overlap(bytes_of(master, n, 4), bytes_of(ag, n, 2))) return ZERO_EALIAS;
+int launch_emit(const float* master, uint16_t* ag, int64_t n, void* stream) {
     const int grid = grid_for(kEmit, n);
     (void)hipGetLastError();
     emit_kernel<<<grid, kBlock, 0, static_cast<hipStream_t>(stream)>>>(master, ag, n);
     return finish_launch();
 }
 
-}  // extern "C"
+int scratch_workspace(void** ws) {
+    // every launch of a step uses one slot per workgroup; the scratch holds
+    // kMaxBlocks of them (a grid never has more: resident_blocks caps it)
+    if (fixed_grid(kFused) > kMaxBlocks || resident_blocks(kCommit) > kMaxBlocks) return ZERO_ECAPACITY;
+    return scratch_addr(ws);
+}
+
+}  // namespace zdp
