@@ -253,7 +253,8 @@ typedef struct zero_adam_hp {
  * the all-gather window from the committed master.  A long window takes its
  * fused pass in consecutive launches (measured faster than one long
  * launch): of about 2^24 elements when it is longer than 2^25 and Nd < 32,
- * of about 2^23 when it is longer than 2^24 and Nd >= 32.  Their partials
+ * of about 2^23 when it is longer than 2^24 and 32 <= Nd < 256, of about
+ * 2^22 when it is longer than 2^23 and Nd >= 256.  Their partials
  * accumulate in the workspace; the results are the same element for
  * element, and the sum of g^2 differs only in its rounding order.  A rank steps its own
  * partition alone and the new parameters then reach every rank by

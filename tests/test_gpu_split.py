@@ -1,6 +1,6 @@
 """GPU parity of a long window, whose fused pass the library runs as several
-consecutive launches (windows of more than 2^25 elements, or of more than
-2^24 from 32 slices up).
+consecutive launches (windows of more than 2^25 elements, of more than 2^24
+from 32 slices up, of more than 2^23 from 256 slices up).
 
 The same window is stepped twice on the device: by zero_adam_step (split
 into launches) and in buckets of 2^20 elements (one launch each; the
@@ -30,6 +30,9 @@ ND = 3
 # longer than 2^24: this window takes three launches there and one below.
 N_BIG_ND = (1 << 24) + 5003
 BIG_ND = 48
+# From 256 slices up it splits at 2^22 once a window is longer than 2^23.
+N_HUGE_ND = (1 << 23) + 5003
+HUGE_ND = 260
 SPLITS = [(ND, N), (BIG_ND, N_BIG_ND)]
 L = 1024.0
 
@@ -52,7 +55,8 @@ def _sumsq(torch, slices, scale=L):
     return float((g * g).sum().item())
 
 
-@pytest.mark.parametrize("nd,n,dynamic", [(ND, N, False), (ND, N, True), (BIG_ND, N_BIG_ND, False)])
+@pytest.mark.parametrize("nd,n,dynamic", [(ND, N, False), (ND, N, True), (BIG_ND, N_BIG_ND, False),
+                                          (HUGE_ND, N_HUGE_ND, False)])
 def test_long_window_split_launches(nd, n, dynamic):
     """With dynamic loss scaling (interval 2, from 4096) the slices carry
     the control block's scale, and the scale trajectory must match the

@@ -302,11 +302,11 @@ int launch_calib_triad(float* a, const float* b, const float* c, float q, int64_
 }
 
 int launch_calib_mix(const SrcArgs& src, const float* const* in, float* const* out, uint16_t* out16, void* stream) {
-    // the fused step's launch pieces: about 2^23 elements from Nd = 32 up
-    // when the window is longer than 2^24, about 2^24 below when it is
-    // longer than 2^25 (multiples of 1024), else one launch
+    // the fused step's launch pieces: about 2^22 elements from Nd = 256 up,
+    // 2^23 from Nd = 32 and 2^24 below, when the window is longer than two
+    // of them (multiples of 1024), else one launch
     const int64_t n = src.n;
-    const int64_t e = src.nd >= 32 ? (int64_t{1} << 23) : (int64_t{1} << 24);
+    const int64_t e = src.nd >= 256 ? (int64_t{1} << 22) : src.nd >= 32 ? (int64_t{1} << 23) : (int64_t{1} << 24);
     int64_t len = n;
     if (n > 2 * e) {
         const int64_t pieces = (n + e - 1) / e;

@@ -1384,16 +1384,25 @@ int fixed_grid(KernelId id) {
 #ifndef ZDP_SPLIT_BIG_LOG2
 #define ZDP_SPLIT_BIG_LOG2 23  // the same for Nd >= ZDP_CH_BIG_ND (the 8-group visits)
 #endif
+#ifndef ZDP_SPLIT_HUGE_ND
+#define ZDP_SPLIT_HUGE_ND 256  // from this Nd on, launches of about 2^(ZDP_SPLIT_BIG_LOG2 - 1)
+#endif
 
 // A window longer than two launch lengths is stepped in launches of about
-// 2^24 elements (2^23 for the big visit shape, Nd >= ZDP_CH_BIG_ND).  One grid-stride launch over 10^8
+// 2^24 elements (2^23 for the big visit shape, Nd >= ZDP_CH_BIG_ND; 2^22
+// from Nd = ZDP_SPLIT_HUGE_ND).  One grid-stride launch over 10^8
 // elements measured 3-16% slower than the same work in such launches (Nd
 // 16, 64 and 400); shorter windows take one launch, where the few
 // microseconds an extra launch costs outweigh the gain.  The 8-group visits
 // of the big shape run 1-2% faster in launches of 2^23 than of 2^24 (the
-// GPT-2-XL shard at Nd = 16 runs 1.4% slower there).
+// GPT-2-XL shard at Nd = 16 runs 1.4% slower there).  Launches of 2^22
+// measured 0.9-1% faster than 2^23 at Nd = 400 and 1-6% slower at Nd 32,
+// 48, 64 and 100 (paired, in one process); 256 is a boundary between the
+// two measured sides.
 int64_t split_elems(int32_t nd) {
-    const int l = nd >= ZDP_CH_BIG_ND ? ZDP_SPLIT_BIG_LOG2 : ZDP_SPLIT_LOG2;
+    const int l = nd >= ZDP_SPLIT_HUGE_ND ? ZDP_SPLIT_BIG_LOG2 - 1
+                  : nd >= ZDP_CH_BIG_ND   ? ZDP_SPLIT_BIG_LOG2
+                                          : ZDP_SPLIT_LOG2;
     return l > 0 ? (int64_t{1} << l) : 0;
 }
 
