@@ -61,6 +61,9 @@ def parse():
                     help="> 0: dynamic loss scaling with this growth interval")
     ap.add_argument("--bucket-elems", type=int, default=0,
                     help="> 0: bucketed step, the window ingested in buckets of this many elements")
+    ap.add_argument("--buckets-per-call", type=int, default=1,
+                    help="bucketed step: pass this many consecutive arrived buckets to one "
+                         "zero_adam_step_buckets call (1: zero_adam_step_bucket per bucket)")
     ap.add_argument("--arrival", action="store_true",
                     help="bucketed step: copy each bucket into one of two constant-size receive "
                          "buffers on a side stream (the simulated reduce-scatter arrival), "
@@ -70,6 +73,9 @@ def parse():
     ap.add_argument("--gather-layers", action="store_true",
                     help="time the Pos+g+p on-demand gather of every layer (GPT-2 shaped workloads) "
                          "instead of the step")
+    ap.add_argument("--layers-per-call", type=int, default=1,
+                    help="with --gather-layers: gather this many consecutive layers per zero_gather_layers "
+                         "call (one layer buffer each)")
     ap.add_argument("--gather-streams", type=int, default=1, choices=(1, 2, 3, 4),
                     help="with --gather-layers: N > 1 rotates the layers over N streams (layer buffer "
                          "k %% N on stream k %% N), so one layer's gather overlaps the next ones' launches")
@@ -78,6 +84,10 @@ def parse():
         ap.error("--bucket-elems must be a multiple of 8, and cannot be combined with clipping")
     if a.arrival and not a.bucket_elems:
         ap.error("--arrival needs --bucket-elems")
+    if a.buckets_per_call < 1 or (a.buckets_per_call > 1 and (a.arrival or not a.bucket_elems)):
+        ap.error("--buckets-per-call > 1 needs --bucket-elems and buckets read in place (no --arrival)")
+    if a.layers_per_call < 1:
+        ap.error("--layers-per-call must be >= 1")
     return a
 
 
@@ -296,8 +306,11 @@ def bench_gather(args):
             del t
         sets.append(ws)
     biggest = max(hi - lo for lo, hi in ranges)
+    K = args.layers_per_call
+    calls = [ranges[c:c + K] for c in range(0, len(ranges), K)]  # the layers gathered together
     nbuf = max(2, args.gather_streams)
-    bufs = [torch.empty(biggest, dtype=torch.float16, device=dev) for _ in range(nbuf)]
+    # one layer buffer per layer of a call, for each of nbuf calls in turn
+    bufs = [[torch.empty(biggest, dtype=torch.float16, device=dev) for _ in range(K)] for _ in range(nbuf)]
     stream = torch.cuda.current_stream()
     # layer buffer b is only ever written on streams[b], so reuse is ordered
     if args.gather_streams > 1:
@@ -309,8 +322,13 @@ def bench_gather(args):
 
     def one_pass(i):
         ws = sets[i % copies]
-        for k, (lo, hi) in enumerate(ranges):
-            B.gather_params(ws, part, lo, hi, bufs[k % nbuf], streams[k % nbuf])
+        for k, group in enumerate(calls):
+            if K == 1:
+                lo, hi = group[0]
+                B.gather_params(ws, part, lo, hi, bufs[k % nbuf][0], streams[k % nbuf])
+            else:
+                B.gather_layers(ws, part, group, [b[:hi - lo] for b, (lo, hi) in zip(bufs[k % nbuf], group)],
+                                streams[k % nbuf])
 
     for i in range(args.warmup):
         one_pass(i)
@@ -332,7 +350,8 @@ def bench_gather(args):
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
     pieces = sum(1 + (hi - 1) // part - lo // part for lo, hi in ranges if hi > lo)
-    launches = sum(-(-(1 + (hi - 1) // part - lo // part) // 16) for lo, hi in ranges if hi > lo)
+    launches = sum(-(-sum(1 + (hi - 1) // part - lo // part for lo, hi in group if hi > lo) // 16)
+                   for group in calls)
     gbs = 4 * w.psi / (ms * 1e-3) / 1e9
     log(f"gather pass: {ms * 1e3:.1f} us ({launches} launches, {pieces} window pieces), {gbs:.0f} GB/s")
     cpu = None
@@ -350,10 +369,12 @@ def bench_gather(args):
         "config": {"workload": f"{w.key}: every layer of {w.title}", "layers": len(ranges),
                    "largest_layer": biggest, "nd": w.nd, "window": part, "launches_per_pass": launches,
                    "window_pieces_per_pass": pieces, "streams": args.gather_streams,
+                   "layers_per_call": K,
                    "window_sets_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": None,
-                     "algorithmic_bytes_per_pass": 4 * w.psi, "kernel": "copy_f16_kernel",
+                     "algorithmic_bytes_per_pass": 4 * w.psi,
+                     "kernel": "copy_f16_kernel" + (f" ({K} layers per zero_gather_layers call)" if K > 1 else ""),
                      "kernel_fingerprint": kernel_fingerprint()},
         "cpu_baseline": cpu,
     }
@@ -477,6 +498,14 @@ def measure_step(args, w, steps, warmup, graph=False, skip_timing=False):
     def launch_bucketed(i, s):
         sh = shards[i % n_shards]
         gs = gsets[i % rot]
+        if args.buckets_per_call > 1:
+            K = args.buckets_per_call
+            calls = [buckets[c:c + K] for c in range(0, len(buckets), K)]
+            for c, group in enumerate(calls):
+                phase = (B.BUCKET_FIRST if c == 0 else 0) | (B.BUCKET_LAST if c == len(calls) - 1 else 0)
+                B.adam_step_buckets([(B.grad_src(gs, S, o, k, w.nd, w.loss_scale), o) for o, k in group],
+                                    sh.state, sh.hp, S, ag, ag_offs[i % n_shards], phase, sh.workspace, s)
+            return
         for b, (o, k) in enumerate(buckets):
             phase = (B.BUCKET_FIRST if b == 0 else 0) | (B.BUCKET_LAST if b == len(buckets) - 1 else 0)
             if args.arrival:
@@ -752,6 +781,7 @@ def main():
             "dynamic_scale_interval": args.dynamic_scale,
             "bucket_elems": args.bucket_elems,
             "bucket_arrival_copies": bool(args.arrival),
+            "buckets_per_call": args.buckets_per_call if bucketed else None,
             "graph_step_us": res["graph_us"],
             "skipped_step": res["skip"],
             "memory_model": mm,
@@ -769,7 +799,9 @@ def main():
             "traffic_bytes_per_launch": traffic,
             "algorithmic_bytes_per_launch": bytes_elem * S,
             "kernel": ("reduce_owned_kernel + clipped_update_kernel + commit_kernel" if clipped else
-                       f"fused_step_kernel x {res['n_buckets']} buckets + commit_kernel" if bucketed else
+                       (f"fused_runs_kernel, {res['n_buckets']} buckets in calls of {args.buckets_per_call}"
+                        " + commit_kernel" if args.buckets_per_call > 1 else
+                        f"fused_step_kernel x {res['n_buckets']} buckets + commit_kernel") if bucketed else
                        "fused_step_kernel + commit_kernel"),
             "kernel_avg_us": kern_avg * 1e3,
             "kernel_us_p10_p50_p90_per_launch_events": res["pcts_us"],

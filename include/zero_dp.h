@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define ZERO_DP_ABI_VERSION 5
+#define ZERO_DP_ABI_VERSION 6
 
 /* ---- status codes --------------------------------------------------- */
 #define ZERO_OK          0
@@ -364,6 +364,36 @@ int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st,
                           uint16_t* allgather, int64_t allgather_off, int32_t phase,
                           void* workspace, void* stream);
 
+/* ---- several arrived buckets in one call ------------------------------
+ * The same step as a sequence of zero_adam_step_bucket calls, one per
+ * bucket in list order, for the buckets that have arrived together: their
+ * elements are stepped in as few launches as fit (consecutive buckets
+ * share a launch up to 16 runs and one launch length, about 2^24 elements
+ * below Nd = 32; a bucket longer than two launch lengths is cut as a long
+ * window is).  A bucket's fixed cost is then paid per launch rather than
+ * per bucket: the launch, the ramp of its first loads and the drain of its
+ * last stores.  Per element the results are those of the one-bucket calls
+ * bit for bit; the sum of g^2 differs only in its rounding order.  phase
+ * applies to the call: ZERO_BUCKET_FIRST if its first bucket is the step's
+ * first, ZERO_BUCKET_LAST to commit after its last bucket.  Calls and
+ * one-bucket calls may be mixed within a step (all on the same stream and
+ * workspace).  A bucket b reads b->src (its receive buffer; nd and
+ * loss_scale equal across the call) for window elements
+ * [b->win_off, b->win_off + b->src.n); the buckets of a call may not cover
+ * the same element twice (ZERO_EINVAL).  Other arguments and rules are
+ * those of zero_adam_step_bucket (window_n, allgather, allgather_off the
+ * whole window's).  1 <= nb <= ZERO_MAX_BUCKETS_PER_CALL.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EALIAS, ZERO_EHIP.
+ */
+typedef struct zero_bucket {
+    zero_grad_src src;   /* the bucket's slices (src.n elements of each) */
+    int64_t win_off;     /* window offset of its first element; multiple of 8 */
+} zero_bucket;
+#define ZERO_MAX_BUCKETS_PER_CALL 1024
+int zero_adam_step_buckets(const zero_bucket* buckets, int32_t nb, const zero_adam_state* st,
+                           const zero_adam_hp* hp, int64_t window_n, uint16_t* allgather,
+                           int64_t allgather_off, int32_t phase, void* workspace, void* stream);
+
 /* Re-emits allgather[off + j] = fp16_RNE(master[ctl->cur][j]) for j < n when
  * ctl->overflow != 0 (the step was skipped), and does nothing otherwise; the
  * decision is taken on the device, so no host synchronisation is needed.
@@ -402,6 +432,18 @@ int zero_restore_skipped(const zero_adam_state* st, int64_t n, uint16_t* allgath
  */
 int zero_gather_params(const uint16_t* const* windows, int32_t nd, int64_t part,
                        int64_t lo, int64_t hi, uint16_t* dst, void* stream);
+
+/* Several layers' gathers in one call: range q is flat elements
+ * [ranges[2q], ranges[2q+1]) into dsts[q] (host array of nranges device
+ * pointers), as zero_gather_params would copy it.  The ranges' window
+ * pieces share launches, up to 16 pieces per launch, so gathering a few
+ * short layers at once (the current layer with the next ones, ahead of
+ * use) pays one launch's fixed cost instead of one per layer.  No
+ * destination may overlap another or a window piece any range reads.  An
+ * empty range copies nothing.  nranges >= 0.  Errors as zero_gather_params.
+ */
+int zero_gather_layers(const uint16_t* const* windows, int32_t nd, int64_t part, const int64_t* ranges,
+                       int32_t nranges, uint16_t* const* dsts, void* stream);
 
 /* ---- emit (all-gather half) ------------------------------------------
  * allgather[allgather_off + j] = fp16_RNE(master[j]) for j < n (IEEE

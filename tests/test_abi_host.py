@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(L):
     for name in declared:
         assert hasattr(L, name), name
     assert declared == set(B.EXPORTED)
-    assert L.zero_abi_version() == B.ABI_VERSION == 5
+    assert L.zero_abi_version() == B.ABI_VERSION == 6
 
 
 def test_strerror(L):
@@ -294,6 +294,64 @@ def test_other_validation(L):
     assert L.zero_restore_skipped(C.byref(_state(ctl=(1 << 30) + 4)), 8, 1 << 29, 0, None) == B.ZERO_EALIGN
     assert L.zero_restore_skipped(C.byref(st), 64, 1 << 24, 0, None) == B.ZERO_EALIAS   # window on master[0]
     assert L.zero_restore_skipped(C.byref(st), 64, (1 << 30) - 64, 0, None) == B.ZERO_EALIAS  # covers the ctl
+
+
+@no_gpu
+def test_bucket_list_validation(L):
+    hp = B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    st = _state()  # a window of 64 elements
+
+    def call(items, nb=None, window_n=64, phase=B.BUCKET_FIRST, hpp=hp, state=st, ag=None, ag_off=0):
+        arr = (B.Bucket * max(len(items), 1))(*[B.Bucket(s, o) for s, o in items])
+        return L.zero_adam_step_buckets(arr, len(items) if nb is None else nb, C.byref(state), C.byref(hpp),
+                                        window_n, ag, ag_off, phase, 1 << 28, None)
+
+    ok = [(B.grad_src(A, 16, 0, 16, 4, 1024.0), 0), (B.grad_src(A + 4096, 16, 0, 16, 4, 1024.0), 16)]
+    assert call(ok, nb=0) == B.ZERO_EINVAL
+    assert call(ok, nb=B.MAX_BUCKETS_PER_CALL + 1) == B.ZERO_EINVAL
+    assert L.zero_adam_step_buckets(None, 1, C.byref(st), C.byref(hp), 64, None, 0, 1, 1 << 28, None) == \
+        B.ZERO_EINVAL
+    assert call(ok, phase=4) == B.ZERO_EINVAL
+    assert call(ok, window_n=-1) == B.ZERO_EINVAL
+    assert call([ok[0], (ok[1][0], 8)]) == B.ZERO_EINVAL           # two buckets cover elements 8..15
+    assert call([ok[0], (ok[1][0], 56)]) == B.ZERO_EINVAL          # past the window
+    assert call([ok[0], (ok[1][0], 20)]) == B.ZERO_EALIGN          # offsets are multiples of 8
+    assert call([ok[0], (ok[1][0], -8)]) == B.ZERO_EINVAL
+    assert call([ok[0], (B.grad_src(A + 4096, 16, 0, 16, 5, 1024.0), 16)]) == B.ZERO_EINVAL  # Nd differs
+    assert call([ok[0], (B.grad_src(A + 4096, 16, 0, 16, 4, 512.0), 16)]) == B.ZERO_EINVAL   # scale differs
+    assert call([ok[0], (B.grad_src(A + 4096, 16, 0, 16, 4, 0.0), 16)]) == B.ZERO_EINVAL
+    assert call([ok[0], (B.grad_src(A + 4098, 16, 0, 16, 4, 1024.0), 16)]) == B.ZERO_EALIGN
+    assert call([ok[0], (B.grad_src(1 << 24, 16, 0, 16, 4, 1024.0), 16)]) == B.ZERO_EALIAS  # slices on master[0]
+    assert call(ok, hpp=B.adam_hp(1e-3, 0.9, 0.999, 1e-8, 0.0, max_grad_norm=1.0)) == B.ZERO_EINVAL
+    assert call(ok, state=_state(ctl=None)) == B.ZERO_EINVAL
+    assert call(ok, ag=1 << 29, ag_off=4) == B.ZERO_EALIGN
+    assert call(ok, ag=A + 64) == B.ZERO_EALIAS                    # the all-gather window on bucket 0's slices
+    assert call([(B.grad_src(A, 16, 0, 2 ** 62, 4, 1024.0), 2 ** 62)], window_n=2 ** 62) == B.ZERO_EOVERFLOW
+
+
+@no_gpu
+def test_gather_layers_validation(L):
+    part = 1024
+    wins = (C.c_void_p * 4)(1 << 24, 1 << 25, 1 << 26, 1 << 27)
+
+    def g(ranges, dsts, w=wins, nd=4, prt=part, nr=None):
+        rr = (C.c_int64 * max(2 * len(ranges), 1))(*[x for r in ranges for x in r])
+        dd = (C.c_void_p * max(len(dsts), 1))(*dsts)
+        return L.zero_gather_layers(w, nd, prt, rr, len(ranges) if nr is None else nr, dd, None)
+
+    assert g([(0, 10)], [1 << 29], nr=-1) == B.ZERO_EINVAL
+    assert g([(0, 10)], [1 << 29], w=None) == B.ZERO_EINVAL
+    assert g([(0, 10), (10, 5)], [1 << 29, 1 << 30]) == B.ZERO_EINVAL          # hi < lo
+    assert g([(0, 10), (0, 4 * part + 1)], [1 << 29, 1 << 30]) == B.ZERO_EINVAL
+    assert g([(0, 10), (20, 30)], [1 << 29, None]) == B.ZERO_EINVAL
+    assert g([(0, 10), (20, 30)], [1 << 29, (1 << 30) + 1]) == B.ZERO_EALIGN
+    assert g([(0, 10), (20, 30)], [1 << 29, (1 << 29) + 8]) == B.ZERO_EALIAS     # destinations overlap
+    assert g([(0, 10), (part, part + 8)], [1 << 29, (1 << 25) + 2]) == B.ZERO_EALIAS  # dst on window 1's piece
+    assert g([(0, 10)], [1 << 29], prt=2 ** 62) == B.ZERO_EOVERFLOW
+    holes = (C.c_void_p * 4)(1 << 24, None, 1 << 26, 1 << 27)
+    assert g([(0, 10), (part - 4, part + 4)], [1 << 29, 1 << 30], w=holes) == B.ZERO_EINVAL
+    assert g([], []) == B.ZERO_OK                                                # nothing to do
+    assert g([(7, 7), (9, 9)], [None, None]) == B.ZERO_OK                        # empty ranges
 
 
 @no_gpu

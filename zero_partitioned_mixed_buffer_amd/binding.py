@@ -30,9 +30,9 @@ EXPORTED = (
     "zero_memory_model", "zero_workspace_bytes", "zero_reduce_owned", "zero_ctl_init",
     "zero_adam_step", "zero_adam_step_clipped", "zero_adam_step_bucket", "zero_restore_skipped",
     "zero_emit_fp16", "zero_gather_params", "zero_adam_step_noalloc", "zero_calib_triad",
-    "zero_calib_stream_mix",
+    "zero_calib_stream_mix", "zero_adam_step_buckets", "zero_gather_layers",
 )
-ABI_VERSION = 5
+ABI_VERSION = 6
 BUCKET_FIRST = 1
 BUCKET_LAST = 2
 
@@ -70,6 +70,13 @@ class StepCtl(C.Structure):
     _fields_ = [("cur", C.c_int32), ("t", C.c_int32), ("overflow", C.c_int32), ("good_steps", C.c_int32),
                 ("beta1_pow", C.c_double), ("beta2_pow", C.c_double), ("sumsq", C.c_double),
                 ("skipped", C.c_int64), ("loss_scale", C.c_double), ("clip_coef", C.c_double)]
+
+
+class Bucket(C.Structure):
+    _fields_ = [("src", GradSrc), ("win_off", C.c_int64)]
+
+
+MAX_BUCKETS_PER_CALL = 1024
 
 
 class AdamState(C.Structure):
@@ -115,10 +122,15 @@ def lib():
     L.zero_restore_skipped.argtypes = [C.POINTER(AdamState), C.c_int64, P, C.c_int64, P]
     L.zero_emit_fp16.argtypes = [P, C.c_int64, P, C.c_int64, P]
     L.zero_gather_params.argtypes = [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int64, C.c_int64, P, P]
+    L.zero_adam_step_buckets.argtypes = [C.POINTER(Bucket), C.c_int32, C.POINTER(AdamState), C.POINTER(AdamHp),
+                                         C.c_int64, P, C.c_int64, C.c_int32, P, P]
+    L.zero_gather_layers.argtypes = [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.POINTER(C.c_int64), C.c_int32,
+                                     C.POINTER(C.c_void_p), P]
     L.zero_calib_triad.argtypes = [P, P, P, C.c_float, C.c_int64, P]
     L.zero_calib_stream_mix.argtypes = [C.POINTER(GradSrc), C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), P, P]
     for name in ("zero_plan_partitions", "zero_memory_model", "zero_reduce_owned", "zero_adam_step",
-                 "zero_adam_step_noalloc", "zero_calib_triad", "zero_calib_stream_mix",
+                 "zero_adam_step_noalloc", "zero_calib_triad", "zero_calib_stream_mix", "zero_adam_step_buckets",
+                 "zero_gather_layers",
                  "zero_adam_step_clipped", "zero_adam_step_bucket", "zero_restore_skipped", "zero_emit_fp16",
                  "zero_gather_params"):
         getattr(L, name).restype = C.c_int
@@ -337,6 +349,19 @@ def adam_step_bucket(src: GradSrc, state: AdamState, hp: AdamHp, win_off: int, w
                                        _stream(stream)), "zero_adam_step_bucket")
 
 
+def adam_step_buckets(buckets: Sequence[Tuple[GradSrc, int]], state: AdamState, hp: AdamHp, window_n: int,
+                      allgather, allgather_off: int, phase: int, workspace, stream=None):
+    """Several arrived buckets of a bucketed step in one call: ``buckets``
+    lists (gradient source, window offset) pairs."""
+    _check_state(state, window_n)
+    _check_span(allgather, allgather_off, window_n, _F16, "all-gather buffer")
+    _check_ws(workspace)
+    arr = (Bucket * max(len(buckets), 1))(*[Bucket(src, int(off)) for src, off in buckets])
+    _check(lib().zero_adam_step_buckets(arr, len(buckets), C.byref(state), C.byref(hp), int(window_n),
+                                        _ptr(allgather), int(allgather_off), int(phase), _ptr(workspace),
+                                        _stream(stream)), "zero_adam_step_buckets")
+
+
 def restore_skipped(state: AdamState, n: int, allgather, allgather_off: int, stream=None):
     _check_state(state, n)
     _check_span(allgather, allgather_off, n, _F16, "all-gather buffer")
@@ -361,6 +386,23 @@ def gather_params(windows: Sequence, part: int, lo: int, hi: int, dst, stream=No
     arr = (C.c_void_p * max(len(windows), 1))(*[_ptr(w) for w in windows])
     _check(lib().zero_gather_params(arr, len(windows), int(part), int(lo), int(hi), _ptr(dst), _stream(stream)),
            "zero_gather_params")
+
+
+def gather_layers(windows: Sequence, part: int, ranges: Sequence[Tuple[int, int]], dsts: Sequence, stream=None):
+    """Flat ranges [lo, hi) of the partitioned fp16 parameters, range q into
+    dsts[q], with the ranges' pieces sharing launches."""
+    for (lo, hi), d in zip(ranges, dsts):
+        if part > 0 and hi > lo:
+            for w in windows[max(lo, 0) // part:min((hi - 1) // part + 1, len(windows))]:
+                _check_span(w, 0, part, _F16, "parameter window")
+        _check_span(d, 0, max(hi - lo, 0), _F16, "layer buffer")
+    if len(ranges) != len(dsts):
+        raise ValueError("one destination per range")
+    arr = (C.c_void_p * max(len(windows), 1))(*[_ptr(w) for w in windows])
+    rng = (C.c_int64 * max(2 * len(ranges), 1))(*[int(x) for r in ranges for x in r])
+    dst = (C.c_void_p * max(len(dsts), 1))(*[_ptr(d) for d in dsts])
+    _check(lib().zero_gather_layers(arr, len(windows), int(part), rng, len(ranges), dst, _stream(stream)),
+           "zero_gather_layers")
 
 
 # ------------------------------------------------------------------ calibration

@@ -86,13 +86,13 @@ Partials make_ws(void* workspace) {
     return p;
 }
 
-// Validates the arguments of a step (fused or clipped) and fills the kernel
-// arguments.  `grad_buf` (the clipped path's fp32 gradient) may be null.
-int check_step(const zero_grad_src* src, const zero_adam_state* st, const zero_adam_hp* hp,
-               uint16_t* allgather, int64_t allgather_off, void* workspace, float* grad_buf, AdamArgs* a) {
-    Range span{};
-    int rc = check_src(src, &span);
-    if (rc != ZERO_OK) return rc;
+// Validates the state, hyperparameters, all-gather window, control block
+// and workspace of a step over a window of n elements, fills the kernel
+// arguments (the window's pointers), and lists the byte ranges the step
+// writes or owns in r[0 .. *nr) (r holds at least 10).  `grad_buf` (the
+// clipped path's fp32 gradient) may be null.
+int check_window(const zero_adam_state* st, const zero_adam_hp* hp, int64_t n, uint16_t* allgather,
+                 int64_t allgather_off, void* workspace, float* grad_buf, AdamArgs* a, Range* r, int* nr) {
     if (st == nullptr || hp == nullptr || st->ctl == nullptr || workspace == nullptr) return ZERO_EINVAL;
     if (!(hp->lr >= 0.0) || !__builtin_isfinite(hp->lr) || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
         !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps > 0.0) || !__builtin_isfinite(hp->eps) ||
@@ -104,18 +104,17 @@ int check_step(const zero_grad_src* src, const zero_adam_state* st, const zero_a
         (!(hp->scale_growth > 0.0) || !__builtin_isfinite(hp->scale_growth) || !(hp->scale_backoff > 0.0) ||
          !__builtin_isfinite(hp->scale_backoff)))
         return ZERO_EINVAL;
-    const int64_t n = src->n;
     int64_t b4 = 0;
+    if (n < 0) return ZERO_EINVAL;
     if (zdp::mul_overflows(n, 4, &b4)) return ZERO_EOVERFLOW;
     float* arrs[7] = {st->master[0],     st->master[1],     st->exp_avg[0], st->exp_avg[1],
                       st->exp_avg_sq[0], st->exp_avg_sq[1], grad_buf};
-    Range r[11];
-    int nr = 0;
+    int k = 0;
     for (int i = 0; i < 7; ++i) {
         if (i == 6 && grad_buf == nullptr) continue;
         if (arrs[i] == nullptr && n != 0) return ZERO_EINVAL;
         if (!aligned16(arrs[i])) return ZERO_EALIGN;
-        r[nr++] = bytes_of(arrs[i], n, 4);
+        r[k++] = bytes_of(arrs[i], n, 4);
     }
     if (!aligned16(workspace)) return ZERO_EALIGN;
     uint16_t* ag = nullptr;
@@ -125,14 +124,14 @@ int check_step(const zero_grad_src* src, const zero_adam_state* st, const zero_a
         if (zdp::add_overflows(allgather_off, n, &e) || zdp::mul_overflows(e, 2, &e)) return ZERO_EOVERFLOW;
         ag = allgather + allgather_off;
         if (!aligned16(ag)) return ZERO_EALIGN;
-        r[nr++] = bytes_of(ag, n, 2);
+        r[k++] = bytes_of(ag, n, 2);
     }
-    r[nr++] = span;
     // the control block and the workspace must not overlap any data either
     if ((reinterpret_cast<uintptr_t>(st->ctl) & 7u) != 0) return ZERO_EALIGN;
-    r[nr++] = bytes_of(st->ctl, 1, static_cast<int64_t>(sizeof(zero_step_ctl)));
-    r[nr++] = bytes_of(workspace, 1, zdp::kWsBytes);
-    if (any_overlap(r, nr)) return ZERO_EALIAS;
+    r[k++] = bytes_of(st->ctl, 1, static_cast<int64_t>(sizeof(zero_step_ctl)));
+    r[k++] = bytes_of(workspace, 1, zdp::kWsBytes);
+    if (any_overlap(r, k)) return ZERO_EALIAS;
+    *nr = k;
     for (int i = 0; i < 2; ++i) {
         a->p[i] = st->master[i];
         a->m[i] = st->exp_avg[i];
@@ -151,6 +150,64 @@ int check_step(const zero_grad_src* src, const zero_adam_state* st, const zero_a
     a->bucket = 0;
     a->window_n = n;
     a->run_count = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + zdp::kWsRunCount);
+    return ZERO_OK;
+}
+
+// Validates the arguments of a step (fused or clipped) over the window of
+// src->n elements and fills the kernel arguments.
+int check_step(const zero_grad_src* src, const zero_adam_state* st, const zero_adam_hp* hp,
+               uint16_t* allgather, int64_t allgather_off, void* workspace, float* grad_buf, AdamArgs* a) {
+    Range span{};
+    const int rc = check_src(src, &span);
+    if (rc != ZERO_OK) return rc;
+    Range r[11];
+    int nr = 0;
+    const int rc2 = check_window(st, hp, src->n, allgather, allgather_off, workspace, grad_buf, a, r, &nr);
+    if (rc2 != ZERO_OK) return rc2;
+    for (int i = 0; i < nr; ++i)
+        if (overlap(r[i], span)) return ZERO_EALIAS;
+    return ZERO_OK;
+}
+
+// Validates gather ranges [lo, hi) of a Psi = nd * part flat buffer, their
+// windows and destinations; an empty range is valid and gathers nothing.
+int check_gather(const uint16_t* const* windows, int32_t nd, int64_t part, const int64_t* ranges,
+                 int32_t nranges, uint16_t* const* dsts) {
+    if (windows == nullptr || nd < 1 || part < 1 || nranges < 0 || (nranges > 0 && (ranges == nullptr ||
+                                                                                      dsts == nullptr)))
+        return ZERO_EINVAL;
+    int64_t total = 0;
+    if (zdp::mul_overflows(static_cast<int64_t>(nd), part, &total)) return ZERO_EOVERFLOW;
+    for (int32_t q = 0; q < nranges; ++q) {
+        const int64_t lo = ranges[2 * q], hi = ranges[2 * q + 1];
+        if (lo < 0 || hi < lo || hi > total) return ZERO_EINVAL;
+        const int64_t n = hi - lo;
+        if (n == 0) continue;  // nothing to gather
+        uint16_t* dst = dsts[q];
+        int64_t bytes = 0;
+        if (dst == nullptr) return ZERO_EINVAL;
+        if (zdp::mul_overflows(n, 2, &bytes)) return ZERO_EOVERFLOW;
+        if ((reinterpret_cast<uintptr_t>(dst) & 1u) != 0) return ZERO_EALIGN;
+        const Range out = bytes_of(dst, n, 2);
+        // every piece is validated before anything is launched; a
+        // destination may overlap no window piece any range reads, nor
+        // another range's destination
+        for (int32_t q2 = 0; q2 < nranges; ++q2) {
+            const int64_t lo2 = ranges[2 * q2], hi2 = ranges[2 * q2 + 1];
+            if (lo2 < 0 || hi2 < lo2 || hi2 > total) return ZERO_EINVAL;
+            if (q2 != q && hi2 > lo2 && dsts[q2] != nullptr && overlap(out, bytes_of(dsts[q2], hi2 - lo2, 2)))
+                return ZERO_EALIAS;
+            for (int64_t f = lo2; f < hi2;) {
+                const int64_t r = f / part;
+                const int64_t take = ((r + 1) * part < hi2 ? (r + 1) * part : hi2) - f;
+                const uint16_t* w = windows[r];
+                if (w == nullptr) return ZERO_EINVAL;
+                if ((reinterpret_cast<uintptr_t>(w) & 1u) != 0) return ZERO_EALIGN;
+                if (overlap(bytes_of(w + (f - r * part), take, 2), out)) return ZERO_EALIAS;
+                f += take;
+            }
+        }
+    }
     return ZERO_OK;
 }
 
@@ -268,29 +325,60 @@ int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st, c
                               make_ws(workspace), stream);
 }
 
+int zero_adam_step_buckets(const zero_bucket* buckets, int32_t nb, const zero_adam_state* st,
+                           const zero_adam_hp* hp, int64_t window_n, uint16_t* allgather, int64_t allgather_off,
+                           int32_t phase, void* workspace, void* stream) {
+    if (buckets == nullptr || nb < 1 || nb > ZERO_MAX_BUCKETS_PER_CALL) return ZERO_EINVAL;
+    if ((phase & ~(ZERO_BUCKET_FIRST | ZERO_BUCKET_LAST)) != 0 || window_n < 0) return ZERO_EINVAL;
+    AdamArgs a;
+    Range r[11];
+    int nr = 0;
+    const int rc = check_window(st, hp, window_n, allgather, allgather_off, workspace, nullptr, &a, r, &nr);
+    if (rc != ZERO_OK) return rc;
+    if (hp->max_grad_norm != 0.0) return ZERO_EINVAL;  // clipping needs the norm before any bucket
+    zdp::BucketRun runs[ZERO_MAX_BUCKETS_PER_CALL];
+    for (int32_t i = 0; i < nb; ++i) {
+        const zero_bucket& b = buckets[i];
+        Range span{};
+        const int rc2 = check_src(&b.src, &span);
+        if (rc2 != ZERO_OK) return rc2;
+        if (b.src.nd != buckets[0].src.nd || b.src.loss_scale != buckets[0].src.loss_scale || b.win_off < 0)
+            return ZERO_EINVAL;
+        int64_t end = 0;
+        if (zdp::add_overflows(b.win_off, b.src.n, &end)) return ZERO_EOVERFLOW;
+        if (end > window_n) return ZERO_EINVAL;
+        if (b.win_off % 8 != 0) return ZERO_EALIGN;
+        // a bucket's slices may overlap nothing the step writes or owns
+        for (int k = 0; k < nr; ++k)
+            if (overlap(r[k], span)) return ZERO_EALIAS;
+        // nor may two buckets of one call cover the same window element
+        for (int32_t j = 0; j < i; ++j)
+            if (b.win_off < runs[j].win_off + runs[j].n && runs[j].win_off < end && b.src.n > 0 && runs[j].n > 0)
+                return ZERO_EINVAL;
+        runs[i] = zdp::BucketRun{b.src.base + b.src.elem_off, b.src.nd > 1 ? b.src.slice_stride : 0, b.src.n,
+                                 b.win_off};
+    }
+    return zdp::launch_buckets(runs, nb, make_src(&buckets[0].src, hp->scale_interval > 0 ? st->ctl : nullptr), a,
+                               phase, make_ws(workspace), stream);
+}
+
 int zero_gather_params(const uint16_t* const* windows, int32_t nd, int64_t part, int64_t lo, int64_t hi,
                        uint16_t* dst, void* stream) {
-    if (windows == nullptr || nd < 1 || part < 1 || lo < 0 || hi < lo) return ZERO_EINVAL;
-    int64_t total = 0, bytes = 0;
-    if (zdp::mul_overflows(static_cast<int64_t>(nd), part, &total)) return ZERO_EOVERFLOW;
-    if (hi > total) return ZERO_EINVAL;
-    const int64_t n = hi - lo;
-    if (n == 0) return ZERO_OK;  // nothing to gather
-    if (dst == nullptr) return ZERO_EINVAL;
-    if (zdp::mul_overflows(n, 2, &bytes)) return ZERO_EOVERFLOW;
-    if ((reinterpret_cast<uintptr_t>(dst) & 1u) != 0) return ZERO_EALIGN;
-    const Range out = bytes_of(dst, n, 2);
-    // every piece is validated before anything is launched
-    for (int64_t f = lo; f < hi;) {
-        const int64_t r = f / part;
-        const int64_t take = ((r + 1) * part < hi ? (r + 1) * part : hi) - f;
-        const uint16_t* w = windows[r];
-        if (w == nullptr) return ZERO_EINVAL;
-        if ((reinterpret_cast<uintptr_t>(w) & 1u) != 0) return ZERO_EALIGN;
-        if (overlap(bytes_of(w + (f - r * part), take, 2), out)) return ZERO_EALIAS;
-        f += take;
-    }
-    return zdp::launch_gather(windows, part, lo, hi, dst, stream);
+    const int64_t range[2] = {lo, hi};
+    const int rc = check_gather(windows, nd, part, range, 1, &dst);
+    if (rc != ZERO_OK) return rc;
+    if (hi == lo) return ZERO_OK;  // nothing to gather
+    return zdp::launch_gather(windows, part, range, 1, &dst, stream);
+}
+
+int zero_gather_layers(const uint16_t* const* windows, int32_t nd, int64_t part, const int64_t* ranges,
+                       int32_t nranges, uint16_t* const* dsts, void* stream) {
+    const int rc = check_gather(windows, nd, part, ranges, nranges, dsts);
+    if (rc != ZERO_OK) return rc;
+    int64_t total = 0;
+    for (int32_t q = 0; q < nranges; ++q) total += ranges[2 * q + 1] - ranges[2 * q];
+    if (total == 0) return ZERO_OK;  // nothing to gather
+    return zdp::launch_gather(windows, part, ranges, nranges, dsts, stream);
 }
 
 int zero_restore_skipped(const zero_adam_state* st, int64_t n, uint16_t* allgather,

@@ -90,9 +90,23 @@ int launch_step_clipped(const SrcArgs& src, const AdamArgs& a, float* grad_buf, 
 // the window's, for the commit after the last bucket).
 int launch_bucket(const SrcArgs& src, const AdamArgs& a, const AdamArgs& whole, int32_t phase,
                   const Partials& ws, void* stream);
-// Flat elements [lo, hi) of the windows into dst (zero_gather_params).
-int launch_gather(const uint16_t* const* windows, int64_t part, int64_t lo, int64_t hi, uint16_t* dst,
-                  void* stream);
+// One arrived bucket of a bucketed step: its slices (row stride `stride`,
+// n elements) and its first window element.
+struct BucketRun {
+    const uint16_t* win;
+    int64_t stride;
+    int64_t n;
+    int64_t win_off;
+};
+// Several buckets of one step in as few launches as fit (`a` holds the
+// window's state and all-gather pointers and window_n; `common` the slice
+// count and the loss scale); the commit follows when phase has LAST.
+int launch_buckets(const BucketRun* runs, int32_t nruns, const SrcArgs& common, const AdamArgs& a,
+                   int32_t phase, const Partials& ws, void* stream);
+// The flat ranges [ranges[2q], ranges[2q+1]) of the windows into dsts[q]
+// (zero_gather_params, zero_gather_layers).
+int launch_gather(const uint16_t* const* windows, int64_t part, const int64_t* ranges, int32_t nranges,
+                  uint16_t* const* dsts, void* stream);
 // The window re-emit of a skipped step, decided on the device.
 int launch_restore(const float* p0, const float* p1, const zero_step_ctl* ctl, uint16_t* ag, int64_t n,
                    void* stream);

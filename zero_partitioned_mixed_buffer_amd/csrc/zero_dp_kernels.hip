@@ -1038,28 +1038,16 @@ __device__ __forceinline__ void ch_dispatch(int64_t nfull, const SrcArgs& src, c
         ch_run<ZDP_CHS_U, ZDP_CHS_R, ZDP_CHS_PIPE != 0, ZDP_CHS_XP>(nfull, src, f, c, sq, bad);
 }
 
-__global__ void __launch_bounds__(kBlock) fused_step_kernel(SrcArgs src_in, AdamArgs a, Partials ws) {
-    const SrcArgs src = resolve_scale(src_in);
-    const int cur = a.ctl->cur;
-    double b1t, b2t;
-    const AdamScalars c = step_scalars(a, b1t, b2t);
-
-    const float* __restrict__ pin = a.p[cur];
-    const float* __restrict__ min_ = a.m[cur];
-    const float* __restrict__ vin = a.v[cur];
-    float* __restrict__ pout = a.p[cur ^ 1];
-    float* __restrict__ mout = a.m[cur ^ 1];
-    float* __restrict__ vout = a.v[cur ^ 1];
-    uint16_t* __restrict__ ag = a.ag;
-
+// The fused step over one contiguous run of the window: `src` holds the
+// run's slices, `f` its state and all-gather pointers; sq and bad
+// accumulate the run's sum of g^2 and flag.
+__device__ __forceinline__ void fused_run(const SrcArgs& src, const FusedPtrs& f, const AdamScalars& c,
+                                          double& sq, int& bad) {
     const int64_t ngroups = (src.n + kV - 1) / kV;
     const int64_t nfull = src.n / kV;
-    double sq = 0.0;
-    int bad = 0;
     bool done = false;
     if (src.nd <= kUnroll) {
         GroupIter it(ngroups);
-        const FusedPtrs f{pin, min_, vin, pout, mout, vout, ag};
         const int64_t endf = it.end < nfull ? it.end : nfull;
         done = pf_dispatch<kUnroll>(src.nd, it.gi, endf, it.step, src, f, c, sq, bad);
         if (done && ngroups > nfull) {
@@ -1068,14 +1056,61 @@ __global__ void __launch_bounds__(kBlock) fused_step_kernel(SrcArgs src_in, Adam
             if (g >= it.gi && g < it.end && (g - it.gi) % it.step == 0) fused_elems(g * kV, src.n, src, f, c, sq, bad);
         }
     }
-    if (!done) {
-        const FusedPtrs f{pin, min_, vin, pout, mout, vout, ag};
-        ch_dispatch(nfull, src, f, c, sq, bad);
-    }
+    if (!done) ch_dispatch(nfull, src, f, c, sq, bad);
+}
+
+__global__ void __launch_bounds__(kBlock) fused_step_kernel(SrcArgs src_in, AdamArgs a, Partials ws) {
+    const SrcArgs src = resolve_scale(src_in);
+    const int cur = a.ctl->cur;
+    double b1t, b2t;
+    const AdamScalars c = step_scalars(a, b1t, b2t);
+    const FusedPtrs f{a.p[cur], a.m[cur], a.v[cur], a.p[cur ^ 1], a.m[cur ^ 1], a.v[cur ^ 1], a.ag};
+    double sq = 0.0;
+    int bad = 0;
+    fused_run(src, f, c, sq, bad);
     // partials for commit_kernel (a bucket after the first adds to its slot)
     const bool more = a.bucket != 0 && (a.bucket & ZERO_BUCKET_FIRST) == 0;
     publish_partial(ws, sq, bad, more);
     if (a.bucket != 0 && blockIdx.x == 0 && threadIdx.x == 0) *a.run_count = (more ? *a.run_count : 0) + src.n;
+}
+
+// Several runs of a bucketed step in one launch (the buckets that have
+// arrived): run i reads its slices from win[i] (rows stride[i] apart) and
+// steps window elements [off[i], off[i] + n[i]); every run is spread over
+// the whole grid, as a one-run launch is, and each workgroup's partial
+// accumulates over the runs before it reaches its slot.
+constexpr int kMaxRuns = 16;
+struct RunList {
+    const uint16_t* win[kMaxRuns];
+    int64_t stride[kMaxRuns];
+    int64_t n[kMaxRuns];
+    int64_t off[kMaxRuns];
+    int32_t count;
+};
+
+__global__ void __launch_bounds__(kBlock) fused_runs_kernel(RunList rl, SrcArgs src_in, AdamArgs a, Partials ws) {
+    const SrcArgs base = resolve_scale(src_in);
+    const int cur = a.ctl->cur;
+    double b1t, b2t;
+    const AdamScalars c = step_scalars(a, b1t, b2t);
+    double sq = 0.0;
+    int bad = 0;
+    int64_t total = 0;
+    for (int i = 0; i < rl.count; ++i) {
+        SrcArgs s = base;
+        s.win = rl.win[i];
+        s.stride = rl.stride[i];
+        s.n = rl.n[i];
+        const int64_t o = rl.off[i];
+        const FusedPtrs f{a.p[cur] + o,     a.m[cur] + o,     a.v[cur] + o,
+                          a.p[cur ^ 1] + o, a.m[cur ^ 1] + o, a.v[cur ^ 1] + o,
+                          a.ag != nullptr ? a.ag + o : nullptr};
+        fused_run(s, f, c, sq, bad);
+        total += rl.n[i];
+    }
+    const bool more = (a.bucket & ZERO_BUCKET_FIRST) == 0;
+    publish_partial(ws, sq, bad, more);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.run_count = (more ? *a.run_count : 0) + total;
 }
 
 
@@ -1285,18 +1320,19 @@ __device__ __forceinline__ void copy_piece(const uint16_t* __restrict__ src, uin
     }
 }
 
-// The pieces of one gather (a layer's parts of consecutive windows), in
-// one launch: piece i copies len[i] elements from src[i] to dst + off[i].
+// The pieces of one launch of a gather (a layer's parts of consecutive
+// windows, or the parts of several layers): piece i copies len[i]
+// elements from src[i] to dst[i].
 constexpr int kMaxPieces = 16;
 struct CopyPieces {
     const uint16_t* src[kMaxPieces];
-    int64_t off[kMaxPieces];
+    uint16_t* dst[kMaxPieces];
     int64_t len[kMaxPieces];
     int32_t np;
 };
 
-__global__ void __launch_bounds__(kBlock) copy_f16_kernel(CopyPieces t, uint16_t* __restrict__ dst) {
-    for (int i = 0; i < t.np; ++i) copy_piece(t.src[i], dst + t.off[i], t.len[i]);
+__global__ void __launch_bounds__(kBlock) copy_f16_kernel(CopyPieces t) {
+    for (int i = 0; i < t.np; ++i) copy_piece(t.src[i], t.dst[i], t.len[i]);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1569,29 +1605,93 @@ int launch_bucket(const SrcArgs& src, const AdamArgs& a, const AdamArgs& whole, 
     return finish_launch();
 }
 
-int launch_gather(const uint16_t* const* windows, int64_t part, int64_t lo, int64_t hi, uint16_t* dst,
-                  void* stream) {
-    // the pieces, kMaxPieces per launch (one launch for any layer that
-    // touches at most kMaxPieces windows)
+int launch_buckets(const BucketRun* runs, int32_t nruns, const SrcArgs& common, const AdamArgs& a_in,
+                   int32_t phase, const Partials& ws, void* stream) {
+    // every launch of a step runs on the same grid (each workgroup adds its
+    // partial to its own slot); a run longer than two launch lengths is cut
+    // into pieces as a long window is, and consecutive pieces share a
+    // launch while they fit in one launch length and kMaxRuns
+    const int grid = fixed_grid(kFused);
+    const int64_t cap = split_elems(common.nd) > 0 ? split_elems(common.nd) : (int64_t{1} << 62);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    AdamArgs a = a_in;
+    bool first = (phase & ZERO_BUCKET_FIRST) != 0;
+    RunList rl{};
+    int64_t total = 0;
+    (void)hipGetLastError();
+    auto flush = [&]() {
+        if (rl.count == 0) return ZERO_OK;
+        a.bucket = 4 | (first ? ZERO_BUCKET_FIRST : 0);
+        fused_runs_kernel<<<grid, kBlock, 0, s>>>(rl, common, a, ws);
+        first = false;
+        rl = RunList{};
+        total = 0;
+        return finish_launch();
+    };
+    for (int32_t i = 0; i < nruns; ++i) {
+        const BucketRun& r = runs[i];
+        int64_t len = r.n;
+        if (split_window(r.n, common.nd)) {
+            const int64_t e = split_elems(common.nd);
+            const int64_t pieces = (r.n + e - 1) / e;
+            len = ((r.n + pieces - 1) / pieces + 1023) / 1024 * 1024;
+        }
+        int64_t off = 0;
+        do {
+            const int64_t k = r.n - off < len ? r.n - off : len;
+            if (rl.count == kMaxRuns || (rl.count > 0 && total + k > cap)) {
+                const int rc = flush();
+                if (rc != ZERO_OK) return rc;
+            }
+            rl.win[rl.count] = r.win + off;
+            rl.stride[rl.count] = r.stride;
+            rl.n[rl.count] = k;
+            rl.off[rl.count] = r.win_off + off;
+            ++rl.count;
+            total += k;
+            off += k;
+        } while (off < r.n);
+    }
+    const int rc = flush();
+    if (rc != ZERO_OK || (phase & ZERO_BUCKET_LAST) == 0) return rc;
+    a.bucket = ZERO_BUCKET_LAST | 4;
+    commit_kernel<<<grid_for(kCommit, a.window_n), kBlock, 0, s>>>(a, ws, grid, a.window_n, 0.0);
+    return finish_launch();
+}
+
+int launch_gather(const uint16_t* const* windows, int64_t part, const int64_t* ranges, int32_t nranges,
+                  uint16_t* const* dsts, void* stream) {
+    // the ranges' pieces in order, kMaxPieces per launch (one launch for a
+    // layer that touches at most kMaxPieces windows)
     const hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    for (int64_t f = lo; f < hi;) {
-        CopyPieces t{};
-        const int64_t first = f;
-        while (f < hi && t.np < kMaxPieces) {
+    CopyPieces t{};
+    int64_t total = 0;
+    auto flush = [&]() {
+        if (t.np == 0) return ZERO_OK;
+        copy_f16_kernel<<<copy_grid(total), kBlock, 0, s>>>(t);
+        t = CopyPieces{};
+        total = 0;
+        return finish_launch();
+    };
+    for (int32_t q = 0; q < nranges; ++q) {
+        const int64_t lo = ranges[2 * q], hi = ranges[2 * q + 1];
+        for (int64_t f = lo; f < hi;) {
             const int64_t r = f / part;
             const int64_t take = ((r + 1) * part < hi ? (r + 1) * part : hi) - f;
             t.src[t.np] = windows[r] + (f - r * part);
-            t.off[t.np] = f - first;
+            t.dst[t.np] = dsts[q] + (f - lo);
             t.len[t.np] = take;
             ++t.np;
+            total += take;
             f += take;
+            if (t.np == kMaxPieces) {
+                const int rc = flush();
+                if (rc != ZERO_OK) return rc;
+            }
         }
-        copy_f16_kernel<<<copy_grid(f - first), kBlock, 0, s>>>(t, dst + (first - lo));
-        const int rc = finish_launch();
-        if (rc != ZERO_OK) return rc;
     }
-    return ZERO_OK;
+    return flush();
 }
 
 int launch_restore(const float* p0, const float* p1, const zero_step_ctl* ctl, uint16_t* ag, int64_t n,

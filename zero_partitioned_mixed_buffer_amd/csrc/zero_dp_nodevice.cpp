@@ -27,7 +27,12 @@ int launch_step_clipped(const SrcArgs&, const AdamArgs&, float*, double, const P
 int launch_bucket(const SrcArgs&, const AdamArgs&, const AdamArgs&, int32_t, const Partials&, void*) {
     return no_device();
 }
-int launch_gather(const uint16_t* const*, int64_t, int64_t, int64_t, uint16_t*, void*) { return no_device(); }
+int launch_buckets(const BucketRun*, int32_t, const SrcArgs&, const AdamArgs&, int32_t, const Partials&, void*) {
+    return no_device();
+}
+int launch_gather(const uint16_t* const*, int64_t, const int64_t*, int32_t, uint16_t* const*, void*) {
+    return no_device();
+}
 int launch_restore(const float*, const float*, const zero_step_ctl*, uint16_t*, int64_t, void*) {
     return no_device();
 }
