@@ -660,7 +660,12 @@ def measure_step(args, w, steps, warmup, graph=False, skip_timing=False):
     # (2*Nd + 4) for the reduce pass + 30 for the update pass
     bytes_elem = 2 * w.nd + (34 if clipped else 26)
     achieved = bytes_elem * S / (kern_avg * 1e-3) / 1e9
-    what = (f"bucketed step ({len(buckets)} launches + commit)" if bucketed else
+    if bucketed and args.buckets_per_call > 1:
+        K = args.buckets_per_call
+        what = f"bucketed step ({len(buckets)} buckets in {-(-len(buckets) // K)} calls of up to {K} + commit)"
+    else:
+        what = None
+    what = what or (f"bucketed step ({len(buckets)} launches + commit)" if bucketed else
             "clipped step (reduce + update + commit kernels)" if clipped else "fused step (fused + commit kernels)")
     ms_step = wall * 1e3 / steps
     log(f"{w.key} {what}: avg {kern_avg * 1e3:.1f} us over {steps} back-to-back steps; "
