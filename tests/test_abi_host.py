@@ -121,6 +121,13 @@ def test_memory_model_errors(L):
     assert L.zero_memory_model(1e9, 4, 1, 12, None) == B.ZERO_EINVAL
 
 
+def test_ctl_bytes_round_trip():
+    c = B.ctl_from_bytes(B.ctl_init_bytes(512.0))
+    c.update(cur=1, t=7, overflow=1, good_steps=3, beta1_pow=0.9 ** 7, skipped=2, sumsq=1.5)
+    assert B.ctl_from_bytes(B.ctl_to_bytes(c)) == c
+    assert len(B.ctl_to_bytes(c)) == B.CTL_BYTES
+
+
 def test_ctl_init():
     c = B.ctl_from_bytes(B.ctl_init_bytes(4096.0))
     assert c == {"cur": 0, "t": 0, "overflow": 0, "good_steps": 0, "beta1_pow": 1.0, "beta2_pow": 1.0,

@@ -4,17 +4,15 @@ launch pieces from n).
 
 The seeded inputs are drawn on the device by torch's generator and copied
 to the host for the oracle; nothing the oracle sees comes from the HIP path.
-The fused step of every workload (C1-C5) is compared element by element
-over the whole window after every step: C1 and C2 (with, for C1/C2, the
-whole all-gather buffer) against the oracle stepping the whole window at
-once, C3-C5 against the oracle stepping the window in column chunks over a
-thread pool (elements are independent; sum g^2 is the chunks' exact sums
-added with fsum).  The clipped, bucketed and dynamically scaled variants at
-the GPT-2-XL and Nd = 400 sizes compare a sampled set of elements, whose
-oracle state the oracle carries from the generated initial parameters, plus
-what holds at any size: flags and step counts, sum of g^2 against a
-float64 torch reduction of the same slices, bit-identical state and window
-across a skipped step.
+Every test compares every element of the window after every step: C1 and
+C2 (with, for C1/C2, the whole all-gather buffer) against the oracle
+stepping the whole window at once; the GPT-2-XL, 7.5B and 60B shards --
+fused, clipped, bucketed and dynamically scaled -- against the oracle
+stepping the window in column chunks over a thread pool (elements are
+independent; sum g^2 and the clip norm are the chunks' exact sums added
+with fsum).  Flags, step counts and the loss scale are exact; a skipped
+step must leave the state and the window as the oracle's, which did not
+move.
 """
 import collections
 import os
@@ -50,29 +48,6 @@ def _setup(w, owner):
 
 def _hp(w):
     return dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
-
-
-def _sumsq_torch(torch, slices, L):
-    """sum((sum_k slices[k, j]) / L)^2 in float64 with torch (exact column
-    sums: fp16 values in float64), in column chunks of about 2 GB."""
-    chunk = max(1 << 16, (1 << 28) // slices.shape[0])
-    tot = torch.zeros((), dtype=torch.float64, device=slices.device)
-    for c in range(0, slices.shape[1], chunk):
-        g = slices[:, c:c + chunk].to(torch.float64).sum(0) * (1.0 / L)
-        tot += (g * g).sum()
-    return float(tot.item())
-
-
-def _sumsq32_torch(torch, slices, L):
-    """sum(fp32((sum_k slices[k, j]) * (1/L))^2) in float64 with torch: the
-    clipping norm's sum over fp32 gradients, in column chunks."""
-    chunk = max(1 << 16, (1 << 28) // slices.shape[0])
-    tot = torch.zeros((), dtype=torch.float64, device=slices.device)
-    inv = 1.0 / L
-    for c in range(0, slices.shape[1], chunk):
-        g = (slices[:, c:c + chunk].to(torch.float64).sum(0) * inv).to(torch.float32).to(torch.float64)
-        tot += (g * g).sum()
-    return float(tot.item())
 
 
 def test_c1_every_rank_full():
@@ -244,86 +219,6 @@ def _full_run(w, owner=0, inject=None, clip=0.0, steps=None, interval=0, bucket=
     return flags, ref
 
 
-def _sample_idx(S, n=1 << 16, extra=()):
-    g = np.random.default_rng(S % 1000003)
-    fixed = np.array([0, 1, 2, 3, S - 4, S - 3, S - 2, S - 1, S // 2 - 1, S // 2, S // 2 + 1, *extra],
-                     dtype=np.int64)
-    idx = np.unique(np.concatenate([g.integers(0, S, n, dtype=np.int64), fixed]))
-    return idx[(idx >= 0) & (idx < S)]
-
-
-def _sampled_run(w, owner=0, inject=None, clip=0.0, bucket=0, steps=None, interval=0):
-    """Steps the workload's window on the device (whole-window fused step,
-    clipped step with max_grad_norm = clip, or buckets of `bucket` elements
-    read in place) and the oracle on sampled elements.  With clipping the
-    oracle takes the window's norm from a float64 torch sum over the same
-    slices."""
-    torch, B, plan, S, valid = _setup(w, owner)
-    from zero_partitioned_mixed_buffer_amd import OwnedShard
-    idx = _sample_idx(S, extra=(inject[2],) if inject else ())
-    tidx = torch.from_numpy(idx).cuda()
-    master = torch.empty(S, dtype=torch.float32, device="cuda")
-    gen.device_fill_params(master, w.seed + owner, w.param_sigma, valid)
-    hp = dict(_hp(w), max_grad_norm=clip)
-    if interval:  # dynamic loss scaling from the workload's scale
-        hp.update(scale_interval=interval, loss_scale=w.loss_scale)
-    ref = oracle.OwnedShard(master[tidx].cpu().numpy(), **hp)
-    sh = OwnedShard(master, **hp)
-    del master
-    ag = torch.zeros(S + 16, dtype=torch.float16, device="cuda")
-    sh.emit(ag, 8)
-    say(f"{w.key}: S={S} Nd={w.nd}, {idx.size} sampled elements")
-    dsl = torch.empty((w.nd, S), dtype=torch.float16, device="cuda")
-    flags = []
-    for step in range(1, (steps or w.steps) + 1):
-        say(f"{w.key} step {step}: filling {2 * w.nd * S / 1e9:.1f} GB of slices")
-        L = ref.scale if interval else w.loss_scale  # the scale the slices carry
-        gen.device_fill_grads(dsl, w.seed, step, w.grad_sigma, L, w.dist, valid)
-        if inject is not None and inject[0] == step:
-            dsl[inject[1], inject[2]] = float("inf")
-        injected = inject is not None and inject[0] == step
-        sq32 = _sumsq32_torch(torch, dsl, L) if (clip and not injected) else None
-        ovf, _ = ref.step(dsl[:, tidx].cpu().numpy(), w.loss_scale, window_sumsq=sq32)
-        if ovf or injected:
-            prev = [x.clone() for x in sh.committed()]
-            prev_ag = ag.clone()
-        else:
-            sq_want = sq32 if clip else _sumsq_torch(torch, dsl, L)
-        if bucket:
-            say(f"{w.key} step {step}: {-(-S // bucket)} buckets of {bucket}")
-            for o in range(0, S, bucket):
-                k = min(bucket, S - o)
-                phase = (B.BUCKET_FIRST if o == 0 else 0) | (B.BUCKET_LAST if o + k >= S else 0)
-                sh.step_bucket(dsl, o, k, phase, w.loss_scale, elem_off=o, allgather=ag, allgather_off=8)
-        else:
-            say(f"{w.key} step {step}: {'clipped' if clip else 'fused'} step")
-            sh.step(dsl, w.loss_scale, allgather=ag, allgather_off=8)
-        torch.cuda.synchronize()
-        ctl = sh.control()
-        flags.append(ctl["overflow"])
-        assert ctl["overflow"] == int(ovf) and ctl["t"] == ref.t
-        if interval:
-            assert ctl["loss_scale"] == ref.scale and ctl["good_steps"] == ref.good_steps
-        if ctl["overflow"]:
-            # skipped: committed state and all-gather window bit-identical
-            for a, b in zip(prev, sh.committed(ctl)):
-                assert torch.equal(a.view(torch.int32), b.view(torch.int32))
-            assert torch.equal(prev_ag.view(torch.int16), ag.view(torch.int16))
-            del prev, prev_ag
-        else:
-            assert ctl["sumsq"] == pytest.approx(sq_want, rel=1e-12)
-            if clip:
-                assert ctl["clip_coef"] == pytest.approx(ref.coefs[-1], rel=1e-12)
-        p, m, v = (x[tidx].cpu().numpy() for x in sh.committed(ctl))
-        for got, want, nm in ((p, ref.p, "p"), (m, ref.m, "m"), (v, ref.v, "v")):
-            assert_state_close(got, want, f"{w.key} step {step} {nm}")
-        bits = ag.view(torch.int16)[8 + tidx].cpu().numpy().view(np.uint16)
-        assert_fp16_close(bits, ref.window().view(np.uint16), f"{w.key} step {step} window")
-    del dsl
-    torch.cuda.empty_cache()
-    return flags, ref
-
-
 def test_c3_gpt2_xl_adamw_full():
     """GPT-2-XL shaped list (1,557,611,200 params), Nd = 16, AdamW wd = 0.01,
     rank 0, 5 steps; every element of the window after every step."""
@@ -392,22 +287,24 @@ def test_c2_clipped_full():
     assert_fp16_close(bits, ref.window().view(np.uint16), "c2 clipped window")
 
 
-def test_c3_bucketed_sampled():
+def test_c3_bucketed_full():
     """GPT-2-XL shaped list, Nd = 16, AdamW: 3 steps ingested in 6 buckets of
-    2^24 elements (the benchmark's bucketed configuration), sampled."""
-    flags, ref = _sampled_run(configs.C3, bucket=1 << 24, steps=3)
+    2^24 elements (the benchmark's bucketed configuration), every element."""
+    flags, ref = _full_run(configs.C3, bucket=1 << 24, steps=3)
     assert flags == [0] * 3 and ref.t == 3
 
 
-def test_c3_clipped_sampled():
-    """GPT-2-XL shaped list, clipped step (max_grad_norm 1.0), 3 steps."""
-    flags, ref = _sampled_run(configs.C3, clip=1.0, steps=3)
+def test_c3_clipped_full():
+    """GPT-2-XL shaped list, clipped step (max_grad_norm 1.0), 3 steps; the
+    clip norm and coefficient from the oracle's chunked sum."""
+    flags, ref = _full_run(configs.C3, clip=1.0, steps=3)
     assert flags == [0] * 3 and max(ref.coefs) < 1.0
 
 
-def test_c5_clipped_overflow_sampled():
+def test_c5_clipped_overflow_full():
     """Nd = 400 Student-t(3) slices, clipped step (max_grad_norm 1.0), +inf
-    at step 2: flags [0, 1, 0], the clip coefficient from the window's norm."""
+    at step 2: flags [0, 1, 0], the clip coefficient from the window's norm
+    as the oracle sums it; every element of the window after every step."""
     w = configs.C5
     torch = torch_mod()
     free, _ = torch.cuda.mem_get_info()
@@ -415,17 +312,17 @@ def test_c5_clipped_overflow_sampled():
         pytest.skip(f"needs ~130 GB of free device memory ({free / 1e9:.0f} GB free)")
     from zero_partitioned_mixed_buffer_amd import binding as B
     S = B.plan_partitions(list(w.numels), w.nd, 256)[0]["part"]
-    flags, ref = _sampled_run(w, inject=(2, 17, S // 2), clip=1.0, steps=3)
+    flags, ref = _full_run(w, inject=(2, 17, S // 2), clip=1.0, steps=3)
     assert flags == [0, 1, 0] and ref.t == 2
     assert all(c < 1.0 for c in ref.coefs if c == c)
 
 
-def test_c3_dynamic_scale_overflow_sampled():
+def test_c3_dynamic_scale_overflow_full():
     """GPT-2-XL shaped list, AdamW, dynamic loss scaling (interval 2, from
     4096), +inf at step 2 in slice 5: the scale backs off to 2048 and grows
-    back to 4096 after two clean steps; 5 steps, sampled, the window split
-    into launches."""
+    back to 4096 after two clean steps; 5 steps, every element, the window
+    split into launches."""
     w = configs.C3
-    flags, ref = _sampled_run(w, inject=(2, 5, 12345), interval=2)
+    flags, ref = _full_run(w, inject=(2, 5, 12345), interval=2)
     assert flags == [0, 1, 0, 0, 0] and ref.t == 4
     assert ref.scales == [4096.0, 4096.0, 2048.0, 2048.0, 4096.0]

@@ -247,6 +247,14 @@ def ctl_from_bytes(b: bytes) -> dict:
     return {name: getattr(c, name) for name, _ in StepCtl._fields_}
 
 
+def ctl_to_bytes(fields: dict) -> bytes:
+    """The control block's bytes from its fields (the inverse of ctl_from_bytes)."""
+    c = StepCtl()
+    for name, _ in StepCtl._fields_:
+        setattr(c, name, fields[name])
+    return bytes(c)
+
+
 CTL_BYTES = C.sizeof(StepCtl)
 
 

@@ -3,7 +3,8 @@
 Holds the ping-pong fp32 Adam state, the device control block and the
 workspace, and forwards each step to the library (zero_adam_step, which
 also restores the all-gather window of a skipped step).  torch is used
-only to allocate device memory and to name the stream.
+only to allocate device memory and to name the stream.  A shard can be
+checkpointed (its committed state and control block) and resumed exactly.
 """
 from __future__ import annotations
 
@@ -77,3 +78,48 @@ class OwnedShard:
     def committed(self, ctl: Optional[dict] = None):
         cur = (ctl or self.control())["cur"]
         return self.master[cur], self.exp_avg[cur], self.exp_avg_sq[cur]
+
+    # ------------------------------------------------------------ checkpoint
+    def state_dict(self) -> dict:
+        """The committed state, enough to resume bit for bit: host copies of
+        the fp32 master, momentum and variance of the window, and the
+        control block (step count, running beta powers, loss scale,
+        clean-step count, last flag) as raw bytes.  Synchronises with the
+        device."""
+        import numpy as np
+        ctl = self.control()
+        p, m, v = (x.cpu().numpy() for x in self.committed(ctl))
+        return {"master": p, "exp_avg": m, "exp_avg_sq": v,
+                "ctl": np.frombuffer(bytes(self.ctl.cpu().numpy().tobytes()), dtype=np.uint8).copy()}
+
+    def load_state_dict(self, sd: dict):
+        """Restores a state_dict of a window of the same size: the state goes
+        to buffer set 0 and the control block is restored with cur = 0, so
+        the next step continues exactly where the saved shard left off."""
+        import numpy as np
+        import torch
+        for k in ("master", "exp_avg", "exp_avg_sq"):
+            a = np.asarray(sd[k])
+            if a.dtype != np.float32 or a.shape != (self.n,):
+                raise ValueError(f"{k}: expected float32[{self.n}], got {a.dtype}{list(a.shape)}")
+        raw = np.asarray(sd["ctl"], dtype=np.uint8).tobytes()
+        if len(raw) != B.CTL_BYTES:
+            raise ValueError(f"control block: expected {B.CTL_BYTES} bytes, got {len(raw)}")
+        fields = B.ctl_from_bytes(raw)
+        fields["cur"] = 0
+        dev = self.master[0].device
+        for dst, k in ((self.master[0], "master"), (self.exp_avg[0], "exp_avg"), (self.exp_avg_sq[0], "exp_avg_sq")):
+            dst.copy_(torch.from_numpy(np.ascontiguousarray(sd[k])).to(dev))
+        self.ctl.copy_(torch.frombuffer(bytearray(B.ctl_to_bytes(fields)), dtype=torch.uint8).to(dev))
+        torch.cuda.synchronize(dev)
+
+    def save(self, path: str):
+        """Writes state_dict() to a .npz file (plain arrays, no pickles)."""
+        import numpy as np
+        np.savez(path, **self.state_dict())
+
+    def load(self, path: str):
+        """Restores a file written by save() (loaded without pickles)."""
+        import numpy as np
+        with np.load(path, allow_pickle=False) as z:
+            self.load_state_dict({k: z[k] for k in ("master", "exp_avg", "exp_avg_sq", "ctl")})
