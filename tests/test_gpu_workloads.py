@@ -142,14 +142,28 @@ def _bounded_map(ex, depth):
     return pmap
 
 
-def _host_chunks(slices, n):
+class _HostChunks:
     """Column chunks (lo, hi, host fp16 [Nd, hi - lo]) of the window [0, n)
-    of a device slice buffer, each about 512 MB or 2^22 columns."""
-    nd = slices.shape[0]
-    width = max(1 << 16, min(1 << 22, 1 << (29 - max(1, (2 * nd - 1).bit_length()))))
-    for lo in range(0, n, width):
-        hi = min(n, lo + width)
-        yield lo, hi, slices[:, lo:hi].contiguous().cpu().numpy()
+    of a device slice buffer, each about 256 MB or 2^22 columns, staged
+    through `depth` reusable pinned host buffers.  With _bounded_map(ex,
+    depth) no chunk is still in a worker when its buffer is reused: a
+    chunk is produced only after the chunk `depth` places before it has
+    been consumed."""
+
+    def __init__(self, torch, nd, depth):
+        self.torch = torch
+        self.width = max(1 << 16, min(1 << 22, 1 << (28 - max(1, (2 * nd - 1).bit_length()))))
+        self.bufs = [torch.empty((nd, self.width), dtype=torch.float16, pin_memory=True) for _ in range(depth)]
+        self.copy_s = 0.0
+
+    def __call__(self, slices, n):
+        for i, lo in enumerate(range(0, n, self.width)):
+            hi = min(n, lo + self.width)
+            buf = self.bufs[i % len(self.bufs)][:, :hi - lo]
+            t0 = time.perf_counter()
+            buf.copy_(slices[:, lo:hi])
+            self.copy_s += time.perf_counter() - t0
+            yield lo, hi, buf.numpy()
 
 
 def _full_run(w, owner=0, inject=None, clip=0.0, steps=None, interval=0, bucket=0):
@@ -175,6 +189,7 @@ def _full_run(w, owner=0, inject=None, clip=0.0, steps=None, interval=0, bucket=
     sh.emit(ag, guard)
     dsl = torch.empty((w.nd, S), dtype=torch.float16, device="cuda")
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    chunks = _HostChunks(torch, w.nd, 2 * threads)
     flags = []
     with ThreadPoolExecutor(threads) as ex:
         pmap = _bounded_map(ex, 2 * threads)
@@ -195,9 +210,10 @@ def _full_run(w, owner=0, inject=None, clip=0.0, steps=None, interval=0, bucket=
             torch.cuda.synchronize()
             ctl = sh.control()
             t0 = time.perf_counter()
-            ovf, sq = ref.step_chunks(_host_chunks(dsl, S), w.loss_scale, pmap=pmap)
+            chunks.copy_s = 0.0
+            ovf, sq = ref.step_chunks(chunks(dsl, S), w.loss_scale, pmap=pmap)
             say(f"{w.key} step {step}: oracle over the window in {time.perf_counter() - t0:.1f} s "
-                f"({threads} threads), flag {int(ovf)}")
+                f"({threads} threads; {chunks.copy_s:.1f} s of it copying slices to the host), flag {int(ovf)}")
             flags.append(ctl["overflow"])
             assert ctl["overflow"] == int(ovf) and ctl["t"] == ref.t
             if interval:

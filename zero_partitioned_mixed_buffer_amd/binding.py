@@ -98,6 +98,14 @@ def lib():
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(f"{_LIB_PATH} is not built; run "
                            "`python -m zero_partitioned_mixed_buffer_amd.build_lib`")
+    # torch first: the library's libamdhip64.so.7 then resolves to the HIP
+    # runtime torch has loaded, and the process holds one HIP runtime.
+    # Loaded the other way round, torch loads a second copy of its own and
+    # the library's runtime reports no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = C.CDLL(_LIB_PATH)
     P = C.c_void_p
     L.zero_strerror.restype = C.c_char_p
