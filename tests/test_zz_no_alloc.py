@@ -105,3 +105,60 @@ def test_noalloc_validates_like_the_step():
     assert L.zero_adam_step_noalloc(None, C.byref(sh.state), C.byref(sh.hp), None, 0, stream) == B.ZERO_EINVAL
     torch.cuda.synchronize()
     assert sh.control()["t"] == 1
+
+
+def test_noalloc_steps_captured_in_a_graph():
+    """The allocation-free step is for code under graph capture: two steps
+    captured once and replayed four times, with fresh gradients written
+    eagerly and the program synchronising between the replays, must match
+    zero_adam_step with a workspace taken eagerly on a twin shard, bit for
+    bit, through skipped steps and dynamic loss scaling."""
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    n, nd = 65536 * 2 + 777, 5
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, scale_interval=3, loss_scale=1024.0)
+    _, shards, ags = _pair(torch, n, hp, 24)
+    eager, graphed = shards
+    stride = (n + 7) // 8 * 8
+    bufs = [torch.zeros((nd, stride), dtype=torch.float16, device="cuda") for _ in range(2)]
+    srcs = [B.grad_src(b, stride, 0, n, nd, 1.0) for b in bufs]
+
+    def fill(step):
+        for k, b in enumerate(bufs):
+            sl = gen.host_grad_slices(24, 2 * step + k, 0, nd, n, 0, n, 1e-3, 1024.0)
+            if (2 * step + k) % 5 == 3:
+                sl[k, (step * 7919) % n] = np.inf  # some steps are skipped
+            b[:, :n] = torch.from_numpy(sl).cuda()
+
+    def graphed_steps(stream):
+        for src in srcs:
+            B.adam_step_noalloc(src, graphed.state, graphed.hp, ags[1], 8, stream)
+
+    def eager_steps():
+        for src in srcs:
+            B.adam_step(src, eager.state, eager.hp, ags[0], 8, eager.workspace)
+
+    fill(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # first calls off the capture (scratch address, launch sizes)
+        graphed_steps(side)
+    torch.cuda.current_stream().wait_stream(side)
+    eager_steps()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        graphed_steps(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(4):
+        fill(rep + 1)
+        torch.cuda.synchronize()
+        graph.replay()
+        eager_steps()
+        torch.cuda.synchronize()
+        ce, cg = eager.control(), graphed.control()
+        assert ce == cg, (rep, ce, cg)
+        for a, b in zip(eager.committed(ce), graphed.committed(cg)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), rep
+        assert torch.equal(ags[0], ags[1]), rep
+    assert ce["t"] + ce["skipped"] == 2 + 2 * 4 and ce["skipped"] > 0
