@@ -232,7 +232,9 @@ def test_emit_parity():
                          "3f801000 3f803000 477fe000 477ff000 33000000 33400000 387fe000 80000000 "
                          "7f800000 ff800000 00000001 80000001 7f7fffff 3dcccccd".split()],
                         dtype=np.uint32).view(F32)
-    for n in (1, 7, 8, 4096 + 5, 300001):
+    # the larger windows give each lane several groups a grid stride apart
+    # (the emit loop takes four at a time, then the rest one by one)
+    for n in (1, 7, 8, 4096 + 5, 300001, (1 << 24) + 5, 13000003):
         x = (g.standard_normal(n) * 10.0 ** g.uniform(-9, 5, n)).astype(F32)
         x[:min(n, specials.size)] = specials[:min(n, specials.size)]
         d = torch.from_numpy(x).cuda()
