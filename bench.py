@@ -656,6 +656,22 @@ def measure_step(args, w, steps, warmup, graph=False, skip_timing=False):
         mix_us = m0.elapsed_time(m1) * 1e3 / steps
         mix = {"us": mix_us, "gbs": (2 * w.nd + 26) * S / (mix_us * 1e-6) / 1e9}
 
+        # The slice reads alone (2*Nd bytes per element) in the same visit
+        # order and launch pieces, with no state streams and no stores: the
+        # rate the step's slice streams attain by themselves.
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for i in range(max(1, min(warmup, 3))):
+            B.calib_slice_read(srcs[i % rot], sink, stream)
+        torch.cuda.synchronize()
+        m0.record(stream)
+        for i in range(steps):
+            B.calib_slice_read(srcs[i % rot], sink, stream)
+        m1.record(stream)
+        torch.cuda.synchronize()
+        read_us = m0.elapsed_time(m1) * 1e3 / steps
+        mix["slice_read_us"] = read_us
+        mix["slice_read_gbs"] = 2 * w.nd * S / (read_us * 1e-6) / 1e9
+
     # algorithmic bytes per owned element: fused 2*Nd + 26; clipped
     # (2*Nd + 4) for the reduce pass + 30 for the update pass
     bytes_elem = 2 * w.nd + (34 if clipped else 26)
@@ -673,6 +689,9 @@ def measure_step(args, w, steps, warmup, graph=False, skip_timing=False):
     if mix is not None:
         log(f"{w.key} the same streams with no arithmetic (stream-mix kernel): {mix['us']:.1f} us, "
             f"{mix['gbs']:.0f} GB/s; the step runs at {achieved / mix['gbs']:.3f} of it")
+        log(f"{w.key} the slice reads alone (slice-read kernel): {mix['slice_read_us']:.1f} us, "
+            f"{mix['slice_read_gbs']:.0f} GB/s of slice reads; they take {mix['slice_read_us'] / (kern_avg * 1e3):.3f} "
+            f"of the step's time")
     res = {
         "w": w, "S": S, "owner": owner, "rot": rot, "n_shards": n_shards, "full": full,
         "ms_step": ms_step, "kern_avg_ms": kern_avg, "pcts_us": [pct(0.1), pct(0.5), pct(0.9)],
@@ -734,7 +753,10 @@ def main():
                            "frac_of_peak": r["achieved_gbs"] / PEAK_HBM_GBS,
                            "elements_per_s": r["S"] / (r["ms_step"] * 1e-3),
                            "mix_gbs": r["mix"]["gbs"] if r["mix"] else None,
-                           "frac_of_mix": r["achieved_gbs"] / r["mix"]["gbs"] if r["mix"] else None}
+                           "frac_of_mix": r["achieved_gbs"] / r["mix"]["gbs"] if r["mix"] else None,
+                           "slice_read_gbs": r["mix"]["slice_read_gbs"] if r["mix"] else None,
+                           "slice_read_share": (r["mix"]["slice_read_us"] / (r["kern_avg_ms"] * 1e3)
+                                                if r["mix"] else None)}
 
     calibration_copy(torch, dev)
     attain = attainable_copy(torch, dev, B)
@@ -742,6 +764,10 @@ def main():
     if res["mix"] is not None:
         attain["mix_gbs"] = res["mix"]["gbs"]
         attain["mix_kernel"] = "stream_mix_kernel (this workload's streams, the step's launch shape, no arithmetic)"
+        attain["slice_read_gbs"] = res["mix"]["slice_read_gbs"]
+        attain["slice_read_us"] = res["mix"]["slice_read_us"]
+        attain["slice_read_kernel"] = ("slice_read_kernel (this workload's 2*Nd bytes of slice reads per element "
+                                       "alone, the step's visit order and launch pieces)")
     log(f"attainable on this GPU: copy {attain['copy_gbs']:.0f} GB/s, triad {attain['triad_gbs']:.0f} GB/s"
         + (f", this step's stream mix {attain['mix_gbs']:.0f} GB/s" if "mix_gbs" in attain else ""))
     traffic = None if (clipped or bucketed) else measured_traffic(w.key)
@@ -813,6 +839,9 @@ def main():
             "attainable": attain,
             "frac_of_attainable": achieved / attain["copy_gbs"],
             "frac_of_mix": achieved / attain["mix_gbs"] if "mix_gbs" in attain else None,
+            # the share of the step's time that its slice reads alone take
+            "slice_read_share": (attain["slice_read_us"] / (kern_avg * 1e3) if "slice_read_us" in attain
+                                 else None),
             "kernel_fingerprint": kernel_fingerprint(),
         },
         "cpu_baseline": cpu,

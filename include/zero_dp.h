@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define ZERO_DP_ABI_VERSION 6
+#define ZERO_DP_ABI_VERSION 7
 
 /* ---- status codes --------------------------------------------------- */
 #define ZERO_OK          0
@@ -476,6 +476,21 @@ int zero_emit_fp16(const float* master, int64_t n, uint16_t* allgather,
 int zero_calib_triad(float* a, const float* b, const float* c, float q, int64_t n, void* stream);
 int zero_calib_stream_mix(const zero_grad_src* src, const float* const* in, float* const* out,
                           uint16_t* out16, void* stream);
+
+/* The fused step's slice reads alone: the Nd fp16 slices of src's window
+ * (2*Nd bytes per element), read in the fused step's launch shape, visit
+ * order and launch pieces, with no state streams and no stores beside
+ * them.  The words read are folded with XOR and XORed into *sink (one
+ * atomic per workgroup and launch): bits 0-15 of the folded word are the
+ * XOR of the fp16 bit patterns of every slice at the window's even
+ * elements (counted from the window's first element), bits 16-31 those at
+ * its odd elements.  Clear *sink first to read that value; it has no other
+ * meaning.  The rate is what the step's slice streams attain on the GPU.
+ *   src as for the step (src->loss_scale is not used but must be valid);
+ *   sink: device uint32, 4-byte aligned, outside the slices' span.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EOVERFLOW, ZERO_EALIAS, ZERO_EHIP.
+ */
+int zero_calib_slice_read(const zero_grad_src* src, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

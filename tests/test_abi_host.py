@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(L):
     for name in declared:
         assert hasattr(L, name), name
     assert declared == set(B.EXPORTED)
-    assert L.zero_abi_version() == B.ABI_VERSION == 6
+    assert L.zero_abi_version() == B.ABI_VERSION == 7
 
 
 def test_strerror(L):
@@ -386,6 +386,13 @@ def test_calibration_validation(L):
     assert mix(C.byref(src), ins, (C.c_void_p * 3)(1 << 27, (1 << 27) + 128, 1 << 29), 1 << 30, None) == \
         B.ZERO_EALIAS  # two outputs overlap
     assert mix(C.byref(B.grad_src(A, 64, 0, 0, 4, 1024.0)), ins, outs, 1 << 30, None) == B.ZERO_OK  # empty
+    rd = L.zero_calib_slice_read
+    assert rd(C.byref(B.grad_src(A, 64, 0, 64, 0, 1024.0)), 1 << 30, None) == B.ZERO_EINVAL  # Nd = 0
+    assert rd(C.byref(B.grad_src(A, 64, 0, 64, 4, 0.0)), 1 << 30, None) == B.ZERO_EINVAL    # 1/L not finite
+    assert rd(C.byref(src), None, None) == B.ZERO_EINVAL
+    assert rd(C.byref(src), (1 << 30) + 2, None) == B.ZERO_EALIGN
+    assert rd(C.byref(src), A + 32, None) == B.ZERO_EALIAS                                  # sink in the slices
+    assert rd(C.byref(B.grad_src(A, 64, 0, 0, 4, 1024.0)), 1 << 30, None) == B.ZERO_OK       # empty
 
 
 def test_missing_library_fails_loudly(monkeypatch):

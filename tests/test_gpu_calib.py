@@ -1,8 +1,9 @@
 """The benchmark's bandwidth calibration kernels, checked for what they
 write (their traffic is what matters, but every byte they read must reach
-an output and nothing outside the outputs may change): STREAM's triad, and
-the stream-mix kernel with the fused step's streams (both visit shapes,
-split launch pieces, ragged tails)."""
+an output and nothing outside the outputs may change): STREAM's triad, the
+stream-mix kernel with the fused step's streams, and the slice reads alone
+(both visit shapes, the prefetch path, split launch pieces, ragged
+tails)."""
 import numpy as np
 import pytest
 
@@ -69,3 +70,31 @@ def test_stream_mix_values(nd, n):
     b16 = o16.cpu().numpy().view(np.uint16)
     assert np.array_equal(b16[:n], o16_want)
     assert all(np.all(x[n:] == 3.0) for x in got) and np.all(b16[n:] == 0x7E5A)
+
+
+@pytest.mark.parametrize("nd,n", [(1, 1003), (3, 4 * 65536 + 5), (8, 262147), (16, 100003), (17, 300001),
+                                  (24, 1000007), (31, 65543), (32, 200003), (48, 1 << 18), (99, 50021),
+                                  (400, 40961), (32, (1 << 24) + (1 << 22) + 5), (260, (1 << 23) + (1 << 22) + 7)])
+def test_slice_read_values(nd, n):
+    """The fold: bits 0-15 the XOR of every slice's fp16 bits at the
+    window's even elements, bits 16-31 at its odd elements, XORed into the
+    sink's previous value."""
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    stride = (n + 7) // 8 * 8 + 16
+    g = torch.Generator(device="cuda")
+    g.manual_seed(nd * 104729 + n)
+    sl = torch.randint(-32768, 32767, (nd, stride), dtype=torch.int16, device="cuda", generator=g)
+    sink = torch.tensor([0x12345678], dtype=torch.int32, device="cuda")
+    src = B.grad_src(sl.view(torch.float16), stride, 8, n, nd, 1.0)
+    B.calib_slice_read(src, sink)
+    torch.cuda.synchronize()
+    row = sl[0, 8:8 + n].clone()
+    for k in range(1, nd):
+        row.bitwise_xor_(sl[k, 8:8 + n])
+    h = row.cpu().numpy().view(np.uint16)
+    lo = int(np.bitwise_xor.reduce(h[0::2])) if n > 0 else 0
+    hi = int(np.bitwise_xor.reduce(h[1::2])) if n > 1 else 0
+    want = 0x12345678 ^ (lo | (hi << 16))
+    got = int(sink.cpu().numpy().view(np.uint32)[0])
+    assert got == want, (hex(got), hex(want))

@@ -30,9 +30,9 @@ EXPORTED = (
     "zero_memory_model", "zero_workspace_bytes", "zero_reduce_owned", "zero_ctl_init",
     "zero_adam_step", "zero_adam_step_clipped", "zero_adam_step_bucket", "zero_restore_skipped",
     "zero_emit_fp16", "zero_gather_params", "zero_adam_step_noalloc", "zero_calib_triad",
-    "zero_calib_stream_mix", "zero_adam_step_buckets", "zero_gather_layers",
+    "zero_calib_stream_mix", "zero_adam_step_buckets", "zero_gather_layers", "zero_calib_slice_read",
 )
-ABI_VERSION = 6
+ABI_VERSION = 7
 BUCKET_FIRST = 1
 BUCKET_LAST = 2
 
@@ -136,9 +136,10 @@ def lib():
                                      C.POINTER(C.c_void_p), P]
     L.zero_calib_triad.argtypes = [P, P, P, C.c_float, C.c_int64, P]
     L.zero_calib_stream_mix.argtypes = [C.POINTER(GradSrc), C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), P, P]
+    L.zero_calib_slice_read.argtypes = [C.POINTER(GradSrc), P, P]
     for name in ("zero_plan_partitions", "zero_memory_model", "zero_reduce_owned", "zero_adam_step",
                  "zero_adam_step_noalloc", "zero_calib_triad", "zero_calib_stream_mix", "zero_adam_step_buckets",
-                 "zero_gather_layers",
+                 "zero_gather_layers", "zero_calib_slice_read",
                  "zero_adam_step_clipped", "zero_adam_step_bucket", "zero_restore_skipped", "zero_emit_fp16",
                  "zero_gather_params"):
         getattr(L, name).restype = C.c_int
@@ -440,3 +441,12 @@ def calib_stream_mix(src: GradSrc, ins: Sequence, outs: Sequence, out16, stream=
     pout = (C.c_void_p * 3)(*[_ptr(t) for t in outs])
     _check(lib().zero_calib_stream_mix(C.byref(src), pin, pout, _ptr(out16), _stream(stream)),
            "zero_calib_stream_mix")
+
+
+def calib_slice_read(src: GradSrc, sink, stream=None):
+    """src's Nd slices read alone in the fused step's schedule; the XOR fold
+    of the words read is XORed into sink (a device int32/uint32 word)."""
+    if sink is not None and not isinstance(sink, int):
+        if _dtype_name(sink) not in ("int32", "uint32") or sink.numel() < 1 or not sink.is_cuda:
+            raise ValueError("slice-read sink: one device int32 word expected")
+    _check(lib().zero_calib_slice_read(C.byref(src), _ptr(sink), _stream(stream)), "zero_calib_slice_read")

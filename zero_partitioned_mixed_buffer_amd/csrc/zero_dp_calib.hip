@@ -16,6 +16,11 @@
 //                      ahead, above).  The slices are combined with XOR
 //                      into the third output, so every load is used; the
 //                      other outputs are copies of the inputs.
+//   slice_read_kernel  the same launch shape, visit order and launch pieces
+//                      with the slice reads alone (2 * Nd bytes per owned
+//                      element, nothing stored but one word per workgroup):
+//                      the rate the step's slice streams attain without the
+//                      state streams and the stores beside them.
 //
 // Neither kernel is part of the step; the step's kernels live in
 // zero_dp_kernels.hip.
@@ -24,6 +29,7 @@
 #include <cstdint>
 
 #include "../../include/zero_dp.h"
+#include "zero_dp_calib.h"
 #include "zero_dp_internal.h"
 
 namespace {
@@ -186,11 +192,12 @@ __device__ __forceinline__ bool mix_pf_dispatch(const MixArgs& a, int64_t nfull)
 }
 
 template <int U, int R>
-__device__ __forceinline__ void mix_chunk_load(hvec (&w)[R][U], const int64_t (&j)[U], const MixArgs& a, int k0) {
+__device__ __forceinline__ void mix_chunk_load(hvec (&w)[R][U], const int64_t (&j)[U], const uint16_t* win,
+                                               int64_t stride, int k0) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int u = 0; u < U; ++u) w[r][u] = ldh(a.win + j[u] + static_cast<int64_t>(k0 + r) * a.stride);
+        for (int u = 0; u < U; ++u) w[r][u] = ldh(win + j[u] + static_cast<int64_t>(k0 + r) * stride);
 }
 
 template <int U, int R>
@@ -232,14 +239,14 @@ __device__ void mix_visits(const MixArgs& a, int64_t nfull) {
 #pragma unroll
         for (int u = 0; u < U; ++u) x[u] = 0;
         hvec wa[R][U], wb[R][U];
-        mix_chunk_load<U, R>(wa, j, a, 0);
+        mix_chunk_load<U, R>(wa, j, a.win, a.stride, 0);
         int c = 0;
         for (;;) {
-            if (c + 1 < nfc) mix_chunk_load<U, R>(wb, j, a, (c + 1) * R);
+            if (c + 1 < nfc) mix_chunk_load<U, R>(wb, j, a.win, a.stride, (c + 1) * R);
             __builtin_amdgcn_sched_barrier(0);
             mix_chunk_xor<U, R>(x, wa);
             if (++c >= nfc) break;
-            if (c + 1 < nfc) mix_chunk_load<U, R>(wa, j, a, (c + 1) * R);
+            if (c + 1 < nfc) mix_chunk_load<U, R>(wa, j, a.win, a.stride, (c + 1) * R);
             __builtin_amdgcn_sched_barrier(0);
             mix_chunk_xor<U, R>(x, wb);
             if (++c >= nfc) break;
@@ -270,6 +277,144 @@ __global__ void __launch_bounds__(kBlock) stream_mix_kernel(MixArgs a) {
     }
 }
 
+// ------------------------------------------------------------- slice read
+struct ReadArgs {
+    const uint16_t* win;  // slice 0 of the window (this launch's piece)
+    int64_t stride;       // elements between slices
+    int64_t n;
+    int32_t nd;
+    uint32_t* sink;
+};
+
+// Elements [e0, n) one at a time: the XOR of element e's slices goes to the
+// low half of the word for even e and to the high half for odd e (a piece
+// starts at an even element of the window, so the halves agree with the
+// 4-element groups' word pairs).
+__device__ uint32_t read_elems(const ReadArgs& a, int64_t e0) {
+    uint32_t x = 0;
+    for (int64_t e = e0; e < a.n; ++e) {
+        uint32_t y = 0;
+        for (int k = 0; k < a.nd; ++k) y ^= a.win[e + static_cast<int64_t>(k) * a.stride];
+        x ^= (e & 1) ? (y << 16) : y;
+    }
+    return x;
+}
+
+// Nd = R <= 16: one group per lane at a time in grid-stride order, the next
+// group's R loads issued before this group is folded (past the end a lane
+// loads group 0 and ignores it).
+template <int R>
+__device__ uint32_t read_pf(const ReadArgs& a, int64_t nfull) {
+    int64_t gi = logical_block() * kBlock + threadIdx.x;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock;
+    uint32_t x = 0;
+    if (gi >= nfull) return x;
+    hvec w[R];
+    auto load = [&](int64_t g) {
+#pragma unroll
+        for (int k = 0; k < R; ++k) w[k] = ldh(a.win + g * kV + static_cast<int64_t>(k) * a.stride);
+    };
+    load(gi);
+    for (;;) {
+        const int64_t gn = gi + step;
+        hvec wc[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k) wc[k] = w[k];
+        load(gn < nfull ? gn : 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < R; ++k) x ^= xor_words(wc[k]);
+        if (gn >= nfull) break;
+        gi = gn;
+    }
+    return x;
+}
+
+template <int R>
+__device__ __forceinline__ uint32_t read_pf_dispatch(const ReadArgs& a, int64_t nfull) {
+    if constexpr (R >= 1) {
+        if (a.nd == R) return read_pf<R>(a, nfull);
+        return read_pf_dispatch<R - 1>(a, nfull);
+    }
+    return 0;
+}
+
+// Nd > 16: the stream-mix kernel's visits (U consecutive 256-element groups
+// per wave visit, chunks of R slices, the next chunk ahead) with no state
+// loads and no stores.  Groups past the window load group 0 and are not
+// folded.
+template <int U, int R>
+__device__ uint32_t read_visits(const ReadArgs& a, int64_t nfull) {
+    const int64_t wave = logical_block() * kWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
+    const int64_t nvis = (nfull + 64 * U - 1) / (64 * U);
+    const int nfc = a.nd / R;
+    uint32_t x = 0;
+    for (int64_t vi = wave; vi < nvis; vi += nwaves) {
+        int64_t j[U];
+        bool act[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = (vi * U + u) * 64 + lane;
+            act[u] = g < nfull;
+            j[u] = (act[u] ? g : 0) * kV;
+        }
+        uint32_t xs[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) xs[u] = 0;
+        hvec wa[R][U], wb[R][U];
+        mix_chunk_load<U, R>(wa, j, a.win, a.stride, 0);
+        int c = 0;
+        for (;;) {
+            if (c + 1 < nfc) mix_chunk_load<U, R>(wb, j, a.win, a.stride, (c + 1) * R);
+            __builtin_amdgcn_sched_barrier(0);
+            mix_chunk_xor<U, R>(xs, wa);
+            if (++c >= nfc) break;
+            if (c + 1 < nfc) mix_chunk_load<U, R>(wa, j, a.win, a.stride, (c + 1) * R);
+            __builtin_amdgcn_sched_barrier(0);
+            mix_chunk_xor<U, R>(xs, wb);
+            if (++c >= nfc) break;
+        }
+        for (int k = nfc * R; k < a.nd; ++k)
+#pragma unroll
+            for (int u = 0; u < U; ++u) xs[u] ^= xor_words(ldh(a.win + j[u] + static_cast<int64_t>(k) * a.stride));
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (act[u]) x ^= xs[u];
+    }
+    // the ragged tail, by the lane that would hold group nfull
+    if (a.n > nfull * kV && (nfull / (64 * U)) % nwaves == wave && nfull % 64 == lane) x ^= read_elems(a, nfull * kV);
+    return x;
+}
+
+__global__ void __launch_bounds__(kBlock) slice_read_kernel(ReadArgs a) {
+    const int64_t nfull = a.n / kV;
+    uint32_t x;
+    if (a.nd <= 16) {
+        x = read_pf_dispatch<16>(a, nfull);
+        const int64_t gi = logical_block() * kBlock + threadIdx.x;
+        const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock;
+        if (a.n > nfull * kV && nfull >= gi && (nfull - gi) % step == 0) x ^= read_elems(a, nfull * kV);
+    } else if (a.nd >= 32) {
+        x = read_visits<8, 2>(a, nfull);
+    } else {
+        x = read_visits<4, 2>(a, nfull);
+    }
+    // one word per workgroup: the waves' XORs, then one atomic XOR
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), o));
+    __shared__ uint32_t part[kWaves];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) t ^= part[w];
+        atomicXor(a.sink, t);
+    }
+}
+
 // One workgroup per CU of the current device (a multiple of 8 on MI355X,
 // so the XCD-contiguous order applies).
 int cu_grid() {
@@ -280,6 +425,17 @@ int cu_grid() {
         return 256;
     }
     return cus;
+}
+
+// The fused step's launch pieces: about 2^22 elements from Nd = 256 up,
+// 2^23 from Nd = 32 and 2^24 below, when the window is longer than two of
+// them (multiples of 1024, so every piece starts at an even element), else
+// one launch.
+int64_t piece_len(int64_t n, int32_t nd) {
+    const int64_t e = nd >= 256 ? (int64_t{1} << 22) : nd >= 32 ? (int64_t{1} << 23) : (int64_t{1} << 24);
+    if (n <= 2 * e) return n;
+    const int64_t pieces = (n + e - 1) / e;
+    return ((n + pieces - 1) / pieces + 1023) / 1024 * 1024;
 }
 
 int finish() {
@@ -302,16 +458,8 @@ int launch_calib_triad(float* a, const float* b, const float* c, float q, int64_
 }
 
 int launch_calib_mix(const SrcArgs& src, const float* const* in, float* const* out, uint16_t* out16, void* stream) {
-    // the fused step's launch pieces: about 2^22 elements from Nd = 256 up,
-    // 2^23 from Nd = 32 and 2^24 below, when the window is longer than two
-    // of them (multiples of 1024), else one launch
     const int64_t n = src.n;
-    const int64_t e = src.nd >= 256 ? (int64_t{1} << 22) : src.nd >= 32 ? (int64_t{1} << 23) : (int64_t{1} << 24);
-    int64_t len = n;
-    if (n > 2 * e) {
-        const int64_t pieces = (n + e - 1) / e;
-        len = ((n + pieces - 1) / pieces + 1023) / 1024 * 1024;
-    }
+    const int64_t len = piece_len(n, src.nd);
     const int grid = cu_grid();
     const hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
@@ -329,6 +477,30 @@ int launch_calib_mix(const SrcArgs& src, const float* const* in, float* const* o
         }
         a.out16 = out16 + off;
         stream_mix_kernel<<<grid, kBlock, 0, s>>>(a);
+        const int rc = finish();
+        if (rc != ZERO_OK) return rc;
+        off += k;
+    } while (off < n);
+    return ZERO_OK;
+}
+
+
+int launch_calib_slice_read(const SrcArgs& src, uint32_t* sink, void* stream) {
+    const int64_t n = src.n;
+    const int64_t len = piece_len(n, src.nd);
+    const int grid = cu_grid();
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    int64_t off = 0;
+    do {
+        const int64_t k = n - off < len ? n - off : len;
+        ReadArgs a;
+        a.win = src.win + off;
+        a.stride = src.stride;
+        a.n = k;
+        a.nd = src.nd;
+        a.sink = sink;
+        slice_read_kernel<<<grid, kBlock, 0, s>>>(a);
         const int rc = finish();
         if (rc != ZERO_OK) return rc;
         off += k;

@@ -12,6 +12,7 @@
 #include <cstdint>
 
 #include "../../include/zero_dp.h"
+#include "zero_dp_calib.h"
 #include "zero_dp_internal.h"
 
 namespace {
@@ -456,6 +457,17 @@ int zero_calib_stream_mix(const zero_grad_src* src, const float* const* in, floa
         for (const Range& x : ins)
             if (overlap(r[i], x)) return ZERO_EALIAS;
     return zdp::launch_calib_mix(make_src(src), in, out, out16, stream);
+}
+
+int zero_calib_slice_read(const zero_grad_src* src, uint32_t* sink, void* stream) {
+    Range span{};
+    const int rc = check_src(src, &span);
+    if (rc != ZERO_OK) return rc;
+    if (sink == nullptr) return ZERO_EINVAL;
+    if (reinterpret_cast<uintptr_t>(sink) % 4 != 0) return ZERO_EALIGN;
+    if (src->n == 0) return ZERO_OK;
+    if (overlap(bytes_of(sink, 1, 4), span)) return ZERO_EALIAS;
+    return zdp::launch_calib_slice_read(make_src(src), sink, stream);
 }
 
 }  // extern "C"

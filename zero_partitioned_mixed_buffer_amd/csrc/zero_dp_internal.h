@@ -3,9 +3,9 @@
 //
 // The host translation unit zero_dp_calls.cpp validates every argument of
 // the asynchronous C entry points and fills the kernel argument structs
-// below; the device translation units (zero_dp_kernels.hip: the step;
-// zero_dp_calib.hip: bandwidth calibration) hold the kernels and the
-// launchers declared here, which choose grids and enqueue the launches.
+// below; the device translation unit zero_dp_kernels.hip holds the step's
+// kernels and the launchers declared here, which choose grids and enqueue
+// the launches.  The calibration launchers are in zero_dp_calib.h.
 #pragma once
 
 #include <cstdint>
@@ -116,11 +116,5 @@ int launch_emit(const float* master, uint16_t* ag, int64_t n, void* stream);
 // zero_adam_step_noalloc uses as its workspace (kWsBytes bytes), or
 // ZERO_ECAPACITY if a step on this device would need more workgroup slots.
 int scratch_workspace(void** ws);
-
-// Bandwidth calibration (zero_dp_calib.hip): STREAM's triad, and the fused
-// step's streams with no arithmetic in its launch shape.
-int launch_calib_triad(float* a, const float* b, const float* c, float q, int64_t n, void* stream);
-int launch_calib_mix(const SrcArgs& src, const float* const* in, float* const* out, uint16_t* out16,
-                     void* stream);
 
 }  // namespace zdp

@@ -4,6 +4,7 @@
 // undefined-behaviour sanitizers.  Every launch reports ZERO_EHIP with
 // hipErrorNoDevice (100), so a call that passes validation fails loudly;
 // nothing here computes anything.
+#include "zero_dp_calib.h"
 #include "zero_dp_internal.h"
 
 namespace {
@@ -40,5 +41,6 @@ int launch_emit(const float*, uint16_t*, int64_t, void*) { return no_device(); }
 int scratch_workspace(void**) { return no_device(); }
 int launch_calib_triad(float*, const float*, const float*, float, int64_t, void*) { return no_device(); }
 int launch_calib_mix(const SrcArgs&, const float* const*, float* const*, uint16_t*, void*) { return no_device(); }
+int launch_calib_slice_read(const SrcArgs&, uint32_t*, void*) { return no_device(); }
 
 }  // namespace zdp
