@@ -427,3 +427,35 @@ def test_largest_nd():
 
     sh, _, _ = _run_case(n, nd, 2, 83, L=65536.0, sigma=1e-4, mutate=mutate)
     assert sh.flags == [0, 0]
+
+
+@pytest.mark.parametrize("nd,n,dist", [(7, 70001, "normal"), (16, 100003, "normal"),
+                                       (48, 2**21 + 2053, "student_t3"), (400, 40961, "student_t3")])
+def test_exact_sum_invariants(nd, n, dist):
+    """Invariants of the exact Nd-way sum on the HIP path itself, beside the
+    oracle comparison: permuting the slices, or doubling every gradient
+    together with the loss scale (exact in fp16 here, and 1/L a power of
+    two), gives the same state, window, Sigma g^2 and step count bit for bit.
+    The prefetch paths, both visit shapes and Student-t tails are covered."""
+    L = 1024.0 if dist == "normal" else 2048.0
+    sigma = 1e-3 if dist == "normal" else 1e-4
+    g = np.random.default_rng(nd * 7 + 1)
+    master0 = (g.standard_normal(n) * 0.02).astype(F32)
+    runs = [GpuShardRun(master0, nd, HP) for _ in range(3)]
+    for step in range(1, 4):
+        sl = gen.host_grad_slices(nd + 40, step, 0, nd, n, 0, n, sigma, L, dist)
+        assert np.all(np.isfinite(sl.astype(np.float32) * 2)), "doubling must stay finite in fp16"
+        perm = g.permutation(nd)
+        outs = [runs[0].step(sl, L), runs[1].step(np.ascontiguousarray(sl[perm]), L),
+                runs[2].step((sl.astype(np.float32) * 2).astype(F16), 2 * L)]
+        ref_ctl, rp, rm, rv, rbits = outs[0]
+        assert ref_ctl["overflow"] == 0 and ref_ctl["t"] == step
+        for k, what in ((1, "permuted"), (2, "doubled")):
+            ctl, p, m, v, bits = outs[k]
+            tag = f"nd={nd} n={n} step={step} {what}"
+            assert ctl["t"] == ref_ctl["t"] and ctl["overflow"] == 0, tag
+            assert ctl["sumsq"] == ref_ctl["sumsq"], tag
+            for a, b, name in ((p, rp, "master"), (m, rm, "exp_avg"), (v, rv, "exp_avg_sq")):
+                assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{tag} {name}"
+            assert np.array_equal(runs[k].window(bits), runs[0].window(rbits)), f"{tag} window"
+            assert runs[k].guards_intact(bits), tag
