@@ -36,8 +36,21 @@ def _shard(torch, master0, hp, guard=64):
 
 
 def _buckets(n, b, seed):
-    bl = [(o, min(b, n - o)) for o in range(0, n, b)]
-    perm = np.random.default_rng(seed).permutation(len(bl))
+    """Buckets of b elements (the last one ragged), or for b = 0 irregular
+    ones: random multiples of 8 from 8 to 3000 elements, and the window's
+    last 3 elements alone (a bucket with no full 4-element group); in a
+    seeded arrival order."""
+    g = np.random.default_rng(seed)
+    if b > 0:
+        bl = [(o, min(b, n - o)) for o in range(0, n, b)]
+    else:
+        bl, o = [], 0
+        while o < n - 3:
+            k = min(int(g.integers(1, 376)) * 8, n - 3 - o)
+            bl.append((o, k))
+            o += k
+        bl.append((o, n - o))
+    perm = g.permutation(len(bl))
     return [bl[i] for i in perm]
 
 
@@ -47,6 +60,8 @@ def _buckets(n, b, seed):
     (300001, 20, 8192, 7),       # Nd > 16: the chunked sum, visits cut by bucket edges
     (600003, 48, 65536, 3),      # Nd >= 32: 8-group visits
     (30011, 1, 512, 59),         # Nd = 1, 59 buckets in one call
+    (300003, 8, 0, 16),          # irregular buckets, 16 runs per launch: a lane's step crosses several runs
+    (100003, 16, 0, 33),         # the same at Nd = 16, calls of 33 buckets (three launches each)
 ])
 def test_bucket_lists_match_single_buckets_and_oracle(n, nd, bucket, group):
     torch = torch_mod()
@@ -60,11 +75,13 @@ def test_bucket_lists_match_single_buckets_and_oracle(n, nd, bucket, group):
     recv_off = 8
     # one receive buffer per bucket (the arrivals queue up); columns past
     # each bucket's own width stay 7.0
-    recv = [torch.full((nd, recv_off + bucket + 16), 7.0, dtype=torch.float16, device="cuda") for _ in bl]
+    width = max(k for _, k in bl)
+    recv = [torch.full((nd, recv_off + width + 16), 7.0, dtype=torch.float16, device="cuda") for _ in bl]
     for step in range(1, 5):
         sl = gen.host_grad_slices(n + nd, step, 0, nd, n, 0, n, 1e-3, 1024.0)
         if step == 3:  # an inf in one bucket skips the whole step
-            sl[nd - 1, bl[len(bl) // 2][0] + 3] = np.inf
+            o_inf, k_inf = bl[len(bl) // 2]
+            sl[nd - 1, o_inf + min(3, k_inf - 1)] = np.inf
         ovf, sq = ref.step(sl, 1024.0)
         dsl = torch.from_numpy(sl).cuda()
         for r, (o, k) in zip(recv, bl):

@@ -1076,9 +1076,11 @@ __global__ void __launch_bounds__(kBlock) fused_step_kernel(SrcArgs src_in, Adam
 
 // Several runs of a bucketed step in one launch (the buckets that have
 // arrived): run i reads its slices from win[i] (rows stride[i] apart) and
-// steps window elements [off[i], off[i] + n[i]); every run is spread over
-// the whole grid, as a one-run launch is, and each workgroup's partial
-// accumulates over the runs before it reaches its slot.
+// steps window elements [off[i], off[i] + n[i]).  For Nd <= kUnroll the
+// full groups of all the runs form one grid-stride sequence (below); for
+// larger Nd every run is spread over the whole grid in turn, as a one-run
+// launch is.  Each workgroup's partial accumulates over the runs before it
+// reaches its slot.
 constexpr int kMaxRuns = 16;
 struct RunList {
     const uint16_t* win[kMaxRuns];
@@ -1088,6 +1090,103 @@ struct RunList {
     int32_t count;
 };
 
+// The runs of one launch as LDS tables, read when a lane's next group lies
+// in a later run: run i's slices, their row stride, its window offset, and
+// pre[i], the number of full groups of the runs before it (pre[count] = all
+// of them).
+struct RunTab {
+    const uint16_t* win[kMaxRuns];
+    int64_t stride[kMaxRuns];
+    int64_t off[kMaxRuns];
+    int64_t pre[kMaxRuns + 1];
+};
+
+// A lane's current run: its full groups are [pre, hi) of the sequence over
+// all the runs, its slices start at win (rows stride apart) and its first
+// element is window element off.  Registers only; the LDS table is read
+// when a lane's next group lies in a later run.
+struct RunCur {
+    int64_t pre, hi;
+    const uint16_t* win;
+    int64_t stride, off;
+    int r;
+};
+
+__device__ __forceinline__ void run_seek(const RunTab& t, RunCur& c, int64_t g) {
+    while (g >= c.hi) {
+        ++c.r;
+        c.pre = c.hi;
+        c.hi = t.pre[c.r + 1];
+        c.win = t.win[c.r];
+        c.stride = t.stride[c.r];
+        c.off = t.off[c.r];
+    }
+}
+
+// Loads group g of run c (g in [c.pre, c.hi)) and returns its window
+// element index.
+template <int R>
+__device__ __forceinline__ int64_t pfr_load(const RunCur& c, int64_t g, hvec (&w)[R], fvec& p, fvec& m, fvec& v,
+                                            const FusedPtrs& f) {
+    const int64_t jl = (g - c.pre) * kV;
+    const int64_t js = c.off + jl;
+    const uint16_t* sw = c.win + jl;
+    p = ldg(reinterpret_cast<const fvec*>(f.pin + js));
+    m = ldg(reinterpret_cast<const fvec*>(f.min_ + js));
+    v = ldg(reinterpret_cast<const fvec*>(f.vin + js));
+#pragma unroll
+    for (int u = 0; u < R; ++u) w[u] = ldh(sw + static_cast<int64_t>(u) * c.stride);
+    return js;
+}
+
+// The one-ahead prefetch loop of pf_run1 over the full groups of all the
+// runs at once: a lane's grid-stride sequence runs on from one run into
+// the next, so the pipeline fills and drains once per launch instead of
+// once per run.  A lane's groups ascend, so its run only advances.  Past
+// the end a lane loads the first full group of the launch (unused).
+template <int R>
+__device__ void pfr_run1(const RunTab& t, int64_t gi, int64_t end, int64_t step, const SrcArgs& src,
+                         const FusedPtrs& f, const AdamScalars& c, double& sq, int& bad) {
+    if (gi >= end) return;
+    RunCur z{0, t.pre[1], t.win[0], t.stride[0], t.off[0], 0};
+    run_seek(t, z, 0);  // the run that holds the first full group
+    RunCur cur = z;
+    run_seek(t, cur, gi);
+    hvec w[R];
+    fvec p, m, v;
+    int64_t js = pfr_load<R>(cur, gi, w, p, m, v, f);
+    for (;;) {
+        const int64_t gn = gi + step;
+        const bool more = gn < end;
+        if (more) run_seek(t, cur, gn);
+        hvec wc[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) wc[u] = w[u];
+        const fvec pc = p, mc = m, vc = v;
+        const int64_t jc = js;
+        const RunCur& at = more ? cur : z;
+        js = pfr_load<R>(at, more ? gn : z.pre, w, p, m, v, f);
+        __builtin_amdgcn_sched_barrier(0);  // keep the next group's loads ahead of this group's work
+        pf_finish<R>(wc, pc, mc, vc, src, f, c, jc, sq, bad);
+        if (!more) break;
+        gi = gn;
+    }
+}
+
+template <int R>
+__device__ __forceinline__ bool pfr_dispatch(int nd, const RunTab& t, int64_t gi, int64_t end, int64_t step,
+                                             const SrcArgs& src, const FusedPtrs& f, const AdamScalars& c,
+                                             double& sq, int& bad) {
+    if constexpr (R >= 1) {
+        if (nd == R) {
+            pfr_run1<R>(t, gi, end, step, src, f, c, sq, bad);
+            return true;
+        }
+        return pfr_dispatch<R - 1>(nd, t, gi, end, step, src, f, c, sq, bad);
+    }
+    return false;
+}
+
 __global__ void __launch_bounds__(kBlock) fused_runs_kernel(RunList rl, SrcArgs src_in, AdamArgs a, Partials ws) {
     const SrcArgs base = resolve_scale(src_in);
     const int cur = a.ctl->cur;
@@ -1096,17 +1195,55 @@ __global__ void __launch_bounds__(kBlock) fused_runs_kernel(RunList rl, SrcArgs 
     double sq = 0.0;
     int bad = 0;
     int64_t total = 0;
-    for (int i = 0; i < rl.count; ++i) {
-        SrcArgs s = base;
-        s.win = rl.win[i];
-        s.stride = rl.stride[i];
-        s.n = rl.n[i];
-        const int64_t o = rl.off[i];
-        const FusedPtrs f{a.p[cur] + o,     a.m[cur] + o,     a.v[cur] + o,
-                          a.p[cur ^ 1] + o, a.m[cur ^ 1] + o, a.v[cur ^ 1] + o,
-                          a.ag != nullptr ? a.ag + o : nullptr};
-        fused_run(s, f, c, sq, bad);
-        total += rl.n[i];
+    for (int i = 0; i < rl.count; ++i) total += rl.n[i];
+    if (base.nd <= kUnroll) {
+        // Nd within one chunk: one grid-stride sequence over every run's
+        // full groups, then each run's ragged tail by one lane
+        __shared__ RunTab t;
+        if (threadIdx.x < static_cast<unsigned>(rl.count)) {
+            const int i = static_cast<int>(threadIdx.x);
+            t.win[i] = rl.win[i];
+            t.stride[i] = rl.stride[i];
+            t.off[i] = rl.off[i];
+        }
+        if (threadIdx.x == 0) {
+            int64_t g = 0;
+            for (int i = 0; i < rl.count; ++i) {
+                t.pre[i] = g;
+                g += rl.n[i] / kV;
+            }
+            t.pre[rl.count] = g;
+        }
+        __syncthreads();
+        const FusedPtrs f{a.p[cur],     a.m[cur],     a.v[cur],
+                          a.p[cur ^ 1], a.m[cur ^ 1], a.v[cur ^ 1], a.ag};
+        GroupIter it(t.pre[rl.count]);
+        (void)pfr_dispatch<kUnroll>(base.nd, t, it.gi, it.end, it.step, base, f, c, sq, bad);
+        const int64_t tid = logical_block() * kBlock + threadIdx.x;
+        if (tid < rl.count && rl.n[tid] % kV != 0) {
+            const int i = static_cast<int>(tid);
+            SrcArgs s = base;
+            s.win = rl.win[i];
+            s.stride = rl.stride[i];
+            s.n = rl.n[i];
+            const int64_t o = rl.off[i];
+            const FusedPtrs fi{a.p[cur] + o,     a.m[cur] + o,     a.v[cur] + o,
+                               a.p[cur ^ 1] + o, a.m[cur ^ 1] + o, a.v[cur ^ 1] + o,
+                               a.ag != nullptr ? a.ag + o : nullptr};
+            fused_elems(s.n / kV * kV, s.n, s, fi, c, sq, bad);
+        }
+    } else {
+        for (int i = 0; i < rl.count; ++i) {
+            SrcArgs s = base;
+            s.win = rl.win[i];
+            s.stride = rl.stride[i];
+            s.n = rl.n[i];
+            const int64_t o = rl.off[i];
+            const FusedPtrs f{a.p[cur] + o,     a.m[cur] + o,     a.v[cur] + o,
+                              a.p[cur ^ 1] + o, a.m[cur ^ 1] + o, a.v[cur ^ 1] + o,
+                              a.ag != nullptr ? a.ag + o : nullptr};
+            fused_run(s, f, c, sq, bad);
+        }
     }
     const bool more = (a.bucket & ZERO_BUCKET_FIRST) == 0;
     publish_partial(ws, sq, bad, more);
