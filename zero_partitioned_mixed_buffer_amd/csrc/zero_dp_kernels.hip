@@ -1442,9 +1442,11 @@ constexpr int kCopyU = ZDP_COPY_U;  // 16-byte vectors per lane per iteration
 // iteration with all loads issued before the stores, each instruction
 // lane-contiguous, and each workgroup a contiguous chunk; the head and tail
 // go element-wise.  Otherwise every element moves on its own (2-byte
-// accesses, coalesced).
+// accesses, coalesced).  The chunks of a launch's pieces are dealt to the
+// workgroups in one rotation (rot: the workgroup next in turn), so no
+// workgroup takes the extra chunk of every piece.
 __device__ __forceinline__ void copy_piece(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
-                                           int64_t n) {
+                                           int64_t n, int64_t& rot) {
     const uintptr_t sa = reinterpret_cast<uintptr_t>(src), da = reinterpret_cast<uintptr_t>(dst);
     if (((sa ^ da) & 15u) != 0) {
         const int64_t nlanes = static_cast<int64_t>(gridDim.x) * kBlock;
@@ -1460,7 +1462,10 @@ __device__ __forceinline__ void copy_piece(const uint16_t* __restrict__ src, uin
     // (no predicates, so all kCopyU loads are in flight together)
     constexpr int64_t kChunk = static_cast<int64_t>(kCopyU) * kBlock;
     const int64_t nfull = nv / kChunk;
-    for (int64_t c = logical_block(); c < nfull; c += gridDim.x) {
+    const int64_t G = gridDim.x;
+    const int64_t lb = logical_block();
+    const int64_t first = ((lb - rot) % G + G) % G;
+    for (int64_t c = first; c < nfull; c += G) {
         const int64_t base = c * kChunk + threadIdx.x;
         u32x4 v[kCopyU];
 #pragma unroll
@@ -1468,12 +1473,13 @@ __device__ __forceinline__ void copy_piece(const uint16_t* __restrict__ src, uin
 #pragma unroll
         for (int u = 0; u < kCopyU; ++u) stg(dv + base + u * kBlock, v[u]);
     }
-    // the last partial chunk, the head and the tail: the last workgroup
-    if (blockIdx.x == gridDim.x - 1) {
+    // the last partial chunk, the head and the tail: the workgroup next in turn
+    if (lb == (rot + nfull) % G) {
         for (int64_t i = nfull * kChunk + threadIdx.x; i < nv; i += kBlock) stg(dv + i, ldg(sv + i));
         for (int64_t i = threadIdx.x; i < head; i += kBlock) dst[i] = src[i];
         for (int64_t i = head + nv * 8 + threadIdx.x; i < n; i += kBlock) dst[i] = src[i];
     }
+    rot = (rot + nfull + 1) % G;
 }
 
 // The pieces of one launch of a gather (a layer's parts of consecutive
@@ -1488,7 +1494,8 @@ struct CopyPieces {
 };
 
 __global__ void __launch_bounds__(kBlock) copy_f16_kernel(CopyPieces t) {
-    for (int i = 0; i < t.np; ++i) copy_piece(t.src[i], t.dst[i], t.len[i]);
+    int64_t rot = 0;
+    for (int i = 0; i < t.np; ++i) copy_piece(t.src[i], t.dst[i], t.len[i], rot);
 }
 
 // ---------------------------------------------------------------- launchers
