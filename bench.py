@@ -494,17 +494,23 @@ def measure_step(args, w, steps, warmup, graph=False, skip_timing=False):
         log(f"bucketed: {len(buckets)} buckets of {nb_elems} elements"
             + ("; arrival copies into 2 constant-size receive buffers on a side stream" if args.arrival else
                "; buckets read in place"))
+        # the gradient sources of every bucket and call, made once per
+        # gradient set outside the timed region (they do not change)
+        K = args.buckets_per_call
+        call_groups = [buckets[c:c + K] for c in range(0, len(buckets), K)]
+        bucket_srcs = [[B.grad_src(gs, S, o, k, w.nd, w.loss_scale) for o, k in buckets] for gs in gsets]
+        call_arrays = [[B.bucket_array([(B.grad_src(gs, S, o, k, w.nd, w.loss_scale), o) for o, k in group])
+                        for group in call_groups] for gs in gsets]
+        recv_srcs = [B.grad_src(r, nb_elems, 0, nb_elems, w.nd, w.loss_scale) for r in recv]
 
     def launch_bucketed(i, s):
         sh = shards[i % n_shards]
         gs = gsets[i % rot]
         if args.buckets_per_call > 1:
-            K = args.buckets_per_call
-            calls = [buckets[c:c + K] for c in range(0, len(buckets), K)]
-            for c, group in enumerate(calls):
-                phase = (B.BUCKET_FIRST if c == 0 else 0) | (B.BUCKET_LAST if c == len(calls) - 1 else 0)
-                B.adam_step_buckets([(B.grad_src(gs, S, o, k, w.nd, w.loss_scale), o) for o, k in group],
-                                    sh.state, sh.hp, S, ag, ag_offs[i % n_shards], phase, sh.workspace, s)
+            arrays = call_arrays[i % rot]
+            for c, arr in enumerate(arrays):
+                phase = (B.BUCKET_FIRST if c == 0 else 0) | (B.BUCKET_LAST if c == len(arrays) - 1 else 0)
+                B.adam_step_buckets(arr, sh.state, sh.hp, S, ag, ag_offs[i % n_shards], phase, sh.workspace, s)
             return
         for b, (o, k) in enumerate(buckets):
             phase = (B.BUCKET_FIRST if b == 0 else 0) | (B.BUCKET_LAST if b == len(buckets) - 1 else 0)
@@ -515,9 +521,11 @@ def measure_step(args, w, steps, warmup, graph=False, skip_timing=False):
                     recv[r][:, :k].copy_(gs[:, o:o + k])
                 arrived[r].record(side)
                 stream.wait_event(arrived[r])
-                src = B.grad_src(recv[r], nb_elems, 0, k, w.nd, w.loss_scale)
+                src = recv_srcs[r]
+                if k != nb_elems:
+                    src = B.grad_src(recv[r], nb_elems, 0, k, w.nd, w.loss_scale)
             else:
-                src = B.grad_src(gs, S, o, k, w.nd, w.loss_scale)
+                src = bucket_srcs[i % rot][b]
             B.adam_step_bucket(src, sh.state, sh.hp, o, S, ag, ag_offs[i % n_shards], phase, sh.workspace, s)
             if args.arrival:
                 consumed[r].record(stream)

@@ -366,15 +366,22 @@ def adam_step_bucket(src: GradSrc, state: AdamState, hp: AdamHp, win_off: int, w
                                        _stream(stream)), "zero_adam_step_bucket")
 
 
-def adam_step_buckets(buckets: Sequence[Tuple[GradSrc, int]], state: AdamState, hp: AdamHp, window_n: int,
+def bucket_array(buckets: Sequence[Tuple[GradSrc, int]]):
+    """The zero_bucket array of (gradient source, window offset) pairs, for
+    callers that pass the same buckets step after step."""
+    return (Bucket * max(len(buckets), 1))(*[Bucket(src, int(off)) for src, off in buckets]), len(buckets)
+
+
+def adam_step_buckets(buckets, state: AdamState, hp: AdamHp, window_n: int,
                       allgather, allgather_off: int, phase: int, workspace, stream=None):
     """Several arrived buckets of a bucketed step in one call: ``buckets``
-    lists (gradient source, window offset) pairs."""
+    lists (gradient source, window offset) pairs, or is what bucket_array
+    made of such a list."""
     _check_state(state, window_n)
     _check_span(allgather, allgather_off, window_n, _F16, "all-gather buffer")
     _check_ws(workspace)
-    arr = (Bucket * max(len(buckets), 1))(*[Bucket(src, int(off)) for src, off in buckets])
-    _check(lib().zero_adam_step_buckets(arr, len(buckets), C.byref(state), C.byref(hp), int(window_n),
+    arr, nb = buckets if isinstance(buckets, tuple) else bucket_array(buckets)
+    _check(lib().zero_adam_step_buckets(arr, nb, C.byref(state), C.byref(hp), int(window_n),
                                         _ptr(allgather), int(allgather_off), int(phase), _ptr(workspace),
                                         _stream(stream)), "zero_adam_step_buckets")
 
