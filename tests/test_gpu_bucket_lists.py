@@ -76,7 +76,9 @@ def test_bucket_lists_match_single_buckets_and_oracle(n, nd, bucket, group):
     # one receive buffer per bucket (the arrivals queue up); columns past
     # each bucket's own width stay 7.0
     width = max(k for _, k in bl)
-    recv = [torch.full((nd, recv_off + width + 16), 7.0, dtype=torch.float16, device="cuda") for _ in bl]
+    # receive buffers of four widths, so the buckets of one launch have different row strides
+    recv = [torch.full((nd, recv_off + width + 16 + 8 * (i % 4)), 7.0, dtype=torch.float16, device="cuda")
+            for i in range(len(bl))]
     for step in range(1, 5):
         sl = gen.host_grad_slices(n + nd, step, 0, nd, n, 0, n, 1e-3, 1024.0)
         if step == 3:  # an inf in one bucket skips the whole step
