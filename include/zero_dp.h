@@ -372,7 +372,8 @@ int zero_adam_step_bucket(const zero_grad_src* src, const zero_adam_state* st,
  * below Nd = 32; a bucket longer than two launch lengths is cut as a long
  * window is).  A bucket's fixed cost is then paid per launch rather than
  * per bucket: the launch, the ramp of its first loads and the drain of its
- * last stores.  Per element the results are those of the one-bucket calls
+ * last stores (for Nd <= 16 a launch walks the elements of all its buckets
+ * as one sequence, so its loads run ahead across bucket edges).  Per element the results are those of the one-bucket calls
  * bit for bit; the sum of g^2 differs only in its rounding order.  phase
  * applies to the call: ZERO_BUCKET_FIRST if its first bucket is the step's
  * first, ZERO_BUCKET_LAST to commit after its last bucket.  Calls and
