@@ -62,6 +62,7 @@ def _buckets(n, b, seed):
     (30011, 1, 512, 59),         # Nd = 1, 59 buckets in one call
     (300003, 8, 0, 16),          # irregular buckets, 16 runs per launch: a lane's step crosses several runs
     (100003, 16, 0, 33),         # the same at Nd = 16, calls of 33 buckets (three launches each)
+    (2**23 + 2**21 + 12347, 32, 2**20, 16),  # Nd = 32, launches of 8 and 3 buckets: 8-group visits across buckets
 ])
 def test_bucket_lists_match_single_buckets_and_oracle(n, nd, bucket, group):
     torch = torch_mod()

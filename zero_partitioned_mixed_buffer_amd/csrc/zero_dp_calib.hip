@@ -13,7 +13,8 @@
 //                      visit order (the next group's loads ahead for
 //                      Nd <= 16; visits of 4 or 8 consecutive 256-element
 //                      groups summed in chunks of 2 slices, one chunk
-//                      ahead, above).  The slices are combined with XOR
+//                      ahead, above; 8 from Nd = 32 when a launch holds at
+//                      least one such visit per wave).  The slices are combined with XOR
 //                      into the third output, so every load is used; the
 //                      other outputs are copies of the inputs.
 //   slice_read_kernel  the same launch shape, visit order and launch pieces
@@ -94,6 +95,12 @@ __global__ void __launch_bounds__(kBlock) triad_kernel(float* __restrict__ a, co
         }
         for (int64_t i = nv * 4 + threadIdx.x; i < n; i += kBlock) a[i] = b[i] + q * c[i];
     }
+}
+
+// The step's choice of visit shape: 8-group visits from Nd = 32 when the
+// launch holds at least one per wave, else 4-group visits.
+__device__ __forceinline__ bool big_visits(int nd, int64_t nfull) {
+    return nd >= 32 && (nfull + 64 * 8 - 1) / (64 * 8) >= static_cast<int64_t>(gridDim.x) * kWaves;
 }
 
 // ------------------------------------------------------------- stream mix
@@ -270,7 +277,7 @@ __global__ void __launch_bounds__(kBlock) stream_mix_kernel(MixArgs a) {
         const int64_t gi = logical_block() * kBlock + threadIdx.x;
         const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock;
         if (a.n > nfull * kV && nfull >= gi && (nfull - gi) % step == 0) mix_elems(a, nfull * kV);
-    } else if (a.nd >= 32) {
+    } else if (big_visits(a.nd, nfull)) {
         mix_visits<8, 2>(a, nfull);
     } else {
         mix_visits<4, 2>(a, nfull);
@@ -396,7 +403,7 @@ __global__ void __launch_bounds__(kBlock) slice_read_kernel(ReadArgs a) {
         const int64_t gi = logical_block() * kBlock + threadIdx.x;
         const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock;
         if (a.n > nfull * kV && nfull >= gi && (nfull - gi) % step == 0) x ^= read_elems(a, nfull * kV);
-    } else if (a.nd >= 32) {
+    } else if (big_visits(a.nd, nfull)) {
         x = read_visits<8, 2>(a, nfull);
     } else {
         x = read_visits<4, 2>(a, nfull);

@@ -398,6 +398,15 @@ __device__ void reduce_tail(int64_t j, const SrcArgs& src, float* grad_out, doub
 static_assert(ZDP_CHB_R >= 1 && ZDP_CHB_R <= ZDP_UNROLL && ZDP_CHS_R >= 1 && ZDP_CHS_R <= ZDP_UNROLL,
               "the chunked path runs only for Nd > ZDP_UNROLL");
 
+// The big visit shape needs at least one visit per wave: a launch with
+// fewer (a window or bucket of under 2^21 elements at U = 8) leaves waves
+// idle, so it takes the small shape, whose visits are half as long.
+__device__ __forceinline__ bool big_visits(int nd, int64_t nfull) {
+    return nd >= ZDP_CH_BIG_ND &&
+           (nfull + 64 * ZDP_CHB_U - 1) / (64 * ZDP_CHB_U) >= static_cast<int64_t>(gridDim.x) * kWaves;
+}
+
+
 // Chunked sum for Nd > kUnroll.  A wave visits U consecutive 256-element
 // sub-groups at a time (lane l holds elements 4l .. 4l+3 of each), so one
 // load instruction per slice and sub-group covers a contiguous 512 B, and a
@@ -630,7 +639,7 @@ __global__ void __launch_bounds__(kBlock) reduce_owned_kernel(SrcArgs src_in, fl
         }
     }
     if (!done) {
-        if (src.nd >= ZDP_CH_BIG_ND)
+        if (big_visits(src.nd, nfull))
             rch_run<ZDP_CHB_U, ZDP_CHB_R, ZDP_CHB_PIPE != 0, kNormOfStored>(nfull, src, grad_out, sq, bad);
         else
             rch_run<ZDP_CHS_U, ZDP_CHS_R, ZDP_CHS_PIPE != 0, kNormOfStored>(nfull, src, grad_out, sq, bad);
@@ -1032,7 +1041,7 @@ __device__ void ch_run(int64_t nfull, const SrcArgs& src, const FusedPtrs& f, co
 
 __device__ __forceinline__ void ch_dispatch(int64_t nfull, const SrcArgs& src, const FusedPtrs& f,
                                             const AdamScalars& c, double& sq, int& bad) {
-    if (src.nd >= ZDP_CH_BIG_ND)
+    if (big_visits(src.nd, nfull))
         ch_run<ZDP_CHB_U, ZDP_CHB_R, ZDP_CHB_PIPE != 0, ZDP_CHB_XP>(nfull, src, f, c, sq, bad);
     else
         ch_run<ZDP_CHS_U, ZDP_CHS_R, ZDP_CHS_PIPE != 0, ZDP_CHS_XP>(nfull, src, f, c, sq, bad);
@@ -1077,9 +1086,9 @@ __global__ void __launch_bounds__(kBlock) fused_step_kernel(SrcArgs src_in, Adam
 // Several runs of a bucketed step in one launch (the buckets that have
 // arrived): run i reads its slices from win[i] (rows stride[i] apart) and
 // steps window elements [off[i], off[i] + n[i]).  For Nd <= kUnroll the
-// full groups of all the runs form one grid-stride sequence (below); for
-// larger Nd every run is spread over the whole grid in turn, as a one-run
-// launch is.  Each workgroup's partial accumulates over the runs before it
+// full groups of all the runs form one grid-stride sequence; for larger Nd
+// the visits of all the runs do (below).  Each run's ragged tail is done by
+// one lane.  Each workgroup's partial accumulates over the runs before it
 // reaches its slot.
 constexpr int kMaxRuns = 16;
 struct RunList {
@@ -1173,6 +1182,47 @@ __device__ void pfr_run1(const RunTab& t, int64_t gi, int64_t end, int64_t step,
     }
 }
 
+// The chunked sum over the visits of all the runs as one sequence: run r's
+// full groups form ceil(nfull_r / (64 U)) visits, each within that run, and
+// wave w takes visits w, w + W, ... of the sequence (as ch_loop does for
+// one window), so short runs do not leave waves idle.  The wave index is
+// made wave-uniform, so the run index and each run's pointers stay in
+// scalar registers.
+template <int U, int R, bool PIPE>
+__device__ void chr_loop(const RunList& rl, const SrcArgs& base, const AdamArgs& a, int cur, const AdamScalars& c,
+                         double& sq, int& bad) {
+    const int64_t wave = __builtin_amdgcn_readfirstlane(static_cast<int>(logical_block() * kWaves + (threadIdx.x >> 6)));
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
+    constexpr int64_t kVis = 64 * U;
+    int r = 0;
+    int64_t vbeg = 0, vend = (rl.n[0] / kV + kVis - 1) / kVis;
+    for (int64_t vi = wave;; vi += nwaves) {
+        while (vi >= vend && r + 1 < rl.count) {
+            ++r;
+            vbeg = vend;
+            vend += (rl.n[r] / kV + kVis - 1) / kVis;
+        }
+        if (vi >= vend) break;
+        SrcArgs s = base;
+        s.win = rl.win[r];
+        s.stride = rl.stride[r];
+        s.n = rl.n[r];
+        const int64_t o = rl.off[r];
+        const FusedPtrs f{a.p[cur] + o,     a.m[cur] + o,     a.v[cur] + o,
+                          a.p[cur ^ 1] + o, a.m[cur ^ 1] + o, a.v[cur ^ 1] + o,
+                          a.ag != nullptr ? a.ag + o : nullptr};
+        int64_t j[U];
+        bool act[U];
+        visit_index<U>(vi - vbeg, s.n / kV, lane, j, act);
+        fvec pv[U], mv[U], vv[U];
+        visit_state<U>(pv, mv, vv, f, j);
+        double acc[U][kV];
+        chu_sum<U, R, PIPE>(acc, j, s.win, s.stride, s.nd);
+        visit_finish<U>(acc, pv, mv, vv, j, act, s, f, c, sq, bad);
+    }
+}
+
 template <int R>
 __device__ __forceinline__ bool pfr_dispatch(int nd, const RunTab& t, int64_t gi, int64_t end, int64_t step,
                                              const SrcArgs& src, const FusedPtrs& f, const AdamScalars& c,
@@ -1219,31 +1269,27 @@ __global__ void __launch_bounds__(kBlock) fused_runs_kernel(RunList rl, SrcArgs 
                           a.p[cur ^ 1], a.m[cur ^ 1], a.v[cur ^ 1], a.ag};
         GroupIter it(t.pre[rl.count]);
         (void)pfr_dispatch<kUnroll>(base.nd, t, it.gi, it.end, it.step, base, f, c, sq, bad);
-        const int64_t tid = logical_block() * kBlock + threadIdx.x;
-        if (tid < rl.count && rl.n[tid] % kV != 0) {
-            const int i = static_cast<int>(tid);
-            SrcArgs s = base;
-            s.win = rl.win[i];
-            s.stride = rl.stride[i];
-            s.n = rl.n[i];
-            const int64_t o = rl.off[i];
-            const FusedPtrs fi{a.p[cur] + o,     a.m[cur] + o,     a.v[cur] + o,
-                               a.p[cur ^ 1] + o, a.m[cur ^ 1] + o, a.v[cur ^ 1] + o,
-                               a.ag != nullptr ? a.ag + o : nullptr};
-            fused_elems(s.n / kV * kV, s.n, s, fi, c, sq, bad);
-        }
     } else {
-        for (int i = 0; i < rl.count; ++i) {
-            SrcArgs s = base;
-            s.win = rl.win[i];
-            s.stride = rl.stride[i];
-            s.n = rl.n[i];
-            const int64_t o = rl.off[i];
-            const FusedPtrs f{a.p[cur] + o,     a.m[cur] + o,     a.v[cur] + o,
-                              a.p[cur ^ 1] + o, a.m[cur ^ 1] + o, a.v[cur ^ 1] + o,
-                              a.ag != nullptr ? a.ag + o : nullptr};
-            fused_run(s, f, c, sq, bad);
-        }
+        int64_t nfull = 0;
+        for (int i = 0; i < rl.count; ++i) nfull += rl.n[i] / kV;
+        if (big_visits(base.nd, nfull))
+            chr_loop<ZDP_CHB_U, ZDP_CHB_R, ZDP_CHB_PIPE != 0>(rl, base, a, cur, c, sq, bad);
+        else
+            chr_loop<ZDP_CHS_U, ZDP_CHS_R, ZDP_CHS_PIPE != 0>(rl, base, a, cur, c, sq, bad);
+    }
+    // each run's ragged tail, by one lane
+    const int64_t tid = logical_block() * kBlock + threadIdx.x;
+    if (tid < rl.count && rl.n[tid] % kV != 0) {
+        const int i = static_cast<int>(tid);
+        SrcArgs s = base;
+        s.win = rl.win[i];
+        s.stride = rl.stride[i];
+        s.n = rl.n[i];
+        const int64_t o = rl.off[i];
+        const FusedPtrs fi{a.p[cur] + o,     a.m[cur] + o,     a.v[cur] + o,
+                           a.p[cur ^ 1] + o, a.m[cur ^ 1] + o, a.v[cur ^ 1] + o,
+                           a.ag != nullptr ? a.ag + o : nullptr};
+        fused_elems(s.n / kV * kV, s.n, s, fi, c, sq, bad);
     }
     const bool more = (a.bucket & ZERO_BUCKET_FIRST) == 0;
     publish_partial(ws, sq, bad, more);
