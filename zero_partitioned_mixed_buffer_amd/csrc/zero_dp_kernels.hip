@@ -1182,6 +1182,51 @@ __device__ void pfr_run1(const RunTab& t, int64_t gi, int64_t end, int64_t step,
     }
 }
 
+// The same, two groups ahead (pf_run2's rotation of NB register sets) for
+// 7 <= Nd <= 9: the run cursor follows the loads, two groups ahead of the
+// group being finished, and each register set keeps its group's window
+// element index.
+template <int R, int NB>
+__device__ void pfr_run2(const RunTab& t, int64_t gi, int64_t end, int64_t step, const SrcArgs& src,
+                         const FusedPtrs& f, const AdamScalars& c, double& sq, int& bad) {
+    if (gi >= end) return;
+    RunCur z{0, t.pre[1], t.win[0], t.stride[0], t.off[0], 0};
+    run_seek(t, z, 0);  // the run that holds the first full group
+    RunCur cur = z;
+    run_seek(t, cur, gi);
+    hvec w[NB][R];
+    fvec p[NB], m[NB], v[NB];
+    int64_t js[NB];
+    js[0] = pfr_load<R>(cur, gi, w[0], p[0], m[0], v[0], f);
+    {
+        const int64_t g1 = gi + step;
+        const bool in = g1 < end;
+        if (in) run_seek(t, cur, g1);
+        const RunCur& at = in ? cur : z;
+        js[1] = pfr_load<R>(at, in ? g1 : z.pre, w[1], p[1], m[1], v[1], f);
+    }
+    bool more = true;
+    while (more) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            if (more) {
+                const int ld = (k + 2) % NB;
+                const int64_t g2 = gi + 2 * step;
+                const bool in = g2 < end;
+                if (in) run_seek(t, cur, g2);
+                const RunCur& at = in ? cur : z;
+                js[ld] = pfr_load<R>(at, in ? g2 : z.pre, w[ld], p[ld], m[ld], v[ld], f);
+                __builtin_amdgcn_sched_barrier(0);
+                pf_finish<R>(w[k], p[k], m[k], v[k], src, f, c, js[k], sq, bad);
+                if (gi + step >= end)
+                    more = false;
+                else
+                    gi += step;
+            }
+        }
+    }
+}
+
 // The chunked sum over the visits of all the runs as one sequence: run r's
 // full groups form ceil(nfull_r / (64 U)) visits, each within that run, and
 // wave w takes visits w, w + W, ... of the sequence (as ch_loop does for
@@ -1229,7 +1274,10 @@ __device__ __forceinline__ bool pfr_dispatch(int nd, const RunTab& t, int64_t gi
                                              double& sq, int& bad) {
     if constexpr (R >= 1) {
         if (nd == R) {
-            pfr_run1<R>(t, gi, end, step, src, f, c, sq, bad);
+            if constexpr (ZDP_PF_NB >= 3 && R >= ZDP_PF2_MINR && R <= ZDP_PF2_MAXR)
+                pfr_run2<R, ZDP_PF_NB>(t, gi, end, step, src, f, c, sq, bad);
+            else
+                pfr_run1<R>(t, gi, end, step, src, f, c, sq, bad);
             return true;
         }
         return pfr_dispatch<R - 1>(nd, t, gi, end, step, src, f, c, sq, bad);
