@@ -169,6 +169,49 @@ def test_bucket_list_long_bucket_and_missing_bucket():
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+@pytest.mark.parametrize("nd", [24, 40])
+def test_bucket_list_big_and_tiny_runs(nd):
+    """Four buckets of 2^19 elements, a 3-element bucket (no full group, so
+    no visit) and 40 tiny ones of 8-3000 elements, in one call: the first
+    launch holds 16 runs, the big ones among them, and at Nd = 40 takes the
+    8-group visits (2^21 elements and more), at Nd = 24 the 4-group ones.
+    Bit-identical to the one-window step over two steps."""
+    torch = torch_mod()
+    from zero_partitioned_mixed_buffer_amd import binding as B
+    from zero_partitioned_mixed_buffer_amd import OwnedShard
+    big = 1 << 19
+    g = np.random.default_rng(nd)
+    tiny, o = [], 4 * big
+    while len(tiny) < 40:
+        k = int(g.integers(1, 376)) * 8
+        tiny.append((o, k))
+        o += k
+    n = o + 3
+    buckets = [(i * big, big) for i in range(4)] + [(n - 3, 3)] + tiny
+    master = torch.from_numpy((g.standard_normal(n) * 0.02).astype(F32)).cuda()
+    a = OwnedShard(master, **HP)
+    b = OwnedShard(master, **HP)
+    aga = torch.zeros(n, dtype=torch.float16, device="cuda")
+    agb = torch.zeros(n, dtype=torch.float16, device="cuda")
+    a.emit(aga)
+    b.emit(agb)
+    stride = (n + 7) // 8 * 8
+    dsl = torch.empty((nd, stride), dtype=torch.float16, device="cuda")
+    for step in (1, 2):
+        gen.device_fill_grads(dsl, 40 + nd, step, 1e-3, 1024.0, "normal", n)
+        a.step(dsl, 1024.0, allgather=aga)
+        items = [(B.grad_src(dsl, stride, o, k, nd, 1024.0), o) for o, k in buckets]
+        B.adam_step_buckets(items, b.state, b.hp, n, agb, 0, B.BUCKET_FIRST | B.BUCKET_LAST, b.workspace)
+        torch.cuda.synchronize()
+        ca, cb = a.control(), b.control()
+        tag = f"nd={nd} step={step}"
+        assert ca["t"] == cb["t"] == step and ca["overflow"] == cb["overflow"] == 0, tag
+        for x, y in zip(a.committed(ca), b.committed(cb)):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), tag
+        assert torch.equal(aga.view(torch.int16), agb.view(torch.int16)), tag
+        assert cb["sumsq"] == pytest.approx(ca["sumsq"], rel=1e-12), tag
+
+
 @pytest.mark.parametrize("nd,part,nranges,seed", [(4, 1000, 7, 1), (16, 4096, 40, 2), (3, 64, 30, 3)])
 def test_gather_layers_matches_oracle(nd, part, nranges, seed):
     torch = torch_mod()
