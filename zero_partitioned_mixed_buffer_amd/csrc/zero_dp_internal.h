@@ -23,6 +23,31 @@ constexpr int kWaves = kBlock / 64;
 // Upper bound on workgroups of the reducing kernels (one partial each).
 constexpr int kMaxBlocks = 8192;
 
+// Launch pieces of a long window.  A piece is a whole number of rounds of
+// its grid (round: q elements, one element group per lane or one visit per
+// wave), about `target` elements long, so every lane or wave has the same
+// number of groups or visits in every piece but the last; a remainder of
+// under half a piece joins the last piece, so a window ends in at most one
+// partial round.  Pieces of equal length would end every launch in a
+// partial round, in which most waves idle.
+inline int64_t piece_length(int64_t target, int64_t q) {
+    const int64_t rounds = (target + q / 2) / q;
+    return (rounds > 0 ? rounds : 1) * q;
+}
+
+// The end of the piece of a window of n elements that starts at off.
+inline int64_t piece_end(int64_t n, int64_t len, int64_t off) {
+    const int64_t rest = n - off;
+    return rest < len + len / 2 ? n : off + len;
+}
+
+// Elements in one round of a grid of `grid` workgroups: a 4-element group
+// per lane (Nd within one chunk), or a visit of `visit_groups` 256-element
+// groups per wave.
+inline int64_t round_elems(int64_t grid, bool visits, int visit_groups) {
+    return visits ? grid * kWaves * 64 * 4 * visit_groups : grid * kBlock * 4;
+}
+
 // Workspace layout (bytes): completion counter, the elements a bucketed
 // step's buckets have covered, then one slot per workgroup of partial sums
 // of g^2 (double) and overflow flags (int32).

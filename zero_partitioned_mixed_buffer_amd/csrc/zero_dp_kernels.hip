@@ -1704,23 +1704,26 @@ bool split_window(int64_t n, int32_t nd) {
     return e > 0 && n > 2 * e;
 }
 
+// The length of the launch pieces of a long window of Nd = nd on a grid of
+// `grid` workgroups: about split_elems(nd) elements, in whole rounds of the
+// grid (a multiple of 1024, so every piece starts 16-byte aligned).
+int64_t piece_len(int32_t nd, int64_t grid) {
+    const int u = nd >= ZDP_CH_BIG_ND ? ZDP_CHB_U : ZDP_CHS_U;
+    return zdp::piece_length(split_elems(nd), zdp::round_elems(grid, nd > kUnroll, u));
+}
+
 // Calls launch(off, k) for consecutive pieces [off, off + k) that cover
-// [0, n): one piece, or pieces of about split_elems(nd) elements (multiples
-// of 1024, so every piece starts 16-byte aligned) when split_window(n, nd).
+// [0, n): one piece, or pieces of piece_len(nd, grid) elements (the last
+// one longer by a remainder under half a piece) when split_window(n, nd).
 template <class Launch>
-int for_each_piece(int64_t n, int32_t nd, Launch&& launch) {
-    int64_t len = n;
-    if (split_window(n, nd)) {
-        const int64_t e = split_elems(nd);
-        const int64_t pieces = (n + e - 1) / e;
-        len = ((n + pieces - 1) / pieces + 1023) / 1024 * 1024;
-    }
+int for_each_piece(int64_t n, int32_t nd, int64_t grid, Launch&& launch) {
+    const int64_t len = split_window(n, nd) ? piece_len(nd, grid) : n;
     int64_t off = 0;
     do {
-        const int64_t k = n - off < len ? n - off : len;
-        const int rc = launch(off, k);
+        const int64_t end = zdp::piece_end(n, len, off);
+        const int rc = launch(off, end - off);
         if (rc != ZERO_OK) return rc;
-        off += k;
+        off = end;
     } while (off < n);
     return ZERO_OK;
 }
@@ -1749,7 +1752,7 @@ AdamArgs piece_args(const AdamArgs& a, int64_t off) {
 // `first` (the first launch of a step).  a.window_n must be set.
 int launch_fused_range(const SrcArgs& src, const AdamArgs& a, bool first, int grid, const Partials& ws,
                        hipStream_t s) {
-    return for_each_piece(src.n, src.nd, [&](int64_t off, int64_t k) {
+    return for_each_piece(src.n, src.nd, grid, [&](int64_t off, int64_t k) {
         AdamArgs b = piece_args(a, off);
         b.bucket = 4 | (first && off == 0 ? ZERO_BUCKET_FIRST : 0);
         fused_step_kernel<<<grid, kBlock, 0, s>>>(piece_src(src, off, k), b, ws);
@@ -1831,14 +1834,14 @@ int launch_step_clipped(const SrcArgs& whole, const AdamArgs& a, float* grad_buf
     // on one grid and accumulate in the workgroup slots
     const int grid1 = split_window(n, whole.nd) ? fixed_grid(kReduce) : grid_for(kReduce, n);
     (void)hipGetLastError();
-    int rc = for_each_piece(n, whole.nd, [&](int64_t off, int64_t k) {
+    int rc = for_each_piece(n, whole.nd, grid1, [&](int64_t off, int64_t k) {
         reduce_owned_kernel<true><<<grid1, kBlock, 0, s>>>(piece_src(whole, off, k), grad_buf + off, nullptr,
                                                             nullptr, ws, off != 0);
         return finish_launch();
     });
     if (rc != ZERO_OK) return rc;
     // the update pass streams g and the state alone: pieces as for small Nd
-    rc = for_each_piece(n, 1, [&](int64_t off, int64_t k) {
+    rc = for_each_piece(n, 1, fixed_grid(kClip), [&](int64_t off, int64_t k) {
         clipped_update_kernel<<<grid_for(kClip, k), kBlock, 0, s>>>(grad_buf + off, k, piece_args(a, off),
                                                                    max_norm, ws, grid1);
         return finish_launch();
@@ -1887,15 +1890,10 @@ int launch_buckets(const BucketRun* runs, int32_t nruns, const SrcArgs& common, 
     };
     for (int32_t i = 0; i < nruns; ++i) {
         const BucketRun& r = runs[i];
-        int64_t len = r.n;
-        if (split_window(r.n, common.nd)) {
-            const int64_t e = split_elems(common.nd);
-            const int64_t pieces = (r.n + e - 1) / e;
-            len = ((r.n + pieces - 1) / pieces + 1023) / 1024 * 1024;
-        }
+        const int64_t len = split_window(r.n, common.nd) ? piece_len(common.nd, grid) : r.n;
         int64_t off = 0;
         do {
-            const int64_t k = r.n - off < len ? r.n - off : len;
+            const int64_t k = zdp::piece_end(r.n, len, off) - off;
             if (rl.count == kMaxRuns || (rl.count > 0 && total + k > cap)) {
                 const int rc = flush();
                 if (rc != ZERO_OK) return rc;
