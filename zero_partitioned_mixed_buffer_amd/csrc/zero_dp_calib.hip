@@ -435,14 +435,13 @@ int cu_grid() {
 }
 
 // The fused step's launch pieces: about 2^22 elements from Nd = 256 up,
-// 2^23 from Nd = 32 and 2^24 below, in whole rounds of the grid, when the
-// window is longer than two of them (multiples of 1024, so every piece
-// starts at an even element; zdp::piece_end places the pieces), else one
-// launch.
-int64_t piece_len(int64_t n, int32_t nd, int grid) {
+// 2^23 from Nd = 32 and 2^24 below, placed as the step places them
+// (zdp::plan_pieces; multiples of 1024, so every piece starts at an even
+// element), when the window is longer than two of them, else one launch.
+zdp::Pieces pieces_for(int64_t n, int32_t nd, int grid) {
     const int64_t e = nd >= 256 ? (int64_t{1} << 22) : nd >= 32 ? (int64_t{1} << 23) : (int64_t{1} << 24);
-    if (n <= 2 * e) return n;
-    return zdp::piece_length(e, zdp::round_elems(grid, nd > 16, nd >= 32 ? 8 : 4));
+    if (n <= 2 * e) return zdp::Pieces{n, false};
+    return zdp::plan_pieces(n, e, zdp::round_elems(grid, nd > 16, nd >= 32 ? 8 : 4));
 }
 
 int finish() {
@@ -467,12 +466,12 @@ int launch_calib_triad(float* a, const float* b, const float* c, float q, int64_
 int launch_calib_mix(const SrcArgs& src, const float* const* in, float* const* out, uint16_t* out16, void* stream) {
     const int64_t n = src.n;
     const int grid = cu_grid();
-    const int64_t len = piece_len(n, src.nd, grid);
+    const zdp::Pieces pc = pieces_for(n, src.nd, grid);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     int64_t off = 0;
     do {
-        const int64_t k = zdp::piece_end(n, len, off) - off;
+        const int64_t k = zdp::piece_end(n, pc, off) - off;
         MixArgs a;
         a.win = src.win + off;
         a.stride = src.stride;
@@ -495,12 +494,12 @@ int launch_calib_mix(const SrcArgs& src, const float* const* in, float* const* o
 int launch_calib_slice_read(const SrcArgs& src, uint32_t* sink, void* stream) {
     const int64_t n = src.n;
     const int grid = cu_grid();
-    const int64_t len = piece_len(n, src.nd, grid);
+    const zdp::Pieces pc = pieces_for(n, src.nd, grid);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     int64_t off = 0;
     do {
-        const int64_t k = zdp::piece_end(n, len, off) - off;
+        const int64_t k = zdp::piece_end(n, pc, off) - off;
         ReadArgs a;
         a.win = src.win + off;
         a.stride = src.stride;

@@ -23,22 +23,46 @@ constexpr int kWaves = kBlock / 64;
 // Upper bound on workgroups of the reducing kernels (one partial each).
 constexpr int kMaxBlocks = 8192;
 
-// Launch pieces of a long window.  A piece is a whole number of rounds of
-// its grid (round: q elements, one element group per lane or one visit per
-// wave), about `target` elements long, so every lane or wave has the same
-// number of groups or visits in every piece but the last; a remainder of
-// under half a piece joins the last piece, so a window ends in at most one
-// partial round.  Pieces of equal length would end every launch in a
-// partial round, in which most waves idle.
-inline int64_t piece_length(int64_t target, int64_t q) {
-    const int64_t rounds = (target + q / 2) / q;
-    return (rounds > 0 ? rounds : 1) * q;
-}
+// Launch pieces of a long window: pieces of `len` elements (a multiple of
+// 1024, so every piece starts 16-byte aligned); with `merge`, a remainder
+// under half a piece joins the last piece, else it is a piece of its own.
+struct Pieces {
+    int64_t len;
+    bool merge;
+};
 
 // The end of the piece of a window of n elements that starts at off.
-inline int64_t piece_end(int64_t n, int64_t len, int64_t off) {
+inline int64_t piece_end(int64_t n, const Pieces& p, int64_t off) {
     const int64_t rest = n - off;
-    return rest < len + len / 2 ? n : off + len;
+    if (p.merge) return rest < p.len + p.len / 2 ? n : off + p.len;
+    return rest <= p.len ? n : off + p.len;
+}
+
+// Rounds of the grid the pieces take (round: q elements, one element group
+// per lane or one visit per wave; a piece ending in a partial round still
+// takes that whole round, most of its waves idle in it).
+inline int64_t piece_rounds(int64_t n, const Pieces& p, int64_t q) {
+    int64_t r = 0;
+    for (int64_t off = 0; off < n;) {
+        const int64_t e = piece_end(n, p, off);
+        r += (e - off + q - 1) / q;
+        off = e;
+    }
+    return r;
+}
+
+// Pieces of about `target` elements: equal ones, unless pieces of whole
+// rounds (the remainder joining the last piece, so only the window's last
+// launch ends in a partial round) take fewer rounds.  Equal pieces can end
+// every launch in a partial round: at 3.1 rounds each, 4 pieces take 16
+// rounds where whole-round pieces take 13.  Where both take as many rounds,
+// equal pieces measured as fast or faster.
+inline Pieces plan_pieces(int64_t n, int64_t target, int64_t q) {
+    const int64_t np = (n + target - 1) / target;
+    const Pieces eq{((n + np - 1) / np + 1023) / 1024 * 1024, false};
+    const int64_t rounds = (target + q / 2) / q;
+    const Pieces whole{(rounds > 0 ? rounds : 1) * q, true};
+    return piece_rounds(n, whole, q) < piece_rounds(n, eq, q) ? whole : eq;
 }
 
 // Elements in one round of a grid of `grid` workgroups: a 4-element group

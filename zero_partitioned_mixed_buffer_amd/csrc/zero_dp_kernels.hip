@@ -1704,23 +1704,23 @@ bool split_window(int64_t n, int32_t nd) {
     return e > 0 && n > 2 * e;
 }
 
-// The length of the launch pieces of a long window of Nd = nd on a grid of
-// `grid` workgroups: about split_elems(nd) elements, in whole rounds of the
-// grid (a multiple of 1024, so every piece starts 16-byte aligned).
-int64_t piece_len(int32_t nd, int64_t grid) {
+// The launch pieces of a window of n elements at Nd = nd on a grid of
+// `grid` workgroups: one piece, or pieces of about split_elems(nd) elements
+// when split_window(n, nd) (zdp::plan_pieces).
+zdp::Pieces pieces_for(int64_t n, int32_t nd, int64_t grid) {
+    if (!split_window(n, nd)) return zdp::Pieces{n, false};
     const int u = nd >= ZDP_CH_BIG_ND ? ZDP_CHB_U : ZDP_CHS_U;
-    return zdp::piece_length(split_elems(nd), zdp::round_elems(grid, nd > kUnroll, u));
+    return zdp::plan_pieces(n, split_elems(nd), zdp::round_elems(grid, nd > kUnroll, u));
 }
 
 // Calls launch(off, k) for consecutive pieces [off, off + k) that cover
-// [0, n): one piece, or pieces of piece_len(nd, grid) elements (the last
-// one longer by a remainder under half a piece) when split_window(n, nd).
+// [0, n), as pieces_for(n, nd, grid) places them.
 template <class Launch>
 int for_each_piece(int64_t n, int32_t nd, int64_t grid, Launch&& launch) {
-    const int64_t len = split_window(n, nd) ? piece_len(nd, grid) : n;
+    const zdp::Pieces pc = pieces_for(n, nd, grid);
     int64_t off = 0;
     do {
-        const int64_t end = zdp::piece_end(n, len, off);
+        const int64_t end = zdp::piece_end(n, pc, off);
         const int rc = launch(off, end - off);
         if (rc != ZERO_OK) return rc;
         off = end;
@@ -1890,10 +1890,10 @@ int launch_buckets(const BucketRun* runs, int32_t nruns, const SrcArgs& common, 
     };
     for (int32_t i = 0; i < nruns; ++i) {
         const BucketRun& r = runs[i];
-        const int64_t len = split_window(r.n, common.nd) ? piece_len(common.nd, grid) : r.n;
+        const zdp::Pieces pc = pieces_for(r.n, common.nd, grid);
         int64_t off = 0;
         do {
-            const int64_t k = zdp::piece_end(r.n, len, off) - off;
+            const int64_t k = zdp::piece_end(r.n, pc, off) - off;
             if (rl.count == kMaxRuns || (rl.count > 0 && total + k > cap)) {
                 const int rc = flush();
                 if (rc != ZERO_OK) return rc;
