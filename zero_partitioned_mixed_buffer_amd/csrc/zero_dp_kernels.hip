@@ -1023,6 +1023,38 @@ __device__ void ch_loop_xp(int64_t nfull, int64_t wave, int lane, int64_t nwaves
     }
 }
 
+// Full groups [g0, nfull) in visits of U groups, wave w taking visits w,
+// w + W, ... of that range (no loads across visits).  A group past nfull
+// is inactive and loads group g0.
+template <int U, int R, bool PIPE>
+__device__ void ch_loop_from(int64_t g0, int64_t nfull, int64_t wave, int lane, int64_t nwaves,
+                             const SrcArgs& src, const FusedPtrs& f, const AdamScalars& c, double& sq, int& bad) {
+    const int64_t ng = nfull - g0;
+    const int64_t nvis = (ng + 64 * U - 1) / (64 * U);
+    for (int64_t vi = wave; vi < nvis; vi += nwaves) {
+        int64_t j[U];
+        bool act[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = (vi * U + u) * 64 + lane;
+            act[u] = g < ng;
+            j[u] = (g0 + (act[u] ? g : 0)) * kV;
+        }
+        fvec pv[U], mv[U], vv[U];
+        visit_state<U>(pv, mv, vv, f, j);
+        double acc[U][kV];
+        chu_sum<U, R, PIPE>(acc, j, src.win, src.stride, src.nd);
+        visit_finish<U>(acc, pv, mv, vv, j, act, src, f, c, sq, bad);
+    }
+}
+
+#ifndef ZDP_TAIL_U
+#define ZDP_TAIL_U 2  // groups per visit of a launch's last partial round (0: no split)
+#endif
+#ifndef ZDP_TAIL_PCT
+#define ZDP_TAIL_PCT 60  // split the last round when it holds under this share of the waves' visits
+#endif
+
 // Full groups [0, nfull) and the ragged tail for Nd > kUnroll, in one shape.
 template <int U, int R, bool PIPE, int XP>
 __device__ void ch_run(int64_t nfull, const SrcArgs& src, const FusedPtrs& f, const AdamScalars& c,
@@ -1030,10 +1062,20 @@ __device__ void ch_run(int64_t nfull, const SrcArgs& src, const FusedPtrs& f, co
     const int64_t wave = logical_block() * kWaves + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
+    int64_t nmain = nfull;
+    if constexpr (ZDP_TAIL_U > 0 && ZDP_TAIL_U < U) {
+        const int64_t nvis = (nfull + 64 * U - 1) / (64 * U);
+        const int64_t full = nvis / nwaves * nwaves;  // visits of the full rounds
+        if (full > 0 && (nvis - full) * 100 < nwaves * ZDP_TAIL_PCT) nmain = full * 64 * U;
+    }
     if (XP != 0 && src.nd % R == 0)
-        ch_loop_xp<U, R, XP == 2>(nfull, wave, lane, nwaves, src, f, c, sq, bad);
+        ch_loop_xp<U, R, XP == 2>(nmain, wave, lane, nwaves, src, f, c, sq, bad);
     else
-        ch_loop<U, R, PIPE>(nfull, wave, lane, nwaves, src, f, c, sq, bad);
+        ch_loop<U, R, PIPE>(nmain, wave, lane, nwaves, src, f, c, sq, bad);
+    if constexpr (ZDP_TAIL_U > 0 && ZDP_TAIL_U < U) {
+        // the last partial round in visits of ZDP_TAIL_U groups, over every wave
+        if (nmain < nfull) ch_loop_from<ZDP_TAIL_U, R, PIPE>(nmain, nfull, wave, lane, nwaves, src, f, c, sq, bad);
+    }
     // the ragged tail group nfull, by the lane that would hold it
     if (src.n > nfull * kV && (nfull / (64 * U)) % nwaves == wave && nfull % 64 == lane)
         fused_elems(nfull * kV, src.n, src, f, c, sq, bad);
