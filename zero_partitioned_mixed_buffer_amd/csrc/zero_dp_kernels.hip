@@ -1048,14 +1048,17 @@ __device__ void ch_loop_from(int64_t g0, int64_t nfull, int64_t wave, int lane, 
     }
 }
 
-#ifndef ZDP_TAIL_U
-#define ZDP_TAIL_U 2  // groups per visit of a launch's last partial round (0: no split)
-#endif
-#ifndef ZDP_TAIL_PCT
-#define ZDP_TAIL_PCT 60  // split the last round when it holds under this share of the waves' visits
+#ifndef ZDP_TAIL_SPLIT
+#define ZDP_TAIL_SPLIT 1  // a launch's last partial round in smaller visits (0: as the others)
 #endif
 
 // Full groups [0, nfull) and the ragged tail for Nd > kUnroll, in one shape.
+// A launch whose visits end in a partial round, most waves idle in it,
+// takes that round in smaller visits over every wave: quarter visits when
+// it holds at most a quarter of the waves' visits, half visits when at
+// most half, so it fits one round of them.  (Measured at Nd = 400 on
+// single launches of 2.12-3.5 visits per wave: 0.70-0.77 of 8 TB/s
+// unsplit, 0.77-0.84 split; whole rounds run at 0.83-0.85.)
 template <int U, int R, bool PIPE, int XP>
 __device__ void ch_run(int64_t nfull, const SrcArgs& src, const FusedPtrs& f, const AdamScalars& c,
                        double& sq, int& bad) {
@@ -1063,18 +1066,30 @@ __device__ void ch_run(int64_t nfull, const SrcArgs& src, const FusedPtrs& f, co
     const int lane = threadIdx.x & 63;
     const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
     int64_t nmain = nfull;
-    if constexpr (ZDP_TAIL_U > 0 && ZDP_TAIL_U < U) {
+    int tail_u = 0;
+    if constexpr (ZDP_TAIL_SPLIT != 0 && U >= 4) {
         const int64_t nvis = (nfull + 64 * U - 1) / (64 * U);
         const int64_t full = nvis / nwaves * nwaves;  // visits of the full rounds
-        if (full > 0 && (nvis - full) * 100 < nwaves * ZDP_TAIL_PCT) nmain = full * 64 * U;
+        const int64_t t = nvis - full;
+        if (full > 0 && t > 0) {
+            if (U >= 8 && 4 * t <= nwaves)
+                tail_u = U / 4;
+            else if (2 * t <= nwaves)
+                tail_u = U / 2;
+            if (tail_u != 0) nmain = full * 64 * U;
+        }
     }
     if (XP != 0 && src.nd % R == 0)
         ch_loop_xp<U, R, XP == 2>(nmain, wave, lane, nwaves, src, f, c, sq, bad);
     else
         ch_loop<U, R, PIPE>(nmain, wave, lane, nwaves, src, f, c, sq, bad);
-    if constexpr (ZDP_TAIL_U > 0 && ZDP_TAIL_U < U) {
-        // the last partial round in visits of ZDP_TAIL_U groups, over every wave
-        if (nmain < nfull) ch_loop_from<ZDP_TAIL_U, R, PIPE>(nmain, nfull, wave, lane, nwaves, src, f, c, sq, bad);
+    if constexpr (ZDP_TAIL_SPLIT != 0 && U >= 4) {
+        if (tail_u == U / 2)
+            ch_loop_from<U / 2, R, PIPE>(nmain, nfull, wave, lane, nwaves, src, f, c, sq, bad);
+        if constexpr (U >= 8) {
+            if (tail_u == U / 4)
+                ch_loop_from<U / 4, R, PIPE>(nmain, nfull, wave, lane, nwaves, src, f, c, sq, bad);
+        }
     }
     // the ragged tail group nfull, by the lane that would hold it
     if (src.n > nfull * kV && (nfull / (64 * U)) % nwaves == wave && nfull % 64 == lane)
