@@ -46,7 +46,8 @@ def _mix_expected(sl, ins):
 
 @pytest.mark.parametrize("nd,n", [(1, 1003), (3, 4 * 65536 + 5), (8, 262147), (16, 100003), (17, 300001),
                                   (24, 1000007), (31, 65543), (32, 200003), (48, 1 << 18), (99, 50021),
-                                  (32, (1 << 24) + (1 << 22) + 5)])
+                                  (32, (1 << 24) + (1 << 22) + 5), (56, 1224 * 2048 - 145),
+                                  (40, 1424 * 2048 - 397), (20, 1324 * 1024 - 41)])
 def test_stream_mix_values(nd, n):
     torch = torch_mod()
     from zero_partitioned_mixed_buffer_amd import binding as B
@@ -74,7 +75,8 @@ def test_stream_mix_values(nd, n):
 
 @pytest.mark.parametrize("nd,n", [(1, 1003), (3, 4 * 65536 + 5), (8, 262147), (16, 100003), (17, 300001),
                                   (24, 1000007), (31, 65543), (32, 200003), (48, 1 << 18), (99, 50021),
-                                  (400, 40961), (32, (1 << 24) + (1 << 22) + 5), (260, (1 << 23) + (1 << 22) + 7)])
+                                  (400, 40961), (32, (1 << 24) + (1 << 22) + 5), (260, (1 << 23) + (1 << 22) + 7),
+                                  (56, 1224 * 2048 - 145), (40, 1424 * 2048 - 397), (20, 1324 * 1024 - 41)])
 def test_slice_read_values(nd, n):
     """The fold: bits 0-15 the XOR of every slice's fp16 bits at the
     window's even elements, bits 16-31 at its odd elements, XORed into the

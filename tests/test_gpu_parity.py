@@ -80,6 +80,19 @@ def test_fused_step_chunked_visits(nd, n):
     _run_case(n, nd, steps=2, seed=500 + nd)
 
 
+# Windows one full pass and a fraction of another long, in visits of the
+# launch's size: at most a quarter of a pass left (Nd >= 32 takes it in
+# quarter visits), at most half (half visits), more than half (no split),
+# for both visit sizes.
+TAIL_SPLIT_CASES = [(56, 1224 * 2048 - 145), (40, 1424 * 2048 - 397), (33, 1900 * 2048 - 29),
+                    (20, 1324 * 1024 - 41), (25, 1724 * 1024 - 17)]
+
+
+@pytest.mark.parametrize("nd,n", TAIL_SPLIT_CASES)
+def test_fused_step_partial_last_pass(nd, n):
+    _run_case(n, nd, steps=2, seed=700 + nd)
+
+
 @pytest.mark.parametrize("nd", [4, 8, 64])
 def test_fused_step_adamw_many_steps(nd):
     hp = dict(HP, weight_decay=0.01)

@@ -215,16 +215,35 @@ __device__ __forceinline__ void mix_chunk_xor(uint32_t (&x)[U], const hvec (&w)[
         for (int u = 0; u < U; ++u) x[u] ^= xor_words(w[r][u]);
 }
 
-// Nd > 16: wave w takes visits w, w + W, ... of U consecutive 256-element
-// groups (lane l holds elements 4l .. 4l+3 of each); a visit's slices come
-// in chunks of R, the next chunk's loads issued before this chunk is
-// folded.  Groups past the window load group 0 and store nothing.
+// The step's rule for a launch whose visits of U groups end in a partial
+// round: that round runs in quarter visits when it holds at most a quarter
+// of the waves' visits (U >= 8), in half visits when at most half.  Returns
+// the tail's visit size (0: no split) and sets nmain, the groups before it.
+__device__ __forceinline__ int tail_visit_groups(int64_t nfull, int u, int64_t nwaves, int64_t& nmain) {
+    nmain = nfull;
+    const int64_t nvis = (nfull + 64 * u - 1) / (64 * u);
+    const int64_t full = nvis / nwaves * nwaves;
+    const int64_t t = nvis - full;
+    if (full == 0 || t == 0) return 0;
+    int tu = 0;
+    if (u >= 8 && 4 * t <= nwaves)
+        tu = u / 4;
+    else if (2 * t <= nwaves)
+        tu = u / 2;
+    if (tu != 0) nmain = full * 64 * u;
+    return tu;
+}
+
+// Nd > 16: groups [g0, nfull), wave w taking visits w, w + W, ... of U
+// consecutive 256-element groups (lane l holds elements 4l .. 4l+3 of
+// each); a visit's slices come in chunks of R, the next chunk's loads
+// issued before this chunk is folded.  Groups past nfull load group g0
+// and store nothing.
 template <int U, int R>
-__device__ void mix_visits(const MixArgs& a, int64_t nfull) {
-    const int64_t wave = logical_block() * kWaves + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
-    const int64_t nvis = (nfull + 64 * U - 1) / (64 * U);
+__device__ void mix_visits_from(const MixArgs& a, int64_t g0, int64_t nfull, int64_t wave, int lane,
+                                int64_t nwaves) {
+    const int64_t ng = nfull - g0;
+    const int64_t nvis = (ng + 64 * U - 1) / (64 * U);
     const int nfc = a.nd / R;
     for (int64_t vi = wave; vi < nvis; vi += nwaves) {
         int64_t j[U];
@@ -232,8 +251,8 @@ __device__ void mix_visits(const MixArgs& a, int64_t nfull) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t g = (vi * U + u) * 64 + lane;
-            act[u] = g < nfull;
-            j[u] = (act[u] ? g : 0) * kV;
+            act[u] = g < ng;
+            j[u] = (g0 + (act[u] ? g : 0)) * kV;
         }
         fvec p[U], m[U], v[U];
 #pragma unroll
@@ -264,6 +283,20 @@ __device__ void mix_visits(const MixArgs& a, int64_t nfull) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (act[u]) mix_store(a, j[u], p[u], m[u], v[u], x[u]);
+    }
+}
+
+template <int U, int R>
+__device__ void mix_visits(const MixArgs& a, int64_t nfull) {
+    const int64_t wave = logical_block() * kWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
+    int64_t nmain;
+    const int tu = tail_visit_groups(nfull, U, nwaves, nmain);
+    mix_visits_from<U, R>(a, 0, nmain, wave, lane, nwaves);
+    if (tu == U / 2) mix_visits_from<U / 2, R>(a, nmain, nfull, wave, lane, nwaves);
+    if constexpr (U >= 8) {
+        if (tu == U / 4) mix_visits_from<U / 4, R>(a, nmain, nfull, wave, lane, nwaves);
     }
     // the ragged tail, by the lane that would hold group nfull
     if (a.n > nfull * kV && (nfull / (64 * U)) % nwaves == wave && nfull % 64 == lane) mix_elems(a, nfull * kV);
@@ -346,16 +379,15 @@ __device__ __forceinline__ uint32_t read_pf_dispatch(const ReadArgs& a, int64_t 
     return 0;
 }
 
-// Nd > 16: the stream-mix kernel's visits (U consecutive 256-element groups
-// per wave visit, chunks of R slices, the next chunk ahead) with no state
-// loads and no stores.  Groups past the window load group 0 and are not
-// folded.
+// Nd > 16: the stream-mix kernel's visits over groups [g0, nfull) (U
+// consecutive 256-element groups per wave visit, chunks of R slices, the
+// next chunk ahead) with no state loads and no stores.  Groups past nfull
+// load group g0 and are not folded.
 template <int U, int R>
-__device__ uint32_t read_visits(const ReadArgs& a, int64_t nfull) {
-    const int64_t wave = logical_block() * kWaves + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
-    const int64_t nvis = (nfull + 64 * U - 1) / (64 * U);
+__device__ uint32_t read_visits_from(const ReadArgs& a, int64_t g0, int64_t nfull, int64_t wave, int lane,
+                                     int64_t nwaves) {
+    const int64_t ng = nfull - g0;
+    const int64_t nvis = (ng + 64 * U - 1) / (64 * U);
     const int nfc = a.nd / R;
     uint32_t x = 0;
     for (int64_t vi = wave; vi < nvis; vi += nwaves) {
@@ -364,8 +396,8 @@ __device__ uint32_t read_visits(const ReadArgs& a, int64_t nfull) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t g = (vi * U + u) * 64 + lane;
-            act[u] = g < nfull;
-            j[u] = (act[u] ? g : 0) * kV;
+            act[u] = g < ng;
+            j[u] = (g0 + (act[u] ? g : 0)) * kV;
         }
         uint32_t xs[U];
 #pragma unroll
@@ -389,6 +421,21 @@ __device__ uint32_t read_visits(const ReadArgs& a, int64_t nfull) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (act[u]) x ^= xs[u];
+    }
+    return x;
+}
+
+template <int U, int R>
+__device__ uint32_t read_visits(const ReadArgs& a, int64_t nfull) {
+    const int64_t wave = logical_block() * kWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
+    int64_t nmain;
+    const int tu = tail_visit_groups(nfull, U, nwaves, nmain);
+    uint32_t x = read_visits_from<U, R>(a, 0, nmain, wave, lane, nwaves);
+    if (tu == U / 2) x ^= read_visits_from<U / 2, R>(a, nmain, nfull, wave, lane, nwaves);
+    if constexpr (U >= 8) {
+        if (tu == U / 4) x ^= read_visits_from<U / 4, R>(a, nmain, nfull, wave, lane, nwaves);
     }
     // the ragged tail, by the lane that would hold group nfull
     if (a.n > nfull * kV && (nfull / (64 * U)) % nwaves == wave && nfull % 64 == lane) x ^= read_elems(a, nfull * kV);
