@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--layers-per-call", type=int, default=1,
                     help="with --gather-layers: gather this many consecutive layers per zero_gather_layers "
                          "call (one layer buffer each)")
+    ap.add_argument("--sweep-nd", action="store_true",
+                    help="time the fused step, its stream-mix and its slice reads on one window per Nd "
+                         "(1 to 400, about 4 GB of algorithmic traffic per step) instead of a workload")
     ap.add_argument("--gather-streams", type=int, default=1, choices=(1, 2, 3, 4),
                     help="with --gather-layers: N > 1 rotates the layers over N streams (layer buffer "
                          "k %% N on stream k %% N), so one layer's gather overlaps the next ones' launches")
@@ -377,6 +380,78 @@ def bench_gather(args):
                      "kernel": "copy_f16_kernel" + (f" ({K} layers per zero_gather_layers call)" if K > 1 else ""),
                      "kernel_fingerprint": kernel_fingerprint()},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+SWEEP_ND = (1, 2, 4, 8, 12, 16, 20, 24, 32, 48, 64, 100, 200, 400)
+
+
+def bench_sweep_nd(args):
+    """The fused step across Nd: for each Nd one window of about 4 GB of
+    algorithmic traffic per step ((2 Nd + 26) bytes per element, Adam), two
+    shards stepped in turn, then the same window's stream-mix and
+    slice-read kernels, each timed with HIP events on the launch stream."""
+    import torch
+    from workloads import gen
+    from zero_partitioned_mixed_buffer_amd import OwnedShard, binding as B
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+
+    def timed(fn):
+        for i in range(max(args.warmup, 1)):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    rows = []
+    log("nd window step_us GB/s frac stream_mix_GB/s step/mix slice_read_GB/s read_share")
+    for nd in SWEEP_ND:
+        n = int(4e9 / (2 * nd + 26)) // 1024 * 1024
+        sl = torch.empty((nd, n), dtype=torch.float16, device=dev)
+        gen.device_fill_grads(sl, 7, 1, 1e-3, 1024.0, "normal", n)
+        shards = [OwnedShard(torch.randn(n, device=dev) * 0.02, **hp) for _ in range(2)]
+        ag = torch.zeros(n, dtype=torch.float16, device=dev)
+        src = B.grad_src(sl, n, 0, n, nd, 1024.0)
+
+        def step(i):
+            sh = shards[i % 2]
+            B.adam_step(src, sh.state, sh.hp, ag, 0, sh.workspace, stream)
+
+        t = timed(step)
+        sh = shards[0]
+        cur = sh.control()["cur"]
+        ins = [sh.master[cur], sh.exp_avg[cur], sh.exp_avg_sq[cur]]
+        outs = [sh.master[cur ^ 1], sh.exp_avg[cur ^ 1], sh.exp_avg_sq[cur ^ 1]]
+        tm = timed(lambda i: B.calib_stream_mix(src, ins, outs, ag, stream))
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        tr = timed(lambda i: B.calib_slice_read(src, sink, stream))
+        by = (2 * nd + 26) * n
+        row = {"nd": nd, "window": n, "step_us": t, "gbs": by / t / 1e3, "frac": by / t / 1e3 / PEAK_HBM_GBS,
+               "stream_mix_gbs": by / tm / 1e3, "step_over_mix": tm / t,
+               "slice_read_gbs": 2 * nd * n / tr / 1e3, "slice_read_share": tr / t}
+        rows.append(row)
+        log(f"{nd} {n} {t:.1f} {row['gbs']:.0f} {row['frac']:.3f} {row['stream_mix_gbs']:.0f} "
+            f"{row['step_over_mix']:.3f} {row['slice_read_gbs']:.0f} {row['slice_read_share']:.3f}")
+        del sl, shards, ag, src, ins, outs, sh
+        torch.cuda.empty_cache()
+    lo = min(rows, key=lambda r: r["frac"])
+    out = {
+        "metric": "fused step HBM rate across Nd, lowest fraction of 8 TB/s",
+        "value": lo["frac"], "unit": "fraction of 8 TB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": lo["step_us"] / 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": "one window per Nd at about 4 GB of algorithmic traffic per step", "rows": rows},
+        "kernel_fingerprint": kernel_fingerprint(),
     }
     print(json.dumps(out), flush=True)
 
@@ -722,6 +797,9 @@ def main():
         sys.exit(2)
     if args.gather_layers:
         bench_gather(args)
+        return
+    if args.sweep_nd:
+        bench_sweep_nd(args)
         return
 
     from workloads import configs
