@@ -910,18 +910,23 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
-            # measured HBM bytes per launch (rocprofv3 counters, committed summary)
-            # over the same average duration, in GB/s like `achieved`
+            # measured HBM bytes per step (rocprofv3 counters, committed summary)
+            # over the same average step duration, in GB/s like `achieved`
             "traffic": None if traffic is None else traffic / (kern_avg * 1e-3) / 1e9,
-            "traffic_bytes_per_launch": traffic,
-            "algorithmic_bytes_per_launch": bytes_elem * S,
+            "timed_unit": ("one step call, timed with HIP events on its stream: every launch of the kernel "
+                           "below over the window (a window longer than two launch lengths takes several "
+                           "fused launches), then the commit launch; a rocprofv3 summary gives the fused "
+                           "kernel per launch, and the launches times their average plus the commit's "
+                           "make this step"),
+            "traffic_bytes_per_step": traffic,
+            "algorithmic_bytes_per_step": bytes_elem * S,
             "kernel": ("reduce_owned_kernel + clipped_update_kernel + commit_kernel" if clipped else
                        (f"fused_runs_kernel, {res['n_buckets']} buckets in calls of {args.buckets_per_call}"
                         " + commit_kernel" if args.buckets_per_call > 1 else
                         f"fused_step_kernel x {res['n_buckets']} buckets + commit_kernel") if bucketed else
                        "fused_step_kernel + commit_kernel"),
-            "kernel_avg_us": kern_avg * 1e3,
-            "kernel_us_p10_p50_p90_per_launch_events": res["pcts_us"],
+            "step_avg_us": kern_avg * 1e3,
+            "step_us_p10_p50_p90_events": res["pcts_us"],
             "attainable": attain,
             "frac_of_attainable": achieved / attain["copy_gbs"],
             "frac_of_mix": achieved / attain["mix_gbs"] if "mix_gbs" in attain else None,
