@@ -142,7 +142,9 @@ int zero_memory_model(double psi, int32_t nd, int32_t stage, int32_t k, zero_mem
  * The Nd ranks' fp16 contributions to the owned window, as the
  * reduce-scatter delivers them: slice k (rank k) starts at
  * base + k*slice_stride, and the owned window is elements
- * [elem_off, elem_off + n) of every slice.
+ * [elem_off, elem_off + n) of every slice.  (Measured at Nd = 400: a
+ * slice_stride that is an exact power of two reads 2-3% slower than one
+ * padded off it by a few thousand elements.)
  */
 typedef struct zero_grad_src {
     const uint16_t* base;   /* device, fp16 bit patterns, 16-byte aligned */
